@@ -1,0 +1,178 @@
+/*
+ * sbl.h -- C ABI of the Sparse-BitLinear forward library for AMD MI355X (gfx950).
+ *
+ * The library computes the forward pass of a Sparse-BitLinear layer as the
+ * Sparse-BitNet summary (paper-graph-ui, section 3.4 "Detailed, Sentence-Based
+ * Technical Breakdown") states it:
+ *   x~    = Q_a(x)                      per-token absmax int8 activations
+ *   M     = Pi_{N:M}(|W|)               keep-mask from master-weight magnitudes
+ *   W_q   = RoundClip(W/(gamma+eps),-1,1), gamma = mean |W| over the tensor
+ *   W_eff = W_q (.) M                   quantize, then apply the mask
+ *   y     = s * (W_eff x~)              int32 accumulation, one fp rescale
+ *
+ * Conventions shared by every call
+ *   - Every device pointer is caller-owned; the library never allocates,
+ *     frees or retains memory. Pointers must be 16-byte aligned.
+ *   - Calls only enqueue work on `stream` and return; nothing waits for the
+ *     device. Scalars computed on the device (gamma, sw) stay there.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     failure the first error is returned and no work is enqueued. Launch
+ *     failures are reported as SBL_ERR_HIP. No exception crosses the ABI.
+ *   - Matrices are row-major: x [T, K] (row stride ldx elements), W [O, K],
+ *     y [T, O]. N:M groups run along K inside each row of W, starting at k=0.
+ *   - Supported: M in {4, 8}, 1 <= N <= M, K % M == 0, 1 <= K <= 2^24.
+ *     T = 0 (or O = 0 where noted) is a valid empty call that enqueues nothing.
+ *   - Inputs must be finite; results for NaN/Inf inputs are unspecified.
+ *   - Thread safety: calls are stateless apart from a per-device property cache.
+ *
+ * Packed ternary-plus-index weight format (this library's own layout; the
+ * pages only fix that four ternary values fit one byte -- BitNet b1.58 2B4T
+ * summary, section 3.4 "Inference Implementation: GPU" -- and that the
+ * structured-sparse kernels share one weight layout -- Sparse-BitNet
+ * paperlayer.ai summary, appendix A.2):
+ *   2-bit code: 0 -> 00, +1 -> 01, -1 -> 11.
+ *   Byte-sliced word: a uint32 holding 16 two-bit fields, field u at bit
+ *     8*(u%4) + 2*(u/4); (word >> 2j) & 0x03030303 yields fields 4j..4j+3 one
+ *     per byte, so one byte-permute turns them into four int8 values.
+ *   Each row of W is one record of fixed pitch (sbl_packed_bytes / O), so
+ *   packed buffers of several tensors with the same K concatenate along O.
+ *   INDEX FORM (N=2, M=4; feeds the gfx950 2:4 sparse MFMA directly):
+ *     pitch = ceil(K/128)*32 bytes. Chunk c (k in [32c, 32c+32), 8 groups q of
+ *     4) is two little-endian uint32: word 0 holds, as byte-sliced field
+ *     v = 2q + j, the code of the j-th kept slot (ascending) of group q;
+ *     word 1 holds the kept slot indices: bits [4q+1:4q] first, [4q+3:4q+2]
+ *     second. Groups past K: slots (0,1), codes 0. 2 bits per weight.
+ *   DENSE FORM (every other N:M):
+ *     pitch = ceil(K/64)*16 + ceil(K/128)*16 bytes. First ceil(K/64)*4 uint32
+ *     byte-sliced words of W_eff codes (word c: k = 16c + u as field u), then
+ *     ceil(K/128)*4 uint32 mask words (bit j of word c = mask[32c + j]).
+ *     Everything past K is zero. 3 bits per weight (2 read by the GEMM).
+ */
+#ifndef SBL_H
+#define SBL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SBL_OK = 0,
+  SBL_ERR_NULL = 1,       /* a required pointer is NULL */
+  SBL_ERR_SHAPE = 2,      /* a size is negative/zero where not allowed, K % M != 0, too large, ldx < K */
+  SBL_ERR_NM = 3,         /* M not in {4,8} or N not in [1, M] */
+  SBL_ERR_DTYPE = 4,      /* dtype not SBL_BF16 / SBL_FP32 */
+  SBL_ERR_ALIGN = 5,      /* a device pointer is not 16-byte aligned */
+  SBL_ERR_WORKSPACE = 6,  /* workspace too small (or NULL while bytes are needed) */
+  SBL_ERR_HIP = 7,        /* a HIP runtime call or kernel launch failed */
+  SBL_ERR_VALUE = 8       /* eps not a positive, normal, finite float */
+} sbl_status;
+
+typedef enum { SBL_BF16 = 0, SBL_FP32 = 1 } sbl_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* sbl_status_string(int status);
+
+/* Library version string, e.g. "sbl 0.1 gfx950". */
+const char* sbl_version(void);
+
+/*
+ * a1. Per-token absmax int8 activation quantization.
+ * Sparse-BitNet summary, section 3.4 "Activation quantization" (Clip(x *
+ * 127/(max|x| + eps), -128, 127)); BitNet b1.58 2B4T summary, section 3.4
+ * "Activation Quantization: Per-Token Absmax" (one scale per token, nearest
+ * integer). For each row t of x, in IEEE fp32:
+ *   m = max_k |x[t,k]|, d = m + eps_a, s = 127 / d,
+ *   xq[t,k] = clamp(rint_half_even(x[t,k] * s), -128, 127), sx[t] = d / 127.
+ * x: device, [T, K] of xdt with row stride ldx >= K elements.
+ * xq: device int8 [T, K] contiguous (written). sx: device float [T] (written).
+ */
+sbl_status sbl_quant_act(const void* x, sbl_dtype xdt, int64_t T, int64_t K, int64_t ldx,
+                         float eps_a, int8_t* xq, float* sx, hipStream_t stream);
+
+/* Workspace bytes sbl_quant_mask_weight needs for an [O, K] tensor. */
+sbl_status sbl_quant_mask_weight_workspace(int64_t O, int64_t K, size_t* bytes);
+
+/*
+ * a2 + a3 + a4. Absmean scale, N:M mask, RoundClip and mask application,
+ * packing -- the weight side of the forward, with the mask recomputed on
+ * every call. Sparse-BitNet summary, section 3.4: "Step 1: Compute the
+ * Rescaling Factor", "Step 2: Rescale and RoundClip" (Eq. 1), "N:M Mask
+ * Generation", "Composition Order: Quant-Then-Mask".
+ *   gamma = fp32( RN64(sum |W|) / (O*K) ), the sum exact and order-free;
+ *   sw = fp32(gamma + eps_w);
+ *   mask: per row and group of M along K keep the N largest |W| (ties: lower
+ *         index first; exactly N kept);
+ *   code = clamp(rint_half_even(fp32(W / sw)), -1, 1); W_eff = code * mask.
+ * w: device [O, K] master weights of wdt (fp32 or bf16), contiguous.
+ * w_eff (int8 [O,K]), mask (uint8 0/1 [O,K]), packed (sbl_packed_bytes bytes),
+ *   sw_rows (float [O], every entry = sw): optional outputs, may be NULL.
+ * gamma_sw: device float[2] (required) <- {gamma, sw}.
+ * ws: device workspace of at least sbl_quant_mask_weight_workspace bytes;
+ *   its contents need no initialisation and are scratch after the call.
+ * O * K must be in [1, 2^31).
+ */
+sbl_status sbl_quant_mask_weight(const void* w, sbl_dtype wdt, int64_t O, int64_t K, int N, int M,
+                                 float eps_w, int8_t* w_eff, uint8_t* mask, void* packed,
+                                 float* gamma_sw, float* sw_rows, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* Size in bytes of the packed format for an [O, K] N:M tensor (O * pitch). */
+sbl_status sbl_packed_bytes(int64_t O, int64_t K, int N, int M, size_t* bytes);
+
+/*
+ * Pack / unpack between (W_eff, mask) and the packed format above.
+ * w_eff: device int8 [O,K] in {-1,0,1}, zero wherever mask is 0; mask: device
+ * uint8 [O,K] with exactly N ones per group of M. Other contents give an
+ * unspecified (but in-bounds) packed result. unpack(pack(w, m)) == (w, m).
+ */
+sbl_status sbl_pack(const int8_t* w_eff, const uint8_t* mask, int64_t O, int64_t K, int N, int M,
+                    void* packed, hipStream_t stream);
+sbl_status sbl_unpack(const void* packed, int64_t O, int64_t K, int N, int M, int8_t* w_eff,
+                      uint8_t* mask, hipStream_t stream);
+
+/*
+ * a5 + a6. int8 x ternary N:M GEMM with an int32 accumulator, dequantized.
+ * Sparse-BitNet summary, section 3.4 "The Full Sparse-BitLinear Layer"
+ * (y = s * (W_eff x~), one scalar absorbs both scales; Eq. 4).
+ *   acc[t,o] = sum_k xq[t,k] * W_eff[o,k]          (exact int32)
+ *   y[t,o]   = fp32(fp32(float(acc) * sx[t]) * sw[o * sw_inc]) -> ydt (bf16: RNE)
+ * xq: device int8 [T,K]; sx: device float [T]; packed: device, packed format;
+ * sw: device float, one value per row of W (sw_inc = 1) or one for all rows
+ *   (sw_inc = 0), e.g. &gamma_sw[1] from sbl_quant_mask_weight;
+ * y: device [T,O] of ydt (written); acc: optional device int32 [T,O].
+ * 2:4 weights run on the gfx950 sparse MFMA (smfmac); other N:M on dense
+ * int8 MFMA; small T uses a bandwidth-oriented variant. Same results.
+ * T = 0 or O = 0: nothing is enqueued.
+ */
+sbl_status sbl_gemm(const int8_t* xq, const float* sx, const void* packed, const float* sw,
+                    int64_t sw_inc, int64_t T, int64_t O, int64_t K, int N, int M, void* y,
+                    sbl_dtype ydt, int32_t* acc, hipStream_t stream);
+
+/* Workspace bytes for sbl_linear_fwd (prepacked != 0: weights come packed). */
+sbl_status sbl_linear_fwd_workspace(int64_t T, int64_t O, int64_t K, int N, int M, int prepacked,
+                                    size_t* bytes);
+
+/*
+ * The whole forward: a1 on x, then either a2-a4 on w_master (mask recomputed
+ * this call) or the caller's prepacked weights with their sw, then a5 + a6.
+ * Sparse-BitNet summary, section 3.4 "The Full Sparse-BitLinear Layer"
+ * (Algorithm 1 forward, Algorithm 2).
+ * x: device [T,K] of xdt, contiguous. Exactly one of w_master (device [O,K]
+ * of wdt) and prepacked (device packed buffer, with sw_prepacked / sw_inc as
+ * in sbl_gemm) must be non-NULL. y: device [T,O] of ydt.
+ * ws: at least sbl_linear_fwd_workspace bytes (scratch).
+ */
+sbl_status sbl_linear_fwd(const void* x, sbl_dtype xdt, const void* w_master, sbl_dtype wdt,
+                          const void* prepacked, const float* sw_prepacked, int64_t sw_inc,
+                          int64_t T, int64_t O, int64_t K, int N, int M, float eps_a, float eps_w,
+                          void* y, sbl_dtype ydt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SBL_H */

@@ -1,0 +1,238 @@
+// C ABI of the Sparse-BitLinear library: argument validation (on the host,
+// before anything is enqueued), workspace sizing and dispatch to the kernels.
+#include "sbl.h"
+#include "sbl_internal.h"
+
+#include <cmath>
+#include <cfloat>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+
+namespace sbl {
+
+static bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("SBL_LOG");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+const DeviceInfo& device_info() {
+  static DeviceInfo infos[64];
+  static std::once_flag flags[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::call_once(flags[dev], [dev] {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      infos[dev].cus = cus;
+  });
+  return infos[dev];
+}
+
+}  // namespace sbl
+
+using namespace sbl;
+
+namespace {
+
+constexpr int64_t kMaxK = int64_t(1) << 24;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool dtype_ok(int d) { return d == SBL_BF16 || d == SBL_FP32; }
+bool nm_ok(int N, int M) { return (M == 4 || M == 8) && N >= 1 && N <= M; }
+bool eps_ok(float e) { return std::isfinite(e) && e >= FLT_MIN; }
+
+sbl_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SBL_OK;
+  if (log_enabled()) std::fprintf(stderr, "sbl: %s failed: %s\n", what, hipGetErrorString(e));
+  return SBL_ERR_HIP;
+}
+
+// Shape check shared by the weight-side calls.
+sbl_status check_wshape(int64_t O, int64_t K, int N, int M) {
+  if (!nm_ok(N, M)) return SBL_ERR_NM;
+  if (O < 0 || K < 1 || K > kMaxK || K % M != 0) return SBL_ERR_SHAPE;
+  if (O > (int64_t(1) << 31)) return SBL_ERR_SHAPE;
+  return SBL_OK;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct LinearWs {
+  size_t xq, sx, gsw, prep, packed, total;
+};
+LinearWs linear_ws_layout(int64_t T, int64_t O, int64_t K, int N, int M, bool prepacked) {
+  LinearWs L{};
+  size_t off = 0;
+  L.xq = off; off += align256((size_t)(T * K));
+  L.sx = off; off += align256((size_t)T * 4);
+  L.gsw = off; off += 256;
+  L.prep = off; off += prepacked ? 0 : align256(prep_workspace_bytes());
+  L.packed = off; off += prepacked ? 0 : align256((size_t)(O * row_pitch(K, N, M)));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sbl_status_string(int s) {
+  switch (s) {
+    case SBL_OK: return "SBL_OK";
+    case SBL_ERR_NULL: return "SBL_ERR_NULL: required pointer is NULL";
+    case SBL_ERR_SHAPE: return "SBL_ERR_SHAPE: invalid size (K % M, bounds, ldx)";
+    case SBL_ERR_NM: return "SBL_ERR_NM: unsupported N:M (M in {4,8}, 1 <= N <= M)";
+    case SBL_ERR_DTYPE: return "SBL_ERR_DTYPE: dtype must be SBL_BF16 or SBL_FP32";
+    case SBL_ERR_ALIGN: return "SBL_ERR_ALIGN: device pointer not 16-byte aligned";
+    case SBL_ERR_WORKSPACE: return "SBL_ERR_WORKSPACE: workspace too small";
+    case SBL_ERR_HIP: return "SBL_ERR_HIP: HIP runtime or launch failure";
+    case SBL_ERR_VALUE: return "SBL_ERR_VALUE: eps must be a positive normal finite float";
+    default: return "SBL: unknown status";
+  }
+}
+
+const char* sbl_version(void) { return "sbl 0.1 gfx950"; }
+
+sbl_status sbl_quant_act(const void* x, sbl_dtype xdt, int64_t T, int64_t K, int64_t ldx,
+                         float eps_a, int8_t* xq, float* sx, hipStream_t stream) {
+  if (!dtype_ok(xdt)) return SBL_ERR_DTYPE;
+  if (T < 0 || K < 1 || K > kMaxK || ldx < K) return SBL_ERR_SHAPE;
+  if (!eps_ok(eps_a)) return SBL_ERR_VALUE;
+  if (T == 0) return SBL_OK;
+  if (!x || !xq || !sx) return SBL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(sx)) return SBL_ERR_ALIGN;
+  return hip_status(launch_quant_act(x, xdt == SBL_BF16, T, K, ldx, eps_a, xq, sx, stream),
+                    "quant_act");
+}
+
+sbl_status sbl_quant_mask_weight_workspace(int64_t O, int64_t K, size_t* bytes) {
+  if (!bytes) return SBL_ERR_NULL;
+  if (O < 1 || K < 1 || O * K >= (int64_t(1) << 31)) return SBL_ERR_SHAPE;
+  *bytes = prep_workspace_bytes();
+  return SBL_OK;
+}
+
+sbl_status sbl_quant_mask_weight(const void* w, sbl_dtype wdt, int64_t O, int64_t K, int N, int M,
+                                 float eps_w, int8_t* w_eff, uint8_t* mask, void* packed,
+                                 float* gamma_sw, float* sw_rows, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  if (!dtype_ok(wdt)) return SBL_ERR_DTYPE;
+  sbl_status st = check_wshape(O, K, N, M);
+  if (st != SBL_OK) return st;
+  if (O < 1 || O * K >= (int64_t(1) << 31)) return SBL_ERR_SHAPE;
+  if (!eps_ok(eps_w)) return SBL_ERR_VALUE;
+  if (!w || !gamma_sw) return SBL_ERR_NULL;
+  if (!ws) return SBL_ERR_WORKSPACE;
+  if (ws_bytes < prep_workspace_bytes()) return SBL_ERR_WORKSPACE;
+  for (const void* p : {w, (const void*)w_eff, (const void*)mask, (const void*)packed,
+                        (const void*)gamma_sw, (const void*)sw_rows, (const void*)ws})
+    if (p && !aligned16(p)) return SBL_ERR_ALIGN;
+  return hip_status(launch_quant_mask_weight(w, wdt == SBL_BF16, O, K, N, M, eps_w, w_eff, mask,
+                                             packed, gamma_sw, sw_rows, ws, stream),
+                    "quant_mask_weight");
+}
+
+sbl_status sbl_packed_bytes(int64_t O, int64_t K, int N, int M, size_t* bytes) {
+  if (!bytes) return SBL_ERR_NULL;
+  sbl_status st = check_wshape(O, K, N, M);
+  if (st != SBL_OK) return st;
+  *bytes = (size_t)(O * row_pitch(K, N, M));
+  return SBL_OK;
+}
+
+sbl_status sbl_pack(const int8_t* w_eff, const uint8_t* mask, int64_t O, int64_t K, int N, int M,
+                    void* packed, hipStream_t stream) {
+  sbl_status st = check_wshape(O, K, N, M);
+  if (st != SBL_OK) return st;
+  if (O == 0) return SBL_OK;
+  if (!w_eff || !mask || !packed) return SBL_ERR_NULL;
+  if (!aligned16(w_eff) || !aligned16(mask) || !aligned16(packed)) return SBL_ERR_ALIGN;
+  return hip_status(launch_pack(w_eff, mask, O, K, N, M, packed, stream), "pack");
+}
+
+sbl_status sbl_unpack(const void* packed, int64_t O, int64_t K, int N, int M, int8_t* w_eff,
+                      uint8_t* mask, hipStream_t stream) {
+  sbl_status st = check_wshape(O, K, N, M);
+  if (st != SBL_OK) return st;
+  if (O == 0) return SBL_OK;
+  if (!w_eff || !mask || !packed) return SBL_ERR_NULL;
+  if (!aligned16(w_eff) || !aligned16(mask) || !aligned16(packed)) return SBL_ERR_ALIGN;
+  return hip_status(launch_unpack(packed, O, K, N, M, w_eff, mask, stream), "unpack");
+}
+
+sbl_status sbl_gemm(const int8_t* xq, const float* sx, const void* packed, const float* sw,
+                    int64_t sw_inc, int64_t T, int64_t O, int64_t K, int N, int M, void* y,
+                    sbl_dtype ydt, int32_t* acc, hipStream_t stream) {
+  if (!dtype_ok(ydt)) return SBL_ERR_DTYPE;
+  sbl_status st = check_wshape(O, K, N, M);
+  if (st != SBL_OK) return st;
+  if (T < 0 || (sw_inc != 0 && sw_inc != 1)) return SBL_ERR_SHAPE;
+  if (T == 0 || O == 0) return SBL_OK;
+  if (!xq || !sx || !packed || !sw || !y) return SBL_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(sx) || !aligned16(packed) || !aligned16(y) ||
+      (acc && !aligned16(acc)) || ((uintptr_t)sw & 3u))
+    return SBL_ERR_ALIGN;
+  return hip_status(launch_gemm(xq, sx, packed, sw, sw_inc, T, O, K, N, M, y, ydt == SBL_BF16,
+                                acc, stream),
+                    "gemm");
+}
+
+sbl_status sbl_linear_fwd_workspace(int64_t T, int64_t O, int64_t K, int N, int M, int prepacked,
+                                    size_t* bytes) {
+  if (!bytes) return SBL_ERR_NULL;
+  sbl_status st = check_wshape(O, K, N, M);
+  if (st != SBL_OK) return st;
+  if (T < 0) return SBL_ERR_SHAPE;
+  *bytes = linear_ws_layout(T, O, K, N, M, prepacked != 0).total;
+  return SBL_OK;
+}
+
+sbl_status sbl_linear_fwd(const void* x, sbl_dtype xdt, const void* w_master, sbl_dtype wdt,
+                          const void* prepacked, const float* sw_prepacked, int64_t sw_inc,
+                          int64_t T, int64_t O, int64_t K, int N, int M, float eps_a, float eps_w,
+                          void* y, sbl_dtype ydt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!dtype_ok(xdt) || !dtype_ok(ydt) || (w_master && !dtype_ok(wdt))) return SBL_ERR_DTYPE;
+  sbl_status st = check_wshape(O, K, N, M);
+  if (st != SBL_OK) return st;
+  if (T < 0) return SBL_ERR_SHAPE;
+  const bool pre = prepacked != nullptr;
+  if (pre == (w_master != nullptr)) return SBL_ERR_NULL;  // exactly one weight source
+  if (pre && sw_inc != 0 && sw_inc != 1) return SBL_ERR_SHAPE;
+  if (!pre && (O < 1 || O * K >= (int64_t(1) << 31))) return SBL_ERR_SHAPE;
+  if (!eps_ok(eps_a) || (!pre && !eps_ok(eps_w))) return SBL_ERR_VALUE;
+  if (T == 0 || O == 0) return SBL_OK;
+  if (!x || !y || (pre && !sw_prepacked)) return SBL_ERR_NULL;
+  const LinearWs L = linear_ws_layout(T, O, K, N, M, pre);
+  if (!ws || ws_bytes < L.total) return SBL_ERR_WORKSPACE;
+  for (const void* p : {x, w_master, prepacked, (const void*)y, (const void*)ws})
+    if (p && !aligned16(p)) return SBL_ERR_ALIGN;
+  if (pre && ((uintptr_t)sw_prepacked & 3u)) return SBL_ERR_ALIGN;
+
+  char* base = (char*)ws;
+  int8_t* xq = (int8_t*)(base + L.xq);
+  float* sx = (float*)(base + L.sx);
+  float* gsw = (float*)(base + L.gsw);
+  hipError_t e = launch_quant_act(x, xdt == SBL_BF16, T, K, K, eps_a, xq, sx, stream);
+  if (e != hipSuccess) return hip_status(e, "linear_fwd/quant_act");
+  const void* packed = prepacked;
+  const float* sw = sw_prepacked;
+  int64_t inc = sw_inc;
+  if (!pre) {
+    void* pk = base + L.packed;
+    e = launch_quant_mask_weight(w_master, wdt == SBL_BF16, O, K, N, M, eps_w, nullptr, nullptr,
+                                 pk, gsw, nullptr, base + L.prep, stream);
+    if (e != hipSuccess) return hip_status(e, "linear_fwd/quant_mask_weight");
+    packed = pk;
+    sw = gsw + 1;
+    inc = 0;
+  }
+  return hip_status(launch_gemm(xq, sx, packed, sw, inc, T, O, K, N, M, y, ydt == SBL_BF16,
+                                nullptr, stream),
+                    "linear_fwd/gemm");
+}
+
+}  // extern "C"

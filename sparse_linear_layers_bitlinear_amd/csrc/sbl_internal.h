@@ -1,0 +1,54 @@
+// Internal declarations shared by the library's translation units.
+// Nothing here is part of the public ABI (include/sbl.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace sbl {
+
+// ---- packed-format geometry (see include/sbl.h) ---------------------------
+__host__ __device__ inline bool index_form(int N, int M) { return M == 4 && N == 2; }
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// bytes of the code area of a dense-form row (ceil(K/64) * 16)
+__host__ __device__ inline int64_t dense_code_bytes(int64_t K) { return cdiv(K, 64) * 16; }
+// bytes of the mask area of a dense-form row (ceil(K/128) * 16)
+__host__ __device__ inline int64_t dense_mask_bytes(int64_t K) { return cdiv(K, 128) * 16; }
+__host__ __device__ inline int64_t row_pitch(int64_t K, int N, int M) {
+  return index_form(N, M) ? cdiv(K, 128) * 32 : dense_code_bytes(K) + dense_mask_bytes(K);
+}
+// 32-wide chunks per packed row record (both forms cover ceil(K/128)*4 chunks)
+__host__ __device__ inline int64_t row_chunks(int64_t K) { return cdiv(K, 128) * 4; }
+
+// Max workgroups of the absmean partial pass; fixes the workspace size.
+constexpr int kAbsmeanMaxBlocks = 1024;
+// Workspace of the weight-prep path: partial exponent bins + device scalars.
+constexpr size_t kPrepScalarBytes = 256;
+inline size_t prep_workspace_bytes() {
+  return (size_t)kAbsmeanMaxBlocks * 16 * sizeof(unsigned long long) + kPrepScalarBytes;
+}
+
+struct DeviceInfo {
+  int cus = 256;
+};
+const DeviceInfo& device_info();  // cached per device
+
+// ---- launchers (return hipGetLastError() of the launch) -------------------
+hipError_t launch_quant_act(const void* x, bool bf16, int64_t T, int64_t K, int64_t ldx,
+                            float eps, int8_t* xq, float* sx, hipStream_t s);
+
+hipError_t launch_quant_mask_weight(const void* w, bool bf16, int64_t O, int64_t K, int N, int M,
+                                    float eps, int8_t* w_eff, uint8_t* mask, void* packed,
+                                    float* gamma_sw, float* sw_rows, void* ws, hipStream_t s);
+
+hipError_t launch_pack(const int8_t* w_eff, const uint8_t* mask, int64_t O, int64_t K, int N,
+                       int M, void* packed, hipStream_t s);
+hipError_t launch_unpack(const void* packed, int64_t O, int64_t K, int N, int M, int8_t* w_eff,
+                         uint8_t* mask, hipStream_t s);
+
+hipError_t launch_gemm(const int8_t* xq, const float* sx, const void* packed, const float* sw,
+                       int64_t sw_inc, int64_t T, int64_t O, int64_t K, int N, int M, void* y,
+                       bool y_bf16, int32_t* acc, hipStream_t s);
+
+}  // namespace sbl

@@ -1,0 +1,62 @@
+"""Shared helpers of the GPU parity tests (comparison rules, case logging)."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle as o
+
+
+def log_case(*parts):
+    """Name the case before the GPU runs it (flushed, so a crash still shows it)."""
+    print("[case]", *parts, flush=True)
+    sys.stdout.flush()
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+    return t if dtype is None else t.to(dtype)
+
+
+def bf16_tensor(x_f32):
+    """bf16-exact fp32 numpy array -> bf16 device tensor (exact)."""
+    return to_dev(x_f32).to(torch.bfloat16)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+def assert_f32_close(y_gpu, y_ref64, rtol=1e-3):
+    """fp32 output: |d| / max(|ref|, 1e-6 * max|ref|) <= rtol."""
+    y_gpu = np.asarray(y_gpu, np.float64)
+    y_ref64 = np.asarray(y_ref64, np.float64)
+    floor = 1e-6 * max(float(np.abs(y_ref64).max(initial=0.0)), 1e-30)
+    rel = np.abs(y_gpu - y_ref64) / np.maximum(np.abs(y_ref64), floor)
+    assert float(rel.max(initial=0.0)) <= rtol, f"max rel err {rel.max()}"
+
+
+def _ordered(bits):
+    b = bits.astype(np.int32)
+    return np.where(b >= 0x8000, 0x8000 - b, b)
+
+
+def assert_bf16_close(y_gpu_f32, y_ref64, max_ulp=1):
+    """bf16 output: at most max_ulp bf16 steps from the correctly rounded value."""
+    ref = o.to_bf16(y_ref64)
+    gb = (np.asarray(y_gpu_f32, np.float32).view(np.uint32) >> 16).astype(np.uint32)
+    rb = (ref.view(np.uint32) >> 16).astype(np.uint32)
+    d = np.abs(_ordered(gb) - _ordered(rb))
+    assert int(d.max(initial=0)) <= max_ulp, f"max bf16 ulp distance {d.max()}"
+    return float((d == 0).mean()) if d.size else 1.0
+
+
+def f32_bits(a):
+    return np.asarray(a, np.float32).view(np.uint32)
