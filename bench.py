@@ -1,0 +1,375 @@
+"""Throughput of the Sparse-BitLinear forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--nm N:M]
+                    [--decode-T T] [--layers L] [--no-cpu-baseline] [--eager]
+
+A step is one pass of the whole forward hot path over one batch:
+  prefill workloads (Qwen2.5-shaped FFN, mask recomputed every call):
+    per-token int8 quantization of each FFN input, absmean + N:M mask +
+    RoundClip + pack of every master weight, the int8 x ternary GEMMs with
+    dequant epilogue (gate and up fused into one GEMM over concatenated rows);
+  decode workload (BitNet-2B4T-shaped layer, prepacked 2:4 weights): for each
+    of L distinct layer copies, int8 quantization of the layer inputs and the
+    q|k|v, o, gate|up and down GEMMs.
+The step is captured once into a HIP graph and replayed (the library launches
+stay the same kernels; the graph only removes Python/ctypes launch cost).
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from sparse_linear_layers_bitlinear_amd import sbl  # noqa: E402
+from sparse_linear_layers_bitlinear_amd.workloads import (  # noqa: E402
+    WORKLOADS, make_workload)
+
+# MI355X published peaks
+PEAK_INT8_DENSE_TOPS = 5000.0     # dense int8 MFMA, TOPS
+PEAK_HBM_GBS = 8000.0             # HBM3E, GB/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="qwen05b_ffn",
+                   choices=["qwen05b_ffn", "qwen15b_ffn", "qwen3b_sweep", "bitnet_decode", "tiny"])
+    p.add_argument("--nm", default=None, help="override N:M, e.g. 2:8")
+    p.add_argument("--decode-T", type=int, default=8)
+    p.add_argument("--layers", type=int, default=30)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    return p.parse_args()
+
+
+class Timeline:
+    """Events around each named call of a step, on the stream the library
+    launches on (torch's current stream)."""
+
+    def __init__(self):
+        self.names, self.evs = [], []
+
+    def mark(self, name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.names.append(name)
+        self.evs.append(e)
+
+    def durations_ms(self):
+        torch.cuda.synchronize()
+        out = {}
+        for i in range(len(self.evs) - 1):
+            n = self.names[i]
+            out.setdefault(n, []).append(self.evs[i].elapsed_time(self.evs[i + 1]))
+        return out
+
+
+# ---------------------------------------------------------------- prefill --
+class PrefillStep:
+    def __init__(self, wl_name, N, M):
+        wl = WORKLOADS[wl_name]
+        self.wl, self.N, self.M = wl, N, M
+        W, X = make_workload(wl_name)
+        dev = torch.device("cuda:0")
+        self.T = wl.T
+        self.x = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in X.items()}
+        self.W = {k: torch.from_numpy(v).to(dev) for k, v in W.items()}
+        self.K_of = dict(wl.x_specs)
+        self.xq = {k: torch.empty((self.T, K), dtype=torch.int8, device=dev)
+                   for k, K in self.K_of.items()}
+        self.sx = {k: torch.empty(self.T, dtype=torch.float32, device=dev) for k in self.K_of}
+        # group projections that share an input into one GEMM over concatenated rows
+        self.groups = {}
+        for lin in wl.linears:
+            self.groups.setdefault(lin.x_name, []).append(lin)
+        self.packed, self.swr, self.y = {}, {}, {}
+        for xn, lins in self.groups.items():
+            K = self.K_of[xn]
+            O = sum(l.O for l in lins)
+            self.packed[xn] = torch.empty(sbl.sbl_packed_bytes(O, K, N, M), dtype=torch.uint8,
+                                          device=dev)
+            self.swr[xn] = torch.empty(O, dtype=torch.float32, device=dev)
+            self.y[xn] = torch.empty((self.T, O), dtype=torch.bfloat16, device=dev)
+        nws = max(sbl.sbl_quant_mask_weight_workspace(l.O, l.K) for l in wl.linears)
+        self.ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+        self.ops = sum(2.0 * self.T * l.O * l.K for l in wl.linears)
+
+    def run(self, tl=None):
+        mark = tl.mark if tl else (lambda n: None)
+        N, M = self.N, self.M
+        for xn in self.groups:
+            mark(f"quant_act[{xn}]")
+            sbl.sbl_quant_act(self.x[xn], xq=self.xq[xn], sx=self.sx[xn])
+        for xn, lins in self.groups.items():
+            off_p, off_o = 0, 0
+            for l in lins:
+                nb = sbl.sbl_packed_bytes(l.O, l.K, N, M)
+                mark(f"quant_mask_weight[{l.name}]")
+                sbl.sbl_quant_mask_weight(self.W[l.name], N, M,
+                                          packed=self.packed[xn][off_p:off_p + nb],
+                                          sw_rows=self.swr[xn][off_o:off_o + l.O], ws=self.ws)
+                off_p += nb
+                off_o += l.O
+        for xn, lins in self.groups.items():
+            O = sum(l.O for l in lins)
+            mark(f"gemm[{'+'.join(l.name for l in lins)}]")
+            sbl.sbl_gemm(self.xq[xn], self.sx[xn], self.packed[xn], self.swr[xn], O, N, M,
+                         y=self.y[xn])
+        mark("end")
+
+    def call_info(self, name):
+        """(bound, algorithmic units per launch, unit) of a named call."""
+        T = self.T
+        if name.startswith("gemm["):
+            xn = [k for k, ls in self.groups.items()
+                  if name == f"gemm[{'+'.join(l.name for l in ls)}]"][0]
+            ops = sum(2.0 * T * l.O * l.K for l in self.groups[xn])
+            return "mfma", ops, "ops"
+        if name.startswith("quant_act["):
+            K = self.K_of[name[10:-1]]
+            return "hbm", 2.0 * T * K + T * K + 4.0 * T, "bytes"
+        l = [l for l in self.wl.linears if name == f"quant_mask_weight[{l.name}]"][0]
+        return "hbm", 8.0 * l.O * l.K + sbl.sbl_packed_bytes(l.O, l.K, self.N, self.M), "bytes"
+
+
+# ----------------------------------------------------------------- decode --
+class DecodeStep:
+    def __init__(self, T, L):
+        wl = WORKLOADS["bitnet_decode"]
+        self.wl, self.N, self.M, self.T, self.L = wl, 2, 4, T, L
+        dev = torch.device("cuda:0")
+        W, X = make_workload("bitnet_decode", T=T)
+        self.x = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in X.items()}
+        self.K_of = dict(wl.x_specs)
+        self.groups = {}
+        for lin in wl.linears:
+            self.groups.setdefault(lin.x_name, []).append(lin)
+        # L distinct prepacked copies: copy 0 from the seeded workload weights, copies
+        # l > 0 from seeded torch draws of the same distribution (not timed)
+        g = torch.Generator(device=dev)
+        self.packed, self.swr = [], []
+        ws = torch.empty(sbl.sbl_quant_mask_weight_workspace(6912, 2560), dtype=torch.uint8,
+                         device=dev)
+        for li in range(L):
+            g.manual_seed(1000 + li)
+            pk, sr = {}, {}
+            for xn, lins in self.groups.items():
+                K = self.K_of[xn]
+                O = sum(l.O for l in lins)
+                pk[xn] = torch.empty(sbl.sbl_packed_bytes(O, K, 2, 4), dtype=torch.uint8,
+                                     device=dev)
+                sr[xn] = torch.empty(O, dtype=torch.float32, device=dev)
+                op, oo = 0, 0
+                for l in lins:
+                    if li == 0:
+                        w = torch.from_numpy(W[l.name]).to(dev)
+                    else:
+                        w = torch.randn((l.O, l.K), generator=g, device=dev) * 0.02
+                    nb = sbl.sbl_packed_bytes(l.O, l.K, 2, 4)
+                    sbl.sbl_quant_mask_weight(w, 2, 4, packed=pk[xn][op:op + nb],
+                                              sw_rows=sr[xn][oo:oo + l.O], ws=ws)
+                    op += nb
+                    oo += l.O
+            self.packed.append(pk)
+            self.swr.append(sr)
+        torch.cuda.synchronize()
+        self.xq = {k: torch.empty((T, K), dtype=torch.int8, device=dev)
+                   for k, K in self.K_of.items()}
+        self.sx = {k: torch.empty(T, dtype=torch.float32, device=dev) for k in self.K_of}
+        self.y = {xn: torch.empty((T, sum(l.O for l in ls)), dtype=torch.bfloat16, device=dev)
+                  for xn, ls in self.groups.items()}
+        self.weights = sum(l.O * l.K for l in wl.linears)
+        self.bytes_layer = sum(self.call_bytes(xn) for xn in self.groups) + \
+            sum(3.0 * T * K + 4 * T for K in self.K_of.values())
+        self.ops = 2.0 * T * self.weights * L
+
+    def call_bytes(self, xn):
+        T = self.T
+        K = self.K_of[xn]
+        O = sum(l.O for l in self.groups[xn])
+        return sbl.sbl_packed_bytes(O, K, 2, 4) + T * K + 4 * T + 4 * O + 2 * T * O
+
+    def run(self, tl=None):
+        mark = tl.mark if tl else (lambda n: None)
+        for li in range(self.L):
+            for xn in self.groups:
+                mark(f"quant_act[{xn}]")
+                sbl.sbl_quant_act(self.x[xn], xq=self.xq[xn], sx=self.sx[xn])
+                O = sum(l.O for l in self.groups[xn])
+                mark(f"gemm[{'+'.join(l.name for l in self.groups[xn])}]")
+                sbl.sbl_gemm(self.xq[xn], self.sx[xn], self.packed[li][xn], self.swr[li][xn],
+                             O, 2, 4, y=self.y[xn])
+        mark("end")
+
+    def call_info(self, name):
+        if name.startswith("gemm["):
+            xn = [k for k, ls in self.groups.items()
+                  if name == f"gemm[{'+'.join(l.name for l in ls)}]"][0]
+            return "hbm", float(self.call_bytes(xn)), "bytes"
+        K = self.K_of[name[10:-1]]
+        return "hbm", 3.0 * self.T * K + 4.0 * self.T, "bytes"
+
+
+# ------------------------------------------------------------------ timing --
+def time_steps(step, steps, warmup, eager):
+    stream = torch.cuda.current_stream()
+    if eager:
+        run = step.run
+    else:
+        s = torch.cuda.Stream()
+        s.wait_stream(stream)
+        with torch.cuda.stream(s):
+            step.run()          # warm the allocator / code objects outside capture
+        stream.wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step.run()
+        run = graph.replay
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        run()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def breakdown(step, steps):
+    """Per-call device time: events around every library call, eager launches,
+    over `steps` further steps (the graph-timed region above is not perturbed)."""
+    tl = Timeline()
+    for _ in range(steps):
+        step.run(tl)
+    d = tl.durations_ms()
+    return {k: float(np.mean(v)) for k, v in d.items()}, {k: len(v) for k, v in d.items()}
+
+
+def cpu_baseline(wl_name, N, M, seconds, decode_T=None):
+    import oracle as o
+    from threadpoolctl import threadpool_info
+    if wl_name == "bitnet_decode":
+        W, X = make_workload(wl_name, T=decode_T)
+        wl = WORKLOADS[wl_name]
+        # decode path: prepacked weights; the oracle's act quant + GEMM + dequant
+        prep = {l.name: o.quant_mask_weight(W[l.name], 2, 4) for l in wl.linears}
+        def one():
+            for l in wl.linears:
+                xq, sx = o.quant_act(X[l.x_name])
+                o.dequant(o.gemm_int(xq, prep[l.name][0]), sx, prep[l.name][3])
+        units = sum(l.O * l.K * 0.25 + decode_T * l.K + 2 * decode_T * l.O
+                    for l in wl.linears)
+        unit, sample = "GB/s", f"one BitNet-2B4T decode layer, T={decode_T}, prepacked 2:4"
+    else:
+        W, X = make_workload(wl_name)
+        wl = WORKLOADS[wl_name]
+        def one():
+            for l in wl.linears:
+                o.linear_fwd(X[l.x_name], W[l.name], N, M)
+        units = sum(2.0 * wl.T * l.O * l.K for l in wl.linears)
+        unit = "TOPS"
+        sample = (f"full {wl_name} step (T={wl.T}, {N}:{M}, every projection, mask "
+                  f"recomputed), repeated")
+    times = []
+    t_end = time.time() + seconds
+    while time.time() < t_end or len(times) < 2:
+        t0 = time.perf_counter()
+        one()
+        times.append(time.perf_counter() - t0)
+    med = float(np.median(times))
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    val = units / med / (1e12 if unit == "TOPS" else 1e9)
+    return {"value": round(val, 6), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{sample} x{len(times)}, median {med * 1e3:.1f} ms per step",
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    torch.cuda.init()
+    wl = WORKLOADS[a.workload]
+    N, M = wl.N, wl.M
+    if a.nm:
+        N, M = (int(v) for v in a.nm.split(":"))
+    if a.workload == "bitnet_decode":
+        step = DecodeStep(a.decode_T, a.layers)
+    else:
+        step = PrefillStep(a.workload, N, M)
+    ms = time_steps(step, a.steps, a.warmup, a.eager)
+    per_call, counts = breakdown(step, a.steps)
+    calls_per_step = {k: counts[k] // a.steps for k in counts}
+    share = {k: per_call[k] * calls_per_step[k] for k in per_call}
+    dom = max(share, key=share.get)
+    bound, units, kind = step.call_info(dom)
+    achieved = units / (per_call[dom] * 1e-3)
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 2),
+                "peak": PEAK_INT8_DENSE_TOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["avg_ms"] = round(per_call[dom], 5)
+
+    if a.workload == "bitnet_decode":
+        total_bytes = step.bytes_layer * step.L
+        value = total_bytes / (ms * 1e-3) / 1e9
+        metric, unit = "Sparse-BitLinear decode GB/s (prepacked 2:4, whole layer stream)", "GB/s"
+        config = {"workload": "bitnet_decode", "tokens": a.decode_T, "layers": a.layers,
+                  "nm": "2:4", "bytes_per_step": total_bytes,
+                  "weights_per_layer": step.weights}
+    else:
+        value = step.ops / (ms * 1e-3) / 1e12
+        metric = "Sparse-BitLinear effective TOPS (prefill)"
+        unit = "TOPS"
+        config = {"workload": a.workload, "tokens": step.T, "nm": f"{N}:{M}",
+                  "projections": [f"{l.name} {l.O}x{l.K}" for l in wl.linears],
+                  "mask": "recomputed every step", "dense_equiv_ops_per_step": step.ops}
+    out = {
+        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8xternary->int32 (bf16 in/out)", "data": "synthetic",
+        "config": config, "roofline": roof,
+        "breakdown_ms": {k: round(share[k], 5) for k in share},
+        "timing": "eager launches" if a.eager else "HIP graph replay",
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(a.workload, N, M, a.cpu_seconds, a.decode_T)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -29,6 +29,9 @@
 #include "sbl_internal.h"
 #include "device_util.cuh"
 
+#include <cmath>
+#include <cstdlib>
+
 namespace sbl {
 
 constexpr int kPitchA = 80;    // bytes per staged W row (64 values + 16 pad / index)
@@ -85,183 +88,117 @@ __device__ __forceinline__ void store_out(void* __restrict__ y, int32_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Dense form: v_mfma_i32_16x16x64_i8
+// Tile order: workgroups are dispatched round-robin over the 8 XCDs, each with
+// its own L2. Block b runs on XCD b % 8; renumber so every XCD owns one
+// contiguous range of tile ids, and walk tiles in groups of kGroupM O-tiles so
+// neighbouring ids share W panels (A) and token panels (B).
 // ---------------------------------------------------------------------------
-template <int WM, int WN, bool KA16, bool YBF16>
-__global__ __launch_bounds__(256) void k_gemm_dense(const int8_t* __restrict__ xq,
-                                                    const float* __restrict__ sx,
-                                                    const uint8_t* __restrict__ packed,
-                                                    int64_t pitch, const float* __restrict__ sw,
-                                                    int64_t sw_inc, int64_t T, int64_t O,
-                                                    int64_t K, void* __restrict__ y,
-                                                    int32_t* __restrict__ acc_out) {
-  constexpr int BM = 2 * WM, BN = 2 * WN, BK = 64;
-  constexpr int FI = WM / 16, FJ = WN / 16;
-  constexpr int TPR_A = 256 / BM;        // threads per staged W row
-  constexpr int WPT_A = 4 / TPR_A;       // code words (16 k each) per thread
-  constexpr int SEG_B = BN * BK / 16;    // 16-byte xq segments per K-step
-  constexpr int NSEG = (SEG_B + 255) / 256;
-  static_assert(TPR_A >= 1 && WPT_A >= 1 && BM <= 256, "tile");
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* As = smem;                          // [2][BM][kPitchA]
-  uint8_t* Bs = smem + 2 * BM * kPitchA;       // [2][BN][kPitchBd]
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wo = wave & 1, wt = wave >> 1;
-  const int64_t o0 = (int64_t)blockIdx.y * BM, t0 = (int64_t)blockIdx.x * BN;
-  const int64_t nk = cdiv(K, BK);
-
-  // this thread's staging slots
-  const int ra = tid / TPR_A, pa = tid % TPR_A;
-  const bool va = o0 + ra < O;
-  const uint8_t* arow = packed + (o0 + ra) * pitch + 4 * WPT_A * pa;
-
-  uint32_t ga[WPT_A];
-  uint4 gb[NSEG];
-  auto gload = [&](int64_t ks) {
-#pragma unroll
-    for (int w = 0; w < WPT_A; ++w) ga[w] = 0;
-    if (va) {
-      const uint8_t* p = arow + ks * 16;
-      if constexpr (WPT_A == 4) { uint4 v = *(const uint4*)p; ga[0] = v.x; ga[1] = v.y; ga[2] = v.z; ga[3] = v.w; }
-      else if constexpr (WPT_A == 2) { uint2 v = *(const uint2*)p; ga[0] = v.x; ga[1] = v.y; }
-      else { ga[0] = *(const uint32_t*)p; }
-    }
-#pragma unroll
-    for (int q = 0; q < NSEG; ++q) {
-      const int seg = tid + 256 * q, rb = seg / (BK / 16), cb = seg % (BK / 16);
-      gb[q] = (seg < SEG_B && t0 + rb < T)
-                  ? load_x16<KA16>(xq + (t0 + rb) * K, ks * BK + 16 * cb, K)
-                  : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* a = As + (buf * BM + ra) * kPitchA + 16 * WPT_A * pa;
-#pragma unroll
-    for (int w = 0; w < WPT_A; ++w) {
-      uint4 v = make_uint4(expand_codes(ga[w], 0), expand_codes(ga[w], 1),
-                           expand_codes(ga[w], 2), expand_codes(ga[w], 3));
-      *(uint4*)(a + 16 * w) = v;
-    }
-#pragma unroll
-    for (int q = 0; q < NSEG; ++q) {
-      const int seg = tid + 256 * q, rb = seg / (BK / 16), cb = seg % (BK / 16);
-      if (seg < SEG_B) *(uint4*)(Bs + (buf * BN + rb) * kPitchBd + 16 * cb) = gb[q];
-    }
-  };
-
-  v4i acc[FI][FJ];
-#pragma unroll
-  for (int i = 0; i < FI; ++i)
-#pragma unroll
-    for (int j = 0; j < FJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int64_t ks = 0; ks < nk; ++ks) {
-    const int buf = (int)(ks & 1);
-    if (ks + 1 < nk) gload(ks + 1);
-    const uint8_t* a = As + buf * BM * kPitchA;
-    const uint8_t* b = Bs + buf * BN * kPitchBd;
-    const int koff = 16 * (lane >> 4);
-    v4i af[FI], bf[FJ];
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-      af[i] = *(const v4i*)(a + (wo * WM + 16 * i + (lane & 15)) * kPitchA + koff);
-#pragma unroll
-    for (int j = 0; j < FJ; ++j)
-      bf[j] = *(const v4i*)(b + (wt * WN + 16 * j + (lane & 15)) * kPitchBd + koff);
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-      for (int j = 0; j < FJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-    if (ks + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int i = 0; i < FI; ++i)
-#pragma unroll
-    for (int j = 0; j < FJ; ++j) {
-      const int64_t t = t0 + wt * WN + 16 * j + (lane & 15);
-      const int64_t o = o0 + wo * WM + 16 * i + 4 * (lane >> 4);
-      store_out<YBF16>(y, acc_out, acc[i][j], t, o, T, O, sx, sw, sw_inc);
-    }
+__device__ __forceinline__ void tile_of(int64_t bid, int64_t nb, int64_t ntm, int64_t ntn,
+                                        int64_t& tm, int64_t& tn) {
+  const int64_t xcd = bid % kXcds, local = bid / kXcds;
+  const int64_t per = nb / kXcds, rem = nb % kXcds;
+  const int64_t pid = xcd < rem ? xcd * (per + 1) + local
+                                : rem * (per + 1) + (xcd - rem) * per + local;
+  const int64_t gsz = (int64_t)kGroupM * ntn;
+  const int64_t g = pid / gsz, first = g * kGroupM;
+  const int64_t rows = (ntm - first) < kGroupM ? (ntm - first) : kGroupM;
+  const int64_t in = pid % gsz;
+  tm = first + in % rows;
+  tn = in / rows;
 }
 
 // ---------------------------------------------------------------------------
-// 2:4 index form: v_smfmac_i32_16x16x128_i8
+// One kernel for both forms. SP = false: dense form, BK = 64,
+// v_mfma_i32_16x16x64_i8. SP = true: 2:4 index form, BK = 128,
+// v_smfmac_i32_16x16x128_i8. Waves are arranged WAVES_M (along O) x WAVES_N
+// (along T); each owns a (BM/WAVES_M) x (BN/WAVES_N) block of 16x16 tiles.
 // ---------------------------------------------------------------------------
-template <int WM, int WN, bool KA16, bool YBF16>
-__global__ __launch_bounds__(256) void k_gemm_sparse24(const int8_t* __restrict__ xq,
-                                                       const float* __restrict__ sx,
-                                                       const uint8_t* __restrict__ packed,
-                                                       int64_t pitch, const float* __restrict__ sw,
-                                                       int64_t sw_inc, int64_t T, int64_t O,
-                                                       int64_t K, void* __restrict__ y,
-                                                       int32_t* __restrict__ acc_out) {
-  constexpr int BM = 2 * WM, BN = 2 * WN, BK = 128;
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool SP, bool KA16, bool YBF16>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void k_gemm(const int8_t* __restrict__ xq, const float* __restrict__ sx,
+            const uint8_t* __restrict__ packed, int64_t pitch, const float* __restrict__ sw,
+            int64_t sw_inc, int64_t T, int64_t O, int64_t K, void* __restrict__ y,
+            int32_t* __restrict__ acc_out) {
+  constexpr int NT = 64 * WAVES_M * WAVES_N;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FI = WM / 16, FJ = WN / 16;
-  constexpr int TPR_A = 256 / BM;        // threads per staged W row
-  constexpr int CPT_A = 4 / TPR_A;       // 32-k chunks (8 bytes each) per thread
-  constexpr int SEG_B = BN * BK / 16;
-  constexpr int NSEG = (SEG_B + 255) / 256;
-  static_assert(TPR_A >= 1 && CPT_A >= 1 && BM <= 256, "tile");
+  constexpr int BK = SP ? 128 : 64;
+  constexpr int PB = SP ? kPitchBs : kPitchBd;
+  constexpr int AROW = SP ? 32 : 16;          // packed bytes per W row per K-step
+  constexpr int APT = BM * AROW / NT;          // packed bytes per thread per K-step
+  constexpr int TPR = AROW / APT;              // threads per W row
+  constexpr int SEG = BN * BK / 16;            // 16-byte xq segments per K-step
+  constexpr int NSEG = (SEG + NT - 1) / NT;
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
+  static_assert(APT >= (SP ? 8 : 4) && APT <= 32 && AROW % APT == 0, "A staging");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* As = smem;                          // [2][BM][kPitchA]: 64 B values, 16 B idx
-  uint8_t* Bs = smem + 2 * BM * kPitchA;       // [2][BN][kPitchBs]
+  uint8_t* As = smem;                          // [2][BM][kPitchA]
+  uint8_t* Bs = smem + 2 * BM * kPitchA;       // [2][BN][PB]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wo = wave & 1, wt = wave >> 1;
-  const int64_t o0 = (int64_t)blockIdx.y * BM, t0 = (int64_t)blockIdx.x * BN;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int64_t ntm = cdiv(O, BM), ntn = cdiv(T, BN);
+  int64_t tm, tn;
+  tile_of(blockIdx.x, ntm * ntn, ntm, ntn, tm, tn);
+  const int64_t o0 = tm * BM, t0 = tn * BN;
   const int64_t nk = cdiv(K, BK);
 
-  const int ra = tid / TPR_A, pa = tid % TPR_A;
+  const int ra = tid / TPR, pa = tid % TPR;
   const bool va = o0 + ra < O;
-  const uint8_t* arow = packed + (o0 + ra) * pitch + 8 * CPT_A * pa;
+  const uint8_t* arow = packed + (o0 + ra) * pitch + APT * pa;
 
-  uint2 ga[CPT_A];
+  uint32_t ga[APT / 4];
   uint4 gb[NSEG];
   auto gload = [&](int64_t ks) {
-#pragma unroll
-    for (int c = 0; c < CPT_A; ++c) ga[c] = make_uint2(0, 0x44444444u);
-    if (va) {
-      const uint8_t* p = arow + ks * 32;
-      if constexpr (CPT_A == 4) {
-        uint4 v0 = *(const uint4*)p, v1 = *(const uint4*)(p + 16);
-        ga[0] = make_uint2(v0.x, v0.y); ga[1] = make_uint2(v0.z, v0.w);
-        ga[2] = make_uint2(v1.x, v1.y); ga[3] = make_uint2(v1.z, v1.w);
-      } else if constexpr (CPT_A == 2) {
-        uint4 v0 = *(const uint4*)p;
-        ga[0] = make_uint2(v0.x, v0.y); ga[1] = make_uint2(v0.z, v0.w);
-      } else {
-        ga[0] = *(const uint2*)p;
-      }
+    const uint8_t* p = arow + ks * AROW;
+    if constexpr (APT == 32) {
+      uint4 v0 = va ? *(const uint4*)p : make_uint4(0, SP ? 0x44444444u : 0, 0, SP ? 0x44444444u : 0);
+      uint4 v1 = va ? *(const uint4*)(p + 16) : v0;
+      ga[0] = v0.x; ga[1] = v0.y; ga[2] = v0.z; ga[3] = v0.w;
+      ga[4] = v1.x; ga[5] = v1.y; ga[6] = v1.z; ga[7] = v1.w;
+    } else if constexpr (APT == 16) {
+      uint4 v = va ? *(const uint4*)p : make_uint4(0, SP ? 0x44444444u : 0, 0, SP ? 0x44444444u : 0);
+      ga[0] = v.x; ga[1] = v.y; ga[2] = v.z; ga[3] = v.w;
+    } else if constexpr (APT == 8) {
+      uint2 v = va ? *(const uint2*)p : make_uint2(0, SP ? 0x44444444u : 0);
+      ga[0] = v.x; ga[1] = v.y;
+    } else {
+      ga[0] = va ? *(const uint32_t*)p : 0u;
     }
 #pragma unroll
     for (int q = 0; q < NSEG; ++q) {
-      const int seg = tid + 256 * q, rb = seg / (BK / 16), cb = seg % (BK / 16);
-      gb[q] = (seg < SEG_B && t0 + rb < T)
+      const int seg = tid + NT * q, rb = seg / (BK / 16), cb = seg % (BK / 16);
+      gb[q] = (seg < SEG && t0 + rb < T)
                   ? load_x16<KA16>(xq + (t0 + rb) * K, ks * BK + 16 * cb, K)
                   : make_uint4(0, 0, 0, 0);
     }
   };
   auto sstore = [&](int buf) {
     uint8_t* a = As + (buf * BM + ra) * kPitchA;
+    if constexpr (SP) {
 #pragma unroll
-    for (int c = 0; c < CPT_A; ++c) {
-      const int ch = CPT_A * pa + c;
-      uint4 v = make_uint4(expand_codes(ga[c].x, 0), expand_codes(ga[c].x, 1),
-                           expand_codes(ga[c].x, 2), expand_codes(ga[c].x, 3));
-      *(uint4*)(a + 16 * ch) = v;
-      *(uint32_t*)(a + 64 + 4 * ch) = ga[c].y;
+      for (int c = 0; c < APT / 8; ++c) {
+        const int ch = (APT / 8) * pa + c;
+        const uint32_t cw = ga[2 * c], iw = ga[2 * c + 1];
+        *(uint4*)(a + 16 * ch) = make_uint4(expand_codes(cw, 0), expand_codes(cw, 1),
+                                            expand_codes(cw, 2), expand_codes(cw, 3));
+        *(uint32_t*)(a + 64 + 4 * ch) = iw;
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < APT / 4; ++w) {
+        *(uint4*)(a + 16 * ((APT / 4) * pa + w)) =
+            make_uint4(expand_codes(ga[w], 0), expand_codes(ga[w], 1), expand_codes(ga[w], 2),
+                       expand_codes(ga[w], 3));
+      }
     }
 #pragma unroll
     for (int q = 0; q < NSEG; ++q) {
-      const int seg = tid + 256 * q, rb = seg / (BK / 16), cb = seg % (BK / 16);
-      if (seg < SEG_B) *(uint4*)(Bs + (buf * BN + rb) * kPitchBs + 16 * cb) = gb[q];
+      const int seg = tid + NT * q, rb = seg / (BK / 16), cb = seg % (BK / 16);
+      if (seg < SEG) *(uint4*)(Bs + (buf * BN + rb) * PB + 16 * cb) = gb[q];
     }
   };
 
@@ -274,32 +211,40 @@ __global__ __launch_bounds__(256) void k_gemm_sparse24(const int8_t* __restrict_
   gload(0);
   sstore(0);
   __syncthreads();
+  const int g = lane >> 4, r16 = lane & 15;
   for (int64_t ks = 0; ks < nk; ++ks) {
     const int buf = (int)(ks & 1);
     if (ks + 1 < nk) gload(ks + 1);
-    const uint8_t* a = As + buf * BM * kPitchA;
-    const uint8_t* b = Bs + buf * BN * kPitchBs;
-    const int g = lane >> 4;
-    v4i af[FI];
-    int ai[FI];
-    v8i bf[FJ];
+    const uint8_t* a = As + (buf * BM + wm * WM + r16) * kPitchA;
+    const uint8_t* b = Bs + (buf * BN + wn * WN + r16) * PB;
+    if constexpr (SP) {
+      v8i bf[FJ];
 #pragma unroll
-    for (int i = 0; i < FI; ++i) {
-      const uint8_t* r = a + (wo * WM + 16 * i + (lane & 15)) * kPitchA;
-      af[i] = *(const v4i*)(r + 16 * g);
-      ai[i] = *(const int*)(r + 64 + 4 * g);
+      for (int j = 0; j < FJ; ++j) {
+        const v4i lo = *(const v4i*)(b + 16 * j * PB + 16 * g);
+        const v4i hi = *(const v4i*)(b + 16 * j * PB + 64 + 16 * g);
+        bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < FI; ++i) {
+        const v4i af = *(const v4i*)(a + 16 * i * kPitchA + 16 * g);
+        const int ai = *(const int*)(a + 16 * i * kPitchA + 64 + 4 * g);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+          acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(af, bf[j], acc[i][j], ai, 0, 0);
+      }
+    } else {
+      v4i bf[FJ];
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) bf[j] = *(const v4i*)(b + 16 * j * PB + 16 * g);
+#pragma unroll
+      for (int i = 0; i < FI; ++i) {
+        const v4i af = *(const v4i*)(a + 16 * i * kPitchA + 16 * g);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[j], acc[i][j], 0, 0, 0);
+      }
     }
-#pragma unroll
-    for (int j = 0; j < FJ; ++j) {
-      const uint8_t* r = b + (wt * WN + 16 * j + (lane & 15)) * kPitchBs;
-      const v4i lo = *(const v4i*)(r + 16 * g), hi = *(const v4i*)(r + 64 + 16 * g);
-      bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-      for (int j = 0; j < FJ; ++j)
-        acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(af[i], bf[j], acc[i][j], ai[i], 0, 0);
     if (ks + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
   }
@@ -308,54 +253,100 @@ __global__ __launch_bounds__(256) void k_gemm_sparse24(const int8_t* __restrict_
   for (int i = 0; i < FI; ++i)
 #pragma unroll
     for (int j = 0; j < FJ; ++j) {
-      const int64_t t = t0 + wt * WN + 16 * j + (lane & 15);
-      const int64_t o = o0 + wo * WM + 16 * i + 4 * (lane >> 4);
+      const int64_t t = t0 + wn * WN + 16 * j + r16;
+      const int64_t o = o0 + wm * WM + 16 * i + 4 * g;
       store_out<YBF16>(y, acc_out, acc[i][j], t, o, T, O, sx, sw, sw_inc);
     }
 }
 
 // ---------------------------------------------------------------------------
-template <int WM, int WN, bool KA16, bool YBF16>
-static hipError_t launch_tiles(bool idx, const int8_t* xq, const float* sx, const uint8_t* packed,
-                               int64_t pitch, const float* sw, int64_t sw_inc, int64_t T,
-                               int64_t O, int64_t K, void* y, int32_t* acc, hipStream_t s) {
-  constexpr int BM = 2 * WM, BN = 2 * WN;
-  const dim3 grid((unsigned)cdiv(T, BN), (unsigned)cdiv(O, BM)), block(256);
-  if (idx) {
-    const size_t lds = 2 * (size_t)BM * kPitchA + 2 * (size_t)BN * kPitchBs;
-    hipLaunchKernelGGL((k_gemm_sparse24<WM, WN, KA16, YBF16>), grid, block, lds, s, xq, sx,
-                       packed, pitch, sw, sw_inc, T, O, K, y, acc);
-  } else {
-    const size_t lds = 2 * (size_t)BM * kPitchA + 2 * (size_t)BN * kPitchBd;
-    hipLaunchKernelGGL((k_gemm_dense<WM, WN, KA16, YBF16>), grid, block, lds, s, xq, sx, packed,
-                       pitch, sw, sw_inc, T, O, K, y, acc);
+// Tile configurations and the per-shape choice.
+// ---------------------------------------------------------------------------
+enum TileCfg { kT256x256 = 0, kT256x128 = 1, kT128x256 = 2, kT128x128 = 3, kT256x32 = 4,
+               kT128x32 = 5, kT256x256w8 = 6, kT128x256w8 = 7, kT256x128w8 = 8,
+               kT256x256w8t = 9, kNumCfg = 10 };
+
+struct Args {
+  const int8_t* xq; const float* sx; const uint8_t* packed; int64_t pitch; const float* sw;
+  int64_t sw_inc, T, O, K; void* y; int32_t* acc;
+};
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool SP, bool KA16, bool YBF16>
+static hipError_t launch_cfg(const Args& a, hipStream_t s) {
+  constexpr int PB = SP ? kPitchBs : kPitchBd;
+  const size_t lds = 2 * (size_t)BM * kPitchA + 2 * (size_t)BN * PB;
+  auto kern = k_gemm<BM, BN, WAVES_M, WAVES_N, SP, KA16, YBF16>;
+  if (lds > 65536) {
+    static bool set = false;  // attribute is per kernel; setting it twice is harmless
+    if (!set) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      set = true;
+    }
   }
+  const int64_t nb = cdiv(a.O, BM) * cdiv(a.T, BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(64 * WAVES_M * WAVES_N), lds, s, a.xq, a.sx,
+                     a.packed, a.pitch, a.sw, a.sw_inc, a.T, a.O, a.K, a.y, a.acc);
   return hipGetLastError();
 }
 
-template <bool KA16, bool YBF16>
-static hipError_t launch_gemm_k(bool idx, const int8_t* xq, const float* sx, const uint8_t* packed,
-                                int64_t pitch, const float* sw, int64_t sw_inc, int64_t T,
-                                int64_t O, int64_t K, void* y, int32_t* acc, hipStream_t s) {
-  if (T <= 32)
-    return launch_tiles<64, 16, KA16, YBF16>(idx, xq, sx, packed, pitch, sw, sw_inc, T, O, K, y, acc, s);
-  return launch_tiles<64, 64, KA16, YBF16>(idx, xq, sx, packed, pitch, sw, sw_inc, T, O, K, y, acc, s);
+template <bool SP, bool KA16, bool YBF16>
+static hipError_t launch_sel(int cfg, const Args& a, hipStream_t s) {
+  switch (cfg) {
+    case kT256x256: return launch_cfg<256, 256, 2, 2, SP, KA16, YBF16>(a, s);
+    case kT256x128: return launch_cfg<256, 128, 2, 2, SP, KA16, YBF16>(a, s);
+    case kT128x256: return launch_cfg<128, 256, 2, 2, SP, KA16, YBF16>(a, s);
+    case kT256x32: return launch_cfg<256, 32, 4, 1, SP, KA16, YBF16>(a, s);
+    case kT128x32: return launch_cfg<128, 32, 4, 1, SP, KA16, YBF16>(a, s);
+    case kT256x256w8: return launch_cfg<256, 256, 2, 4, SP, KA16, YBF16>(a, s);
+    case kT128x256w8: return launch_cfg<128, 256, 2, 4, SP, KA16, YBF16>(a, s);
+    case kT256x128w8: return launch_cfg<256, 128, 4, 2, SP, KA16, YBF16>(a, s);
+    case kT256x256w8t: return launch_cfg<256, 256, 4, 2, SP, KA16, YBF16>(a, s);
+    default: return launch_cfg<128, 128, 2, 2, SP, KA16, YBF16>(a, s);
+  }
+}
+
+// Estimated time of a configuration: rounds of workgroups over the CUs times
+// the per-workgroup MFMA work, scaled by the relative efficiency of the tile.
+static int choose_cfg(int64_t T, int64_t O, int64_t K) {
+  // tuning override (read on every call so tests can force each configuration)
+  const char* ev = std::getenv("SBL_GEMM_TILE");
+  const int forced = ev ? std::atoi(ev) : -1;
+  if (forced >= 0 && forced < kNumCfg) return forced;
+  if (T <= 32) return O >= 8192 ? kT256x32 : kT128x32;
+  const int cus = device_info().cus;
+  struct C { int cfg, bm, bn, per_cu; double eff; };
+  const C cs[] = {{kT256x256, 256, 256, 1, 1.0}, {kT256x128, 256, 128, 2, 0.85},
+                  {kT128x256, 128, 256, 2, 0.85}, {kT128x128, 128, 128, 2, 0.6}};
+  int best = kT128x128;
+  double best_t = 1e30;
+  for (const C& c : cs) {
+    const double nb = (double)cdiv(O, c.bm) * (double)cdiv(T, c.bn);
+    const double rounds = std::ceil(nb / (double)(cus * c.per_cu));
+    const double t = rounds * c.per_cu * (double)c.bm * c.bn * (double)K / c.eff;
+    if (t < best_t) { best_t = t; best = c.cfg; }
+  }
+  return best;
 }
 
 hipError_t launch_gemm(const int8_t* xq, const float* sx, const void* packed, const float* sw,
                        int64_t sw_inc, int64_t T, int64_t O, int64_t K, int N, int M, void* y,
                        bool y_bf16, int32_t* acc, hipStream_t s) {
   if (T == 0 || O == 0) return hipSuccess;
-  const bool idx = index_form(N, M);
-  const int64_t pitch = row_pitch(K, N, M);
-  const uint8_t* p = (const uint8_t*)packed;
+  const bool sp = index_form(N, M);
+  const Args a{xq, sx, (const uint8_t*)packed, row_pitch(K, N, M), sw, sw_inc, T, O, K, y, acc};
+  const int cfg = choose_cfg(T, O, K);
   const bool ka16 = (K % 16) == 0;
-  if (ka16) {
-    return y_bf16 ? launch_gemm_k<true, true>(idx, xq, sx, p, pitch, sw, sw_inc, T, O, K, y, acc, s)
-                  : launch_gemm_k<true, false>(idx, xq, sx, p, pitch, sw, sw_inc, T, O, K, y, acc, s);
+#define SBL_DISPATCH(SPV, KAV, YV) return launch_sel<SPV, KAV, YV>(cfg, a, s)
+  if (sp) {
+    if (ka16) { if (y_bf16) SBL_DISPATCH(true, true, true); else SBL_DISPATCH(true, true, false); }
+    else { if (y_bf16) SBL_DISPATCH(true, false, true); else SBL_DISPATCH(true, false, false); }
+  } else {
+    if (ka16) { if (y_bf16) SBL_DISPATCH(false, true, true); else SBL_DISPATCH(false, true, false); }
+    else { if (y_bf16) SBL_DISPATCH(false, false, true); else SBL_DISPATCH(false, false, false); }
   }
-  return y_bf16 ? launch_gemm_k<false, true>(idx, xq, sx, p, pitch, sw, sw_inc, T, O, K, y, acc, s)
-                : launch_gemm_k<false, false>(idx, xq, sx, p, pitch, sw, sw_inc, T, O, K, y, acc, s);
+#undef SBL_DISPATCH
 }
 
 }  // namespace sbl

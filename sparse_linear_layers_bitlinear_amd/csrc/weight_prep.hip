@@ -67,10 +67,10 @@ __global__ __launch_bounds__(256) void k_absmean_partial(const void* __restrict_
   __syncthreads();
   AbsSlot st;
   constexpr int V = BF16 ? 8 : 4;  // elements per 16-byte load
+  constexpr int U = 8;             // loads in flight per thread
   const int64_t nvec = n / V;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) {
-    const uint4 d = *((const uint4*)wv + i);
+  auto consume = [&](const uint4& d) {
     const uint32_t w[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -81,12 +81,21 @@ __global__ __launch_bounds__(256) void k_absmean_partial(const void* __restrict_
         abs_accumulate(st, bins, w[h]);
       }
     }
+  };
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + (U - 1) * stride < nvec; i += U * stride) {
+    uint4 d[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[u] = *((const uint4*)wv + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) consume(d[u]);
   }
+  for (; i < nvec; i += stride) consume(*((const uint4*)wv + i));
   // tail elements (n % V) by block 0
   if (blockIdx.x == 0) {
-    for (int64_t i = nvec * V + threadIdx.x; i < n; i += blockDim.x) {
-      const uint32_t u = BF16 ? ((uint32_t)((const uint16_t*)wv)[i] << 16)
-                              : ((const uint32_t*)wv)[i];
+    for (int64_t j = nvec * V + threadIdx.x; j < n; j += blockDim.x) {
+      const uint32_t u = BF16 ? ((uint32_t)((const uint16_t*)wv)[j] << 16)
+                              : ((const uint32_t*)wv)[j];
       abs_accumulate(st, bins, u);
     }
   }
@@ -124,64 +133,94 @@ __global__ __launch_bounds__(256) void k_absmean_finalize(const unsigned long lo
                                                           int nblocks, int64_t n, float eps,
                                                           float* __restrict__ gamma_sw,
                                                           PrepScalars* __restrict__ scal) {
-  __shared__ unsigned long long red[16][256];
+  // thread t sums the 16 bins of blocks t, t + 256, ... (all loads independent),
+  // then a wave reduction and a 4-way combine in LDS
+  __shared__ unsigned long long red[4][16];
   unsigned long long acc[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc[j] = 0;
   for (int b = threadIdx.x; b < nblocks; b += 256) {
+    const uint4* p = (const uint4*)(partials + (int64_t)b * 16);
+    uint4 v[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] += partials[(int64_t)b * 16 + j];
-  }
+    for (int q = 0; q < 8; ++q) v[q] = p[q];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) red[j][threadIdx.x] = acc[j];
-  __syncthreads();
-  for (int s = 128; s >= 1; s >>= 1) {
-    if ((int)threadIdx.x < s) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) red[j][threadIdx.x] += red[j][threadIdx.x + s];
+    for (int q = 0; q < 8; ++q) {
+      acc[2 * q] += (unsigned long long)v[q].x | ((unsigned long long)v[q].y << 32);
+      acc[2 * q + 1] += (unsigned long long)v[q].z | ((unsigned long long)v[q].w << 32);
     }
-    __syncthreads();
   }
+  // two-level reduction through LDS: 256 x 16 -> 16 x 16 -> 16
+  __shared__ unsigned long long part[16][257];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) part[j][threadIdx.x] = acc[j];
+  __syncthreads();
+  {
+    const int col = threadIdx.x & 15, grp = threadIdx.x >> 4;  // 16 groups of 16 rows
+    unsigned long long sum = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += part[col][grp * 16 + r];
+    __syncthreads();
+    part[col][grp] = sum;
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    unsigned long long sum = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += part[threadIdx.x][r];
+    red[0][threadIdx.x] = sum;
+    red[1][threadIdx.x] = red[2][threadIdx.x] = red[3][threadIdx.x] = 0;
+  }
+  __syncthreads();
   if (threadIdx.x != 0) return;
 
-  // Exact sum in units of 2^-150 as 32-bit limbs.
-  unsigned long long limb[14];
+  // Exact sum in units of 2^-150 as 32-bit limbs (registers only: constant indices).
+  constexpr int NL = 12;
+  uint32_t L[NL];
+  {
+    unsigned long long w[NL + 1];
 #pragma unroll
-  for (int i = 0; i < 14; ++i) limb[i] = 0;
-  for (int tag = 0; tag < 8; ++tag) {
-    const unsigned long long lo = red[2 * tag][0], hi = red[2 * tag + 1][0];
-    limb[tag] += lo & 0xFFFFFFFFull;
-    limb[tag + 1] += lo >> 32;
-    limb[tag + 1] += hi & 0xFFFFFFFFull;
-    limb[tag + 2] += hi >> 32;
-  }
-  for (int i = 0; i < 13; ++i) {
-    limb[i + 1] += limb[i] >> 32;
-    limb[i] &= 0xFFFFFFFFull;
+    for (int i = 0; i <= NL; ++i) w[i] = 0;
+#pragma unroll
+    for (int tag = 0; tag < 8; ++tag) {
+      const unsigned long long lo = red[0][2 * tag] + red[1][2 * tag] + red[2][2 * tag] + red[3][2 * tag];
+      const unsigned long long hi = red[0][2 * tag + 1] + red[1][2 * tag + 1] + red[2][2 * tag + 1] +
+                                    red[3][2 * tag + 1];
+      w[tag] += lo & 0xFFFFFFFFull;
+      w[tag + 1] += (lo >> 32) + (hi & 0xFFFFFFFFull);
+      w[tag + 2] += hi >> 32;
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      w[i + 1] += w[i] >> 32;
+      L[i] = (uint32_t)w[i];
+    }
   }
   int top = -1;
-  for (int i = 13; i >= 0; --i)
-    if (limb[i]) { top = i; break; }
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    if (L[i]) top = i;
   double S = 0.0;
   if (top >= 0) {
-    const int p = 32 * top + (31 - __clz((uint32_t)limb[top]));  // highest set bit
-    auto bit = [&](int i) -> unsigned long long {
-      return i < 0 ? 0ull : (limb[i >> 5] >> (i & 31)) & 1ull;
-    };
-    if (p <= 52) {
-      unsigned long long v = 0;
-      for (int i = p; i >= 0; --i) v = (v << 1) | bit(i);
-      S = ldexp((double)v, -150);
-    } else {
-      unsigned long long mant = 0;
-      for (int i = p; i >= p - 52; --i) mant = (mant << 1) | bit(i);
-      const unsigned long long rb = bit(p - 53);
-      bool sticky = false;
-      for (int i = p - 54; i >= 0; --i)
-        if (bit(i)) { sticky = true; break; }
-      if (rb && (sticky || (mant & 1ull))) ++mant;  // round to nearest, ties to even
-      S = ldexp((double)mant, p - 52 - 150);
+    // 96-bit window of the three highest limbs, plus a sticky bit for the rest
+    uint32_t h = 0, m = 0, l = 0;
+    bool below = false;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      if (i == top) h = L[i];
+      if (i == top - 1) m = L[i];
+      if (i == top - 2) l = L[i];
+      if (i < top - 2 && L[i]) below = true;
     }
+    const int c = __clz(h);                               // h != 0
+    unsigned __int128 V = ((unsigned __int128)h << 64) | ((unsigned __int128)m << 32) | l;
+    V <<= c;                                              // bit 95 set
+    unsigned long long mant = (unsigned long long)(V >> 43) & ((1ull << 53) - 1);
+    const bool rb = (V >> 42) & 1;
+    const bool sticky = below || ((V & (((unsigned __int128)1 << 42) - 1)) != 0);
+    if (rb && (sticky || (mant & 1ull))) ++mant;          // nearest, ties to even
+    // value = V_window * 2^(32*(top-2)) * 2^-150, V_window = mant * 2^(43 - c)
+    S = ldexp((double)mant, 43 - c + 32 * (top - 2) - 150);
   }
   const double q = S / (double)n;
   const float gamma = (float)q;
@@ -205,22 +244,46 @@ __global__ __launch_bounds__(256) void k_absmean_finalize(const unsigned long lo
 constexpr int kChunksPerBlock = 256;
 constexpr int kLdsStride = 33;
 
+// Keep bits of one group of M magnitudes (bit i = slot i kept):
+// rank_i = #{j : |w_j| > |w_i|} + #{j < i : |w_j| == |w_i|}; keep iff rank_i < N.
+// With c = [a_j > a_i] for a pair i < j: rank_i gains c and rank_j gains 1 - c,
+// so rank = sum_i i<<4i-style base + sum over pairs of c * (field_i - field_j),
+// held as 4-bit fields of one register (final values are in [0, M-1]).
 template <int M>
 __device__ __forceinline__ uint32_t topn_keep_bits(const uint32_t* a, int N) {
-  // rank_i = #{j : |w_j| > |w_i|} + #{j < i : |w_j| == |w_i|}; keep iff rank_i < N
-  int rank[M];
+  uint32_t R = 0;
 #pragma unroll
-  for (int i = 0; i < M; ++i) rank[i] = 0;
+  for (int i = 0; i < M; ++i) R += (uint32_t)i << (4 * i);
 #pragma unroll
   for (int i = 0; i < M; ++i)
 #pragma unroll
-    for (int j = i + 1; j < M; ++j) {
-      if (a[j] > a[i]) ++rank[i]; else ++rank[j];
-    }
+    for (int j = i + 1; j < M; ++j)
+      R += (a[j] > a[i]) ? ((1u << (4 * i)) - (1u << (4 * j))) : 0u;
   uint32_t keep = 0;
 #pragma unroll
-  for (int i = 0; i < M; ++i) keep |= (rank[i] < N ? 1u : 0u) << i;
+  for (int i = 0; i < M; ++i) keep |= (((R >> (4 * i)) & 15u) < (uint32_t)N ? 1u : 0u) << i;
   return keep;
+}
+
+// Byte-slice 16 two-bit fields: bit u of lo (u = 4b + a) -> bit 8a + 2b, and
+// the same for hi one position up; i.e. a 4x4 transpose of 2-bit cells.
+__device__ __forceinline__ uint32_t byte_slice16(uint32_t lo, uint32_t hi) {
+  // interleave: bit u of lo -> 2u, bit u of hi -> 2u + 1
+  auto spread = [](uint32_t x) {
+    x &= 0xFFFFu;
+    x = (x | (x << 8)) & 0x00FF00FFu;
+    x = (x | (x << 4)) & 0x0F0F0F0Fu;
+    x = (x | (x << 2)) & 0x33333333u;
+    x = (x | (x << 1)) & 0x55555555u;
+    return x;
+  };
+  uint32_t v = spread(lo) | (spread(hi) << 1);   // cell (b, a) at 8b + 2a
+  // transpose the 4x4 matrix of 2-bit cells: (b, a) -> (a, b)
+  uint32_t t = (v ^ (v >> 6)) & 0x00CC00CCu;      // swap cells at distance (1,-1)
+  v ^= t ^ (t << 6);
+  t = (v ^ (v >> 12)) & 0x0000F0F0u;              // swap 2x2 blocks
+  v ^= t ^ (t << 12);
+  return v;
 }
 
 template <bool BF16, int M, bool IDX>
@@ -232,112 +295,109 @@ __global__ __launch_bounds__(256) void k_qmp(const void* __restrict__ wv, int64_
                                              uint8_t* __restrict__ mask_out,
                                              float* __restrict__ sw_rows) {
   __shared__ uint32_t lds[kChunksPerBlock * kLdsStride];
-  const int64_t total = O * C;
-  const int64_t base = (int64_t)blockIdx.x * kChunksPerBlock;
+  // all chunk/row indices fit in 32 bits: O * C < 2^31 (O * K < 2^31)
+  const uint32_t total = (uint32_t)(O * C), C32 = (uint32_t)C, K32 = (uint32_t)K;
+  const uint32_t base = blockIdx.x * kChunksPerBlock;
 
-  // ---- stage: |w| bits (sign kept) of 256 chunks x 32 elements ----
+  // ---- stage: raw bits of 256 chunks x 32 elements ----
   constexpr int V = BF16 ? 8 : 4;              // elements per 16-byte piece
-  constexpr int PIECES = 32 / V;               // pieces per chunk
-  for (int p = threadIdx.x; p < kChunksPerBlock * PIECES; p += 256) {
-    const int lc = p / PIECES, pc = p % PIECES;
-    const int64_t ch = base + lc;
-    uint32_t vals[V];
+  constexpr int PIECES = 32 / V;               // pieces per chunk = pieces per thread
+  const bool rows16 = ((K32 * (BF16 ? 2u : 4u)) % 16u) == 0;
+  uint4 d[PIECES];
 #pragma unroll
-    for (int e = 0; e < V; ++e) vals[e] = 0;
+  for (int q = 0; q < PIECES; ++q) {
+    const uint32_t p = threadIdx.x + 256u * q;
+    const uint32_t ch = base + p / PIECES, pc = p % PIECES;
+    d[q] = make_uint4(0, 0, 0, 0);
     if (ch < total) {
-      const int64_t o = ch / C, c = ch % C;
-      const int64_t k = 32 * c + (int64_t)V * pc;
-      if (k < K) {  // K % 4 == 0; a piece is whole when k + V <= K
-        if (k + V <= K && ((K * (BF16 ? 2 : 4)) % 16 == 0)) {
-          const uint4 d = BF16 ? *(const uint4*)((const uint16_t*)wv + o * K + k)
-                               : *(const uint4*)((const float*)wv + o * K + k);
-          const uint32_t w[4] = {d.x, d.y, d.z, d.w};
-          if constexpr (BF16) {
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              vals[2 * h] = (w[h] & 0xFFFFu) << 16;
-              vals[2 * h + 1] = w[h] & 0xFFFF0000u;
-            }
-          } else {
-#pragma unroll
-            for (int h = 0; h < 4; ++h) vals[h] = w[h];
-          }
-        } else {
-          for (int e = 0; e < V && k + e < K; ++e)
-            vals[e] = BF16 ? ((uint32_t)((const uint16_t*)wv)[o * K + k + e] << 16)
-                           : ((const uint32_t*)wv)[o * K + k + e];
+      const uint32_t o = ch / C32, c = ch - o * C32;
+      const uint32_t k = 32u * c + V * pc;
+      const int64_t off = (int64_t)o * K + k;
+      if (k + V <= K32 && rows16) {
+        d[q] = BF16 ? *(const uint4*)((const uint16_t*)wv + off)
+                    : *(const uint4*)((const float*)wv + off);
+      } else if (k < K32) {  // K % 4 == 0: a partial piece holds whole 4-element groups
+        uint32_t t[4] = {0, 0, 0, 0};
+        for (uint32_t e = 0; e < (uint32_t)V && k + e < K32; ++e) {
+          const uint32_t u = BF16 ? (uint32_t)((const uint16_t*)wv)[off + e]
+                                  : ((const uint32_t*)wv)[off + e];
+          if constexpr (BF16) t[e >> 1] |= u << (16 * (e & 1)); else t[e] = u;
         }
+        d[q] = make_uint4(t[0], t[1], t[2], t[3]);
       }
     }
+  }
 #pragma unroll
-    for (int e = 0; e < V; ++e) lds[lc * kLdsStride + pc * V + e] = vals[e];
+  for (int q = 0; q < PIECES; ++q) {
+    const uint32_t p = threadIdx.x + 256u * q;
+    const uint32_t lc = p / PIECES, pc = p % PIECES;
+    const uint32_t w[4] = {d[q].x, d[q].y, d[q].z, d[q].w};
+    uint32_t* dst = lds + lc * kLdsStride + pc * V;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        dst[2 * h] = (w[h] & 0xFFFFu) << 16;
+        dst[2 * h + 1] = w[h] & 0xFFFF0000u;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) dst[h] = w[h];
+    }
   }
   __syncthreads();
 
-  const int64_t ch = base + threadIdx.x;
+  const uint32_t ch = base + threadIdx.x;
   if (ch >= total) return;
-  const int64_t o = ch / C, c = ch % C;
-  const int64_t k0 = 32 * c;
+  const uint32_t o = ch / C32, c = ch - o * C32;
+  const uint32_t k0 = 32u * c;
   const uint32_t tb = scal->t_bits;
 
-  uint32_t a[32], sgn = 0;
+  uint32_t a[32], sgn = 0, nz = 0;
 #pragma unroll
   for (int e = 0; e < 32; ++e) {
     const uint32_t u = lds[threadIdx.x * kLdsStride + e];
     a[e] = u & 0x7FFFFFFFu;
     sgn |= (u >> 31) << e;
+    nz |= ((tb - 1u - a[e]) >> 31) << e;          // a >= tb  (both < 2^31, tb >= 1)
   }
-  // valid elements of this chunk: k0 + e < K
-  const int64_t rem = K - k0;
-  const uint32_t valid = rem >= 32 ? 0xFFFFFFFFu : (rem <= 0 ? 0u : ((1u << rem) - 1u));
+  const uint32_t valid = k0 >= K32 ? 0u : (K32 - k0 >= 32u ? 0xFFFFFFFFu : ((1u << (K32 - k0)) - 1u));
 
   uint32_t keep = 0;
 #pragma unroll
   for (int g = 0; g < 32 / M; ++g) keep |= topn_keep_bits<M>(a + g * M, N) << (g * M);
-  uint32_t nz = 0;  // code != 0
-#pragma unroll
-  for (int e = 0; e < 32; ++e) nz |= (a[e] >= tb ? 1u : 0u) << e;
-  const uint32_t kept_nz = nz & keep & valid;
+  const uint32_t kn = nz & keep & valid;          // nonzero code, kept
+  const uint32_t kneg = kn & sgn;                 // ... and negative
 
   // optional unpacked outputs (k < K only)
   if (w_eff || mask_out) {
     for (int e = 0; e < 32; ++e) {
       if (!((valid >> e) & 1u)) break;
-      const int64_t idx = o * K + k0 + e;
-      if (w_eff) w_eff[idx] = ((kept_nz >> e) & 1u) ? (((sgn >> e) & 1u) ? (int8_t)-1 : (int8_t)1) : (int8_t)0;
+      const int64_t idx = (int64_t)o * K + k0 + e;
+      if (w_eff) w_eff[idx] = ((kn >> e) & 1u) ? (((kneg >> e) & 1u) ? (int8_t)-1 : (int8_t)1) : (int8_t)0;
       if (mask_out) mask_out[idx] = (uint8_t)((keep & valid) >> e & 1u);
     }
   }
   if (sw_rows && c == 0) sw_rows[o] = scal->sw;
 
-  uint8_t* rec = packed ? packed + o * pitch : nullptr;
-  if (!rec) return;
+  if (!packed) return;
+  uint8_t* rec = packed + (int64_t)o * pitch;
   if constexpr (IDX) {
     // 8 groups of 4: kept slots i0 < i1 (exactly two; padding groups keep 0,1)
-    uint32_t cw = 0, iw = 0;
+    uint32_t iw = 0, lo = 0, hi = 0;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const uint32_t kb = (keep >> (4 * q)) & 0xFu;
       const uint32_t i0 = __builtin_ctz(kb | 0x10u);
       const uint32_t i1 = 31u - __builtin_clz(kb | 1u);
       iw |= (i0 | (i1 << 2)) << (4 * q);
-      const uint32_t s0 = 4 * q + i0, s1 = 4 * q + i1;
-      const uint32_t f0 = ((kept_nz >> s0) & 1u) ? (((sgn >> s0) & 1u) ? 3u : 1u) : 0u;
-      const uint32_t f1 = ((kept_nz >> s1) & 1u) ? (((sgn >> s1) & 1u) ? 3u : 1u) : 0u;
-      cw |= f0 << field_shift(2 * q);
-      cw |= f1 << field_shift(2 * q + 1);
+      lo |= ((kn >> (4 * q + i0)) & 1u) << (2 * q) | ((kn >> (4 * q + i1)) & 1u) << (2 * q + 1);
+      hi |= ((kneg >> (4 * q + i0)) & 1u) << (2 * q) | ((kneg >> (4 * q + i1)) & 1u) << (2 * q + 1);
     }
-    *(uint2*)(rec + 8 * c) = make_uint2(cw, iw);
+    *(uint2*)(rec + 8 * c) = make_uint2(byte_slice16(lo, hi), iw);
   } else {
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const uint32_t f0 = ((kept_nz >> u) & 1u) ? (((sgn >> u) & 1u) ? 3u : 1u) : 0u;
-      const uint32_t f1 = ((kept_nz >> (u + 16)) & 1u) ? (((sgn >> (u + 16)) & 1u) ? 3u : 1u) : 0u;
-      w0 |= f0 << field_shift(u);
-      w1 |= f1 << field_shift(u);
-    }
-    if (c < code_chunks) *(uint2*)(rec + 8 * c) = make_uint2(w0, w1);
+    const uint32_t w0 = byte_slice16(kn & 0xFFFFu, kneg & 0xFFFFu);
+    const uint32_t w1 = byte_slice16(kn >> 16, kneg >> 16);
+    if (c < (uint32_t)code_chunks) *(uint2*)(rec + 8 * c) = make_uint2(w0, w1);
     *(uint32_t*)(rec + mask_off + 4 * c) = keep & valid;
   }
 }
@@ -370,8 +430,9 @@ hipError_t launch_quant_mask_weight(const void* w, bool bf16, int64_t O, int64_t
   auto* partials = (unsigned long long*)ws;
   auto* scal = (PrepScalars*)((char*)ws + (size_t)kAbsmeanMaxBlocks * 16 * sizeof(unsigned long long));
   const int V = bf16 ? 8 : 4;
-  int64_t want = cdiv(cdiv(n, V), 256 * 8);  // >= 8 vectors per thread
-  int nblocks = (int)(want < 1 ? 1 : (want > kAbsmeanMaxBlocks ? kAbsmeanMaxBlocks : want));
+  // about 8 vectors per thread, at most 512 blocks (two per CU)
+  const int64_t want = cdiv(cdiv(n, V), 256 * 8);
+  const int nblocks = (int)(want < 1 ? 1 : (want > 512 ? 512 : want));
   if (bf16)
     hipLaunchKernelGGL((k_absmean_partial<true>), dim3(nblocks), dim3(256), 0, s, w, n, partials);
   else
