@@ -21,11 +21,11 @@
 // index word), and B lane l = column l%16 with dense k in [16g, 16g+16) and
 // [64+16g, 64+16g+16).
 //
-// Tiles: 4 wavefronts per workgroup in a 2 (o) x 2 (t) grid, each wave a
-// WM x WN block of 16x16 MFMA tiles; K advances BK = 64 (dense) or 128
-// (2:4) per step; LDS is double-buffered so global loads of step s+1 overlap
-// the MFMAs of step s. Row pitches of 80 / 144 bytes make the 16-byte
-// fragment reads bank-conflict free.
+// Tiles: 4 or 8 wavefronts per workgroup, each owning a block of 16x16 MFMA
+// tiles; K advances BK = 64 (dense) or 128 (2:4) per step; LDS is
+// double-buffered so global loads of step s+1 overlap the MFMAs of step s.
+// Staged rows have pitches of 80 / 144 bytes so that the 16-byte fragment
+// reads of 16 consecutive rows fall in distinct banks.
 #include "sbl_internal.h"
 #include "device_util.cuh"
 
@@ -37,6 +37,7 @@ namespace sbl {
 constexpr int kPitchA = 80;    // bytes per staged W row (64 values + 16 pad / index)
 constexpr int kPitchBd = 80;   // bytes per staged xq row, dense (64 k)
 constexpr int kPitchBs = 144;  // bytes per staged xq row, 2:4 (128 k)
+
 
 template <bool KA16>
 __device__ __forceinline__ uint4 load_x16(const int8_t* __restrict__ row, int64_t k, int64_t K) {
@@ -87,6 +88,39 @@ __device__ __forceinline__ void store_out(void* __restrict__ y, int32_t* __restr
   }
 }
 
+// Epilogue of one 16x16 tile slice held by a lane: outputs o..o+3 of token t.
+// y = fp32(fp32(acc * sx[t]) * sw[o]), rounded to bf16 (RNE) or kept fp32.
+template <bool YBF16>
+__device__ __forceinline__ void store_tile(void* __restrict__ y, int32_t* __restrict__ acc_out,
+                                           const v4i& c, int t, int o, int O, float s_t,
+                                           const float* __restrict__ sw, int sw_inc) {
+  float v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float a = (float)c[r] * s_t;
+    v[r] = a * sw[min(o + r, O - 1) * sw_inc];
+  }
+  const int64_t base = (int64_t)t * O + o;
+  if (o + 3 < O && (O & 3) == 0) {
+    if constexpr (YBF16) {
+      const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+      const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+      *(uint2*)((uint16_t*)y + base) = make_uint2(lo, hi);
+    } else {
+      *(float4*)((float*)y + base) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    if (acc_out) *(int4*)(acc_out + base) = make_int4(c[0], c[1], c[2], c[3]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (o + r >= O) break;
+      if constexpr (YBF16) ((uint16_t*)y)[base + r] = (uint16_t)f32_to_bf16_bits(v[r]);
+      else ((float*)y)[base + r] = v[r];
+      if (acc_out) acc_out[base + r] = c[r];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, each with
 // its own L2. Block b runs on XCD b % 8; renumber so every XCD owns one
@@ -116,8 +150,9 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nb, int64_t ntm, in
 // v_smfmac_i32_16x16x128_i8. Waves are arranged WAVES_M (along O) x WAVES_N
 // (along T); each owns a (BM/WAVES_M) x (BN/WAVES_N) block of 16x16 tiles.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool SP, bool KA16, bool YBF16>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(1, 2)))
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool SP, bool KA16, bool YBF16,
+          int MAXW = ((BM / WAVES_M) * (BN / WAVES_N) >= 128 * 128 ? 1 : 2)>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(1, MAXW)))
 void k_gemm(const int8_t* __restrict__ xq, const float* __restrict__ sx,
             const uint8_t* __restrict__ packed, int64_t pitch, const float* __restrict__ sw,
             int64_t sw_inc, int64_t T, int64_t O, int64_t K, void* __restrict__ y,
@@ -130,7 +165,8 @@ void k_gemm(const int8_t* __restrict__ xq, const float* __restrict__ sx,
   constexpr int AROW = SP ? 32 : 16;          // packed bytes per W row per K-step
   constexpr int APT = BM * AROW / NT;          // packed bytes per thread per K-step
   constexpr int TPR = AROW / APT;              // threads per W row
-  constexpr int SEG = BN * BK / 16;            // 16-byte xq segments per K-step
+  constexpr int SEGR = BK / 16;                // 16-byte xq segments per row per K-step
+  constexpr int SEG = BN * SEGR;
   constexpr int NSEG = (SEG + NT - 1) / NT;
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
   static_assert(APT >= (SP ? 8 : 4) && APT <= 32 && AROW % APT == 0, "A staging");
@@ -143,41 +179,58 @@ void k_gemm(const int8_t* __restrict__ xq, const float* __restrict__ sx,
   const int64_t ntm = cdiv(O, BM), ntn = cdiv(T, BN);
   int64_t tm, tn;
   tile_of(blockIdx.x, ntm * ntn, ntm, ntn, tm, tn);
-  const int64_t o0 = tm * BM, t0 = tn * BN;
-  const int64_t nk = cdiv(K, BK);
+  const int o0 = (int)(tm * BM), t0 = (int)(tn * BN);
+  const int Oi = (int)O, Ti = (int)T, Ki = (int)K;
+  const int nkf = Ki / BK;                     // full K-steps
+  const int nk = (Ki + BK - 1) / BK;           // plus a masked tail step if K % BK != 0
 
+  // Staging sources: consecutive lanes read consecutive 16-byte segments of a
+  // row. Rows past O / T are clamped to the last valid row: they stay in
+  // bounds and only feed accumulators that are never stored.
   const int ra = tid / TPR, pa = tid % TPR;
-  const bool va = o0 + ra < O;
-  const uint8_t* arow = packed + (o0 + ra) * pitch + APT * pa;
+  const uint8_t* ap = packed + (int64_t)min(o0 + ra, Oi - 1) * pitch + APT * pa;
+  const int8_t* bp[NSEG];
+  int boff[NSEG];
+#pragma unroll
+  for (int q = 0; q < NSEG; ++q) {
+    const int seg = min(tid + NT * q, SEG - 1);
+    const int rb = seg / SEGR, cb = seg % SEGR;
+    bp[q] = xq + (int64_t)min(t0 + rb, Ti - 1) * K + 16 * cb;
+    boff[q] = rb * PB + 16 * cb;
+  }
+  const int aoff = ra * kPitchA;
 
   uint32_t ga[APT / 4];
   uint4 gb[NSEG];
-  auto gload = [&](int64_t ks) {
-    const uint8_t* p = arow + ks * AROW;
+  auto gload = [&](int ks) {
+    const uint8_t* p = ap + (int64_t)ks * AROW;
     if constexpr (APT == 32) {
-      uint4 v0 = va ? *(const uint4*)p : make_uint4(0, SP ? 0x44444444u : 0, 0, SP ? 0x44444444u : 0);
-      uint4 v1 = va ? *(const uint4*)(p + 16) : v0;
+      const uint4 v0 = *(const uint4*)p, v1 = *(const uint4*)(p + 16);
       ga[0] = v0.x; ga[1] = v0.y; ga[2] = v0.z; ga[3] = v0.w;
       ga[4] = v1.x; ga[5] = v1.y; ga[6] = v1.z; ga[7] = v1.w;
     } else if constexpr (APT == 16) {
-      uint4 v = va ? *(const uint4*)p : make_uint4(0, SP ? 0x44444444u : 0, 0, SP ? 0x44444444u : 0);
+      const uint4 v = *(const uint4*)p;
       ga[0] = v.x; ga[1] = v.y; ga[2] = v.z; ga[3] = v.w;
     } else if constexpr (APT == 8) {
-      uint2 v = va ? *(const uint2*)p : make_uint2(0, SP ? 0x44444444u : 0);
+      const uint2 v = *(const uint2*)p;
       ga[0] = v.x; ga[1] = v.y;
     } else {
-      ga[0] = va ? *(const uint32_t*)p : 0u;
+      ga[0] = *(const uint32_t*)p;
     }
+    const int kb = ks * BK;
+    if (KA16 && ks < nkf) {
 #pragma unroll
-    for (int q = 0; q < NSEG; ++q) {
-      const int seg = tid + NT * q, rb = seg / (BK / 16), cb = seg % (BK / 16);
-      gb[q] = (seg < SEG && t0 + rb < T)
-                  ? load_x16<KA16>(xq + (t0 + rb) * K, ks * BK + 16 * cb, K)
-                  : make_uint4(0, 0, 0, 0);
+      for (int q = 0; q < NSEG; ++q) gb[q] = *(const uint4*)(bp[q] + kb);
+    } else {  // tail step, or rows only 4-byte aligned
+#pragma unroll
+      for (int q = 0; q < NSEG; ++q) {
+        const int cb = min(tid + NT * q, SEG - 1) % SEGR;
+        gb[q] = load_x16<KA16>(bp[q] - 16 * cb, kb + 16 * cb, K);
+      }
     }
   };
   auto sstore = [&](int buf) {
-    uint8_t* a = As + (buf * BM + ra) * kPitchA;
+    uint8_t* a = As + buf * BM * kPitchA + aoff;
     if constexpr (SP) {
 #pragma unroll
       for (int c = 0; c < APT / 8; ++c) {
@@ -195,11 +248,10 @@ void k_gemm(const int8_t* __restrict__ xq, const float* __restrict__ sx,
                        expand_codes(ga[w], 3));
       }
     }
+    uint8_t* b = Bs + buf * BN * PB;
 #pragma unroll
-    for (int q = 0; q < NSEG; ++q) {
-      const int seg = tid + NT * q, rb = seg / (BK / 16), cb = seg % (BK / 16);
-      if (seg < SEG) *(uint4*)(Bs + (buf * BN + rb) * PB + 16 * cb) = gb[q];
-    }
+    for (int q = 0; q < NSEG; ++q)
+      if (NSEG * NT == SEG || tid + NT * q < SEG) *(uint4*)(b + boff[q]) = gb[q];
   };
 
   v4i acc[FI][FJ];
@@ -212,13 +264,22 @@ void k_gemm(const int8_t* __restrict__ xq, const float* __restrict__ sx,
   sstore(0);
   __syncthreads();
   const int g = lane >> 4, r16 = lane & 15;
-  for (int64_t ks = 0; ks < nk; ++ks) {
-    const int buf = (int)(ks & 1);
+  const int afrag = (wm * WM + r16) * kPitchA, bfrag = (wn * WN + r16) * PB;
+  for (int ks = 0; ks < nk; ++ks) {
+    const int buf = ks & 1;
     if (ks + 1 < nk) gload(ks + 1);
-    const uint8_t* a = As + (buf * BM + wm * WM + r16) * kPitchA;
-    const uint8_t* b = Bs + (buf * BN + wn * WN + r16) * PB;
+    const uint8_t* a = As + buf * BM * kPitchA + afrag;
+    const uint8_t* b = Bs + buf * BN * PB + bfrag;
+    // all fragments of this K-step are requested before the first MFMA
     if constexpr (SP) {
       v8i bf[FJ];
+      v4i af[FI];
+      int ai[FI];
+#pragma unroll
+      for (int i = 0; i < FI; ++i) {
+        af[i] = *(const v4i*)(a + 16 * i * kPitchA + 16 * g);
+        ai[i] = *(const int*)(a + 16 * i * kPitchA + 64 + 4 * g);
+      }
 #pragma unroll
       for (int j = 0; j < FJ; ++j) {
         const v4i lo = *(const v4i*)(b + 16 * j * PB + 16 * g);
@@ -226,37 +287,337 @@ void k_gemm(const int8_t* __restrict__ xq, const float* __restrict__ sx,
         bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
 #pragma unroll
-      for (int i = 0; i < FI; ++i) {
-        const v4i af = *(const v4i*)(a + 16 * i * kPitchA + 16 * g);
-        const int ai = *(const int*)(a + 16 * i * kPitchA + 64 + 4 * g);
+      for (int j = 0; j < FJ; ++j)
 #pragma unroll
-        for (int j = 0; j < FJ; ++j)
-          acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(af, bf[j], acc[i][j], ai, 0, 0);
-      }
+        for (int i = 0; i < FI; ++i)
+          acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(af[i], bf[j], acc[i][j], ai[i], 0, 0);
     } else {
-      v4i bf[FJ];
+      v4i bf[FJ], af[FI];
+#pragma unroll
+      for (int i = 0; i < FI; ++i) af[i] = *(const v4i*)(a + 16 * i * kPitchA + 16 * g);
 #pragma unroll
       for (int j = 0; j < FJ; ++j) bf[j] = *(const v4i*)(b + 16 * j * PB + 16 * g);
 #pragma unroll
-      for (int i = 0; i < FI; ++i) {
-        const v4i af = *(const v4i*)(a + 16 * i * kPitchA + 16 * g);
+      for (int j = 0; j < FJ; ++j)
 #pragma unroll
-        for (int j = 0; j < FJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, bf[j], acc[i][j], 0, 0, 0);
-      }
+        for (int i = 0; i < FI; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
     if (ks + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
   }
 
+  // epilogue: one token column per lane and j; four consecutive outputs per tile
+#pragma unroll
+  for (int j = 0; j < FJ; ++j) {
+    const int t = t0 + wn * WN + 16 * j + r16;
+    if (t >= Ti) continue;
+    const float s_t = sx[t];
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const int o = o0 + wm * WM + 16 * i + 4 * g;
+      if (o >= Oi) continue;
+      store_tile<YBF16>(y, acc_out, acc[i][j], t, o, Oi, s_t, sw, (int)sw_inc);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill kernel with LDS DMA (global_load_lds): used when K is a multiple of
+// BK. Operand tiles go straight from global memory into an S-slot LDS ring in
+// fragment-major order -- xq as 16-byte lane slots, packed W as 4-byte code
+// (and, for 2:4, index) words -- without passing through registers, so S-2
+// K-steps of MFMA work cover the global latency. One K-step ahead, the
+// workgroup expands the next stage's 2-bit codes into an int8 A buffer.
+// Every stage issues the same DMA instructions per wave (stages past the end
+// reload the last stage into a free slot), so the wait count is a constant.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int waitcnt_vmcnt(int n) {
+  // gfx9 s_waitcnt immediate: vmcnt in bits [3:0] and [15:14]; lgkmcnt and
+  // expcnt at their maxima (not waited on)
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+// Workgroup barrier for the DMA pipeline: wait until this wave has at most n
+// vector-memory operations (LDS DMAs) outstanding and all its LDS operations
+// are done, then s_barrier. Unlike __syncthreads() this does not drain the
+// DMAs still in flight for later stages. The empty asm statements only stop
+// the compiler from moving memory accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <typename P>
+__device__ __forceinline__ void dma16(const P* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+template <typename P>
+__device__ __forceinline__ void dma4(const P* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool SP, bool YBF16, int S>
+struct DmaCfg {
+  static constexpr int NW = WAVES_M * WAVES_N, NT = 64 * NW;
+  static constexpr int FA = BM / 16, FB = BN / 16;
+  static constexpr int BFB = SP ? 2048 : 1024;
+  static constexpr int SLOT_B = FB * BFB, SLOT_AC = FA * 256, SLOT_AI = SP ? FA * 256 : 0;
+  static constexpr int SLOT = SLOT_B + SLOT_AC + SLOT_AI;
+  static constexpr int AEXP = FA * 1024;
+  static constexpr size_t LDS = (size_t)S * SLOT + 2 * AEXP;
+};
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool SP, bool YBF16, int S>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void k_gemm_dma(const int8_t* __restrict__ xq, const float* __restrict__ sx,
+                const uint8_t* __restrict__ packed, int64_t pitch, const float* __restrict__ sw,
+                int64_t sw_inc, int64_t T, int64_t O, int64_t K, void* __restrict__ y,
+                int32_t* __restrict__ acc_out) {
+  using C = DmaCfg<BM, BN, WAVES_M, WAVES_N, SP, YBF16, S>;
+  constexpr int NW = C::NW, NT = C::NT;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int FI = WM / 16, FJ = WN / 16;
+  constexpr int BK = SP ? 128 : 64;
+  constexpr int AROW = SP ? 32 : 16;
+  constexpr int NBI = C::FB * (SP ? 2 : 1), NAI = C::FA * (SP ? 2 : 1), NI = NBI + NAI;
+  constexpr int IPW = NI / NW;                 // DMA instructions per wave per stage
+  constexpr int NEXP = C::FA * 64 / NT;        // A lane slots expanded per thread
+  static_assert(NI % NW == 0 && (C::FA * 64) % NT == 0 && NEXP >= 1, "staging split");
+  static_assert(S >= 3 && IPW * (S - 3) < 64, "pipeline depth");
+  // Each ring slot is its own LDS object and the K-loop is unrolled by S, so
+  // every LDS access names a compile-time slot: the compiler then only waits
+  // for the DMAs that target the slot being read. The expanded-A buffer is a
+  // separate object (no DMA ever targets it).
+  constexpr int SL = C::SLOT;
+  __shared__ __attribute__((aligned(16))) uint8_t rs0[SL], rs1[SL], rs2[SL];
+  __shared__ __attribute__((aligned(16))) uint8_t rs3[S > 3 ? SL : 16], rs4[S > 4 ? SL : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t aexp[2 * C::AEXP];
+  uint8_t* const slots[5] = {rs0, rs1, rs2, rs3, rs4};
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int64_t ntm = cdiv(O, BM), ntn = cdiv(T, BN);
+  int64_t tm, tn;
+  tile_of(blockIdx.x, ntm * ntn, ntm, ntn, tm, tn);
+  const int o0 = (int)(tm * BM), t0 = (int)(tn * BN);
+  const int Oi = (int)O, Ti = (int)T;
+  const int nk = (int)(K / BK);
+
+  // this wave's DMA sources (stage 0) and slot-relative LDS destinations;
+  // rows past O / T are clamped to the last valid row (never stored)
+  const uint8_t* src[IPW];
+  int dst[IPW];
+  // Slot order inside a 16-row block: DMA lane l fills slot l with row l/4,
+  // k-block (l%4) ^ ((l/16)%4), so four consecutive lanes fetch one row's 64
+  // contiguous bytes; MFMA lane (row r, k-block g) reads slot
+  // 4r + (g ^ (r/4)%4), which keeps each 16-lane group in distinct banks.
+  const int drow = lane >> 2, dkb = (lane & 3) ^ ((lane >> 4) & 3);
+#pragma unroll
+  for (int u = 0; u < IPW; ++u) {
+    const int idx = wave * IPW + u;
+    if (idx < NBI) {
+      const int f = SP ? idx >> 1 : idx, h = SP ? idx & 1 : 0;
+      const int row = 16 * f + drow, seg = 4 * h + dkb;
+      src[u] = (const uint8_t*)(xq + (int64_t)min(t0 + row, Ti - 1) * K + 16 * seg);
+      dst[u] = f * C::BFB + h * 1024;
+    } else {
+      const int a = idx - NBI;
+      const int f = SP ? a >> 1 : a, part = SP ? a & 1 : 0;
+      const int row = 16 * f + drow, kb = dkb;
+      src[u] = packed + (int64_t)min(o0 + row, Oi - 1) * pitch + (SP ? 8 * kb + 4 * part : 4 * kb);
+      dst[u] = C::SLOT_B + part * C::SLOT_AC + f * 256;
+    }
+  }
+  auto issue = [&](int ks, uint8_t* base) {
+    const int kc = min(ks, nk - 1);
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+      const int idx = wave * IPW + u;          // uniform across the wave
+      if (idx < NBI) dma16(src[u] + (int64_t)kc * BK, base + dst[u]);
+      else dma4(src[u] + (int64_t)kc * AROW, base + dst[u]);
+    }
+  };
+  auto expand = [&](const uint8_t* slot, int ebuf) {
+    const uint8_t* codes = slot + C::SLOT_B;
+    uint8_t* out = aexp + ebuf * C::AEXP;
+#pragma unroll
+    for (int q = 0; q < NEXP; ++q) {
+      const int p = tid + NT * q, f = p >> 6, l = p & 63;
+      const uint32_t cw = *(const uint32_t*)(codes + f * 256 + l * 4);
+      *(uint4*)(out + f * 1024 + l * 16) =
+          make_uint4(expand_codes(cw, 0), expand_codes(cw, 1), expand_codes(cw, 2), expand_codes(cw, 3));
+    }
+  };
+
+  v4i acc[FI][FJ];
 #pragma unroll
   for (int i = 0; i < FI; ++i)
 #pragma unroll
-    for (int j = 0; j < FJ; ++j) {
-      const int64_t t = t0 + wn * WN + 16 * j + r16;
-      const int64_t o = o0 + wm * WM + 16 * i + 4 * g;
-      store_out<YBF16>(y, acc_out, acc[i][j], t, o, T, O, sx, sw, sw_inc);
+    for (int j = 0; j < FJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+  const int rs = 4 * (lane & 15) + ((lane >> 4) ^ ((lane >> 2) & 3));   // this lane's slot
+  auto compute = [&](const uint8_t* slot, int ebuf) {
+    const uint8_t* b = slot + (wn * FJ) * C::BFB + rs * 16;
+    const uint8_t* a = aexp + ebuf * C::AEXP + (wm * FI) * 1024 + rs * 16;
+    if constexpr (SP) {
+      const uint8_t* ai_base = slot + C::SLOT_B + C::SLOT_AC + (wm * FI) * 256 + rs * 4;
+      v8i bf[FJ];
+      v4i af[FI];
+      int ai[FI];
+#pragma unroll
+      for (int i = 0; i < FI; ++i) {
+        af[i] = *(const v4i*)(a + i * 1024);
+        ai[i] = *(const int*)(ai_base + i * 256);
+      }
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        const v4i lo = *(const v4i*)(b + j * C::BFB);
+        const v4i hi = *(const v4i*)(b + j * C::BFB + 1024);
+        bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+      for (int j = 0; j < FJ; ++j)
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+          acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(af[i], bf[j], acc[i][j], ai[i], 0, 0);
+    } else {
+      v4i bf[FJ], af[FI];
+#pragma unroll
+      for (int i = 0; i < FI; ++i) af[i] = *(const v4i*)(a + i * 1024);
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) bf[j] = *(const v4i*)(b + j * C::BFB);
+#pragma unroll
+      for (int j = 0; j < FJ; ++j)
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
+  };
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) issue(st, slots[st]);
+  dma_barrier<IPW * (S - 2)>();        // every wave's stage-0 DMAs landed
+  expand(slots[0], 0);
+  for (int ks0 = 0; ks0 < nk; ks0 += S) {
+#pragma unroll
+    for (int I = 0; I < S; ++I) {
+      const int ks = ks0 + I;                 // stage ks lives in slot I
+      if (ks < nk) {
+        // stage ks+1 landed and visible; expand(ks) and compute(ks-1) done everywhere
+        dma_barrier<IPW * (S - 3)>();
+        issue(ks + S - 1, slots[(I + S - 1) % S]);   // into the slot of stage ks-1
+        expand(slots[(I + 1) % S], (ks + 1) & 1);
+        compute(slots[I], ks & 1);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vmcnt(0));   // no DMA may still target LDS at exit
+
+  const int g = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int j = 0; j < FJ; ++j) {
+    const int t = t0 + wn * WN + 16 * j + r16;
+    if (t >= Ti) continue;
+    const float s_t = sx[t];
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const int o = o0 + wm * WM + 16 * i + 4 * g;
+      if (o >= Oi) continue;
+      store_tile<YBF16>(y, acc_out, acc[i][j], t, o, Oi, s_t, sw, (int)sw_inc);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode (T <= 16): bandwidth-oriented variant. One workgroup per 16-row tile
+// of W; its 4 wavefronts split the K-steps into contiguous ranges and each
+// issues the loads of kGemvUnroll steps before consuming them, so a wave keeps
+// several KB of packed weights in flight. Tokens occupy the 16 columns of the
+// MFMA (columns >= T read zeros). The 4 partial accumulators are summed in LDS.
+// ---------------------------------------------------------------------------
+constexpr int kGemvUnroll = 8;
+
+template <bool SP, bool KA16, bool YBF16>
+__global__ __launch_bounds__(256) void k_gemv(const int8_t* __restrict__ xq,
+                                              const float* __restrict__ sx,
+                                              const uint8_t* __restrict__ packed, int64_t pitch,
+                                              const float* __restrict__ sw, int64_t sw_inc,
+                                              int64_t T, int64_t O, int64_t K,
+                                              void* __restrict__ y, int32_t* __restrict__ acc_out) {
+  constexpr int BK = SP ? 128 : 64;
+  constexpr int U = kGemvUnroll;
+  __shared__ v4i red[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t o0 = (int64_t)blockIdx.x * 16;
+  const int64_t nk = cdiv(K, BK);
+  const int64_t per = cdiv(nk, 4);
+  const int64_t ks0 = wave * per, ks1 = (ks0 + per < nk) ? ks0 + per : nk;
+  const bool rowv = o0 + r16 < O;
+  const uint8_t* arow = packed + (o0 + r16) * pitch + (SP ? 8 * g : 4 * g);
+  const bool tv = r16 < T;
+  const int8_t* xrow = xq + r16 * K;
+
+  v4i acc = {0, 0, 0, 0};
+  for (int64_t ks = ks0; ks < ks1; ks += U) {
+    uint2 a[U];
+    uint4 b0[U], b1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = ks + u;
+      a[u] = make_uint2(0, SP ? 0x44444444u : 0u);
+      b0[u] = b1[u] = make_uint4(0, 0, 0, 0);
+      if (k < ks1) {
+        if (rowv) {
+          if constexpr (SP) a[u] = *(const uint2*)(arow + k * 32);
+          else a[u].x = *(const uint32_t*)(arow + k * 16);
+        }
+        if (tv) {
+          if constexpr (SP) {
+            b0[u] = load_x16<KA16>(xrow, k * BK + 16 * g, K);
+            b1[u] = load_x16<KA16>(xrow, k * BK + 64 + 16 * g, K);
+          } else {
+            b0[u] = load_x16<KA16>(xrow, k * BK + 16 * g, K);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ks + u < ks1) {
+        const v4i af = {(int)expand_codes(a[u].x, 0), (int)expand_codes(a[u].x, 1),
+                        (int)expand_codes(a[u].x, 2), (int)expand_codes(a[u].x, 3)};
+        const v4i lo = {(int)b0[u].x, (int)b0[u].y, (int)b0[u].z, (int)b0[u].w};
+        if constexpr (SP) {
+          const v8i bf = {lo[0], lo[1], lo[2], lo[3], (int)b1[u].x, (int)b1[u].y, (int)b1[u].z,
+                          (int)b1[u].w};
+          acc = __builtin_amdgcn_smfmac_i32_16x16x128_i8(af, bf, acc, (int)a[u].y, 0, 0);
+        } else {
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, lo, acc, 0, 0, 0);
+        }
+      }
+    }
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  const v4i c = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+  store_out<YBF16>(y, acc_out, c, (int64_t)r16, o0 + 4 * g, T, O, sx, sw, sw_inc);
+}
+
+template <bool SP, bool KA16, bool YBF16>
+static hipError_t launch_gemv(const int8_t* xq, const float* sx, const uint8_t* packed,
+                              int64_t pitch, const float* sw, int64_t sw_inc, int64_t T,
+                              int64_t O, int64_t K, void* y, int32_t* acc, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemv<SP, KA16, YBF16>), dim3((unsigned)cdiv(O, 16)), dim3(256), 0, s, xq,
+                     sx, packed, pitch, sw, sw_inc, T, O, K, y, acc);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -264,7 +625,8 @@ void k_gemm(const int8_t* __restrict__ xq, const float* __restrict__ sx,
 // ---------------------------------------------------------------------------
 enum TileCfg { kT256x256 = 0, kT256x128 = 1, kT128x256 = 2, kT128x128 = 3, kT256x32 = 4,
                kT128x32 = 5, kT256x256w8 = 6, kT128x256w8 = 7, kT256x128w8 = 8,
-               kT256x256w8t = 9, kNumCfg = 10 };
+               kT256x256w8t = 9, kDma128x256 = 10, kDma256x128 = 11, kDma128x128 = 12,
+               kDma256x256 = 13, kT64x128 = 14, kNumCfg = 15 };
 
 struct Args {
   const int8_t* xq; const float* sx; const uint8_t* packed; int64_t pitch; const float* sw;
@@ -273,8 +635,7 @@ struct Args {
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool SP, bool KA16, bool YBF16>
 static hipError_t launch_cfg(const Args& a, hipStream_t s) {
-  constexpr int PB = SP ? kPitchBs : kPitchBd;
-  const size_t lds = 2 * (size_t)BM * kPitchA + 2 * (size_t)BN * PB;
+  const size_t lds = 2 * (size_t)BM * kPitchA + 2 * (size_t)BN * (SP ? kPitchBs : kPitchBd);
   auto kern = k_gemm<BM, BN, WAVES_M, WAVES_N, SP, KA16, YBF16>;
   if (lds > 65536) {
     static bool set = false;  // attribute is per kernel; setting it twice is harmless
@@ -291,9 +652,23 @@ static hipError_t launch_cfg(const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool SP, bool YBF16, int S>
+static hipError_t launch_dma(const Args& a, hipStream_t s) {
+  auto kern = k_gemm_dma<BM, BN, WAVES_M, WAVES_N, SP, YBF16, S>;  // static LDS
+  const int64_t nb = cdiv(a.O, BM) * cdiv(a.T, BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(64 * WAVES_M * WAVES_N), 0, s, a.xq, a.sx,
+                     a.packed, a.pitch, a.sw, a.sw_inc, a.T, a.O, a.K, a.y, a.acc);
+  return hipGetLastError();
+}
+
 template <bool SP, bool KA16, bool YBF16>
 static hipError_t launch_sel(int cfg, const Args& a, hipStream_t s) {
   switch (cfg) {
+    case kT64x128: return launch_cfg<64, 128, 2, 2, SP, KA16, YBF16>(a, s);
+    case kDma128x256: return launch_dma<128, 256, 2, 4, SP, YBF16, SP ? 3 : 4>(a, s);
+    case kDma256x128: return launch_dma<256, 128, 4, 2, SP, YBF16, SP ? 4 : 5>(a, s);
+    case kDma128x128: return launch_dma<128, 128, 2, 2, SP, YBF16, SP ? 4 : 5>(a, s);
+    case kDma256x256: return launch_dma<256, 256, 2, 4, SP, YBF16, SP ? 3 : 4>(a, s);
     case kT256x256: return launch_cfg<256, 256, 2, 2, SP, KA16, YBF16>(a, s);
     case kT256x128: return launch_cfg<256, 128, 2, 2, SP, KA16, YBF16>(a, s);
     case kT128x256: return launch_cfg<128, 256, 2, 2, SP, KA16, YBF16>(a, s);
@@ -307,27 +682,23 @@ static hipError_t launch_sel(int cfg, const Args& a, hipStream_t s) {
   }
 }
 
-// Estimated time of a configuration: rounds of workgroups over the CUs times
-// the per-workgroup MFMA work, scaled by the relative efficiency of the tile.
-static int choose_cfg(int64_t T, int64_t O, int64_t K) {
+// Tile choice for T > 32, from measured sweeps over the Qwen2.5-shaped FFN
+// projections on MI355X: 2:4 runs best on 256(O)x128(T) tiles; dense N:M on
+// 128x256 (8 waves), on 256x256 (8 waves) when K is long, and on smaller
+// tiles when O is too small to give every CU a workgroup.
+static int choose_cfg(int64_t T, int64_t O, int64_t K, bool sp) {
   // tuning override (read on every call so tests can force each configuration)
   const char* ev = std::getenv("SBL_GEMM_TILE");
   const int forced = ev ? std::atoi(ev) : -1;
   if (forced >= 0 && forced < kNumCfg) return forced;
   if (T <= 32) return O >= 8192 ? kT256x32 : kT128x32;
   const int cus = device_info().cus;
-  struct C { int cfg, bm, bn, per_cu; double eff; };
-  const C cs[] = {{kT256x256, 256, 256, 1, 1.0}, {kT256x128, 256, 128, 2, 0.85},
-                  {kT128x256, 128, 256, 2, 0.85}, {kT128x128, 128, 128, 2, 0.6}};
-  int best = kT128x128;
-  double best_t = 1e30;
-  for (const C& c : cs) {
-    const double nb = (double)cdiv(O, c.bm) * (double)cdiv(T, c.bn);
-    const double rounds = std::ceil(nb / (double)(cus * c.per_cu));
-    const double t = rounds * c.per_cu * (double)c.bm * c.bn * (double)K / c.eff;
-    if (t < best_t) { best_t = t; best = c.cfg; }
-  }
-  return best;
+  const int64_t t128 = cdiv(O, 128) * cdiv(T, 128);
+  if (t128 < cus) return kT64x128;          // too few tiles: smaller ones fill the chip
+  if (t128 < 2 * cus) return kT128x128;
+  if (sp) return kT256x128w8;
+  if (K >= 8192) return kT256x256w8;
+  return kT128x256w8;
 }
 
 hipError_t launch_gemm(const int8_t* xq, const float* sx, const void* packed, const float* sw,
@@ -336,8 +707,22 @@ hipError_t launch_gemm(const int8_t* xq, const float* sx, const void* packed, co
   if (T == 0 || O == 0) return hipSuccess;
   const bool sp = index_form(N, M);
   const Args a{xq, sx, (const uint8_t*)packed, row_pitch(K, N, M), sw, sw_inc, T, O, K, y, acc};
-  const int cfg = choose_cfg(T, O, K);
   const bool ka16 = (K % 16) == 0;
+  const char* ev = std::getenv("SBL_GEMM_TILE");
+  if (T <= 16 && !(ev && std::atoi(ev) >= 0)) {
+#define SBL_GEMV(SPV, KAV, YV) \
+    return launch_gemv<SPV, KAV, YV>(xq, sx, a.packed, a.pitch, sw, sw_inc, T, O, K, y, acc, s)
+    if (sp) {
+      if (ka16) { if (y_bf16) SBL_GEMV(true, true, true); else SBL_GEMV(true, true, false); }
+      else { if (y_bf16) SBL_GEMV(true, false, true); else SBL_GEMV(true, false, false); }
+    } else {
+      if (ka16) { if (y_bf16) SBL_GEMV(false, true, true); else SBL_GEMV(false, true, false); }
+      else { if (y_bf16) SBL_GEMV(false, false, true); else SBL_GEMV(false, false, false); }
+    }
+#undef SBL_GEMV
+  }
+  int cfg = choose_cfg(T, O, K, sp);
+  if (cfg >= kDma128x256 && K % (sp ? 128 : 64) != 0) cfg = kT128x128;  // DMA path needs whole K-steps
 #define SBL_DISPATCH(SPV, KAV, YV) return launch_sel<SPV, KAV, YV>(cfg, a, s)
   if (sp) {
     if (ka16) { if (y_bf16) SBL_DISPATCH(true, true, true); else SBL_DISPATCH(true, true, false); }
