@@ -52,29 +52,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
-
-
-class Timeline:
-    """Events around each named call of a step, on the stream the library
-    launches on (torch's current stream)."""
-
-    def __init__(self):
-        self.names, self.evs = [], []
-
-    def mark(self, name):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.names.append(name)
-        self.evs.append(e)
-
-    def durations_ms(self):
-        torch.cuda.synchronize()
-        out = {}
-        for i in range(len(self.evs) - 1):
-            n = self.names[i]
-            out.setdefault(n, []).append(self.evs[i].elapsed_time(self.evs[i + 1]))
-        return out
 
 
 # ---------------------------------------------------------------- prefill --
@@ -107,28 +87,32 @@ class PrefillStep:
         self.ws = torch.empty(nws, dtype=torch.uint8, device=dev)
         self.ops = sum(2.0 * self.T * l.O * l.K for l in wl.linears)
 
-    def run(self, tl=None):
-        mark = tl.mark if tl else (lambda n: None)
+    def calls(self):
+        """The step as an ordered list of (name, launch) pairs."""
         N, M = self.N, self.M
+        out = []
         for xn in self.groups:
-            mark(f"quant_act[{xn}]")
-            sbl.sbl_quant_act(self.x[xn], xq=self.xq[xn], sx=self.sx[xn])
+            out.append((f"quant_act[{xn}]",
+                        lambda xn=xn: sbl.sbl_quant_act(self.x[xn], xq=self.xq[xn], sx=self.sx[xn])))
         for xn, lins in self.groups.items():
             off_p, off_o = 0, 0
             for l in lins:
                 nb = sbl.sbl_packed_bytes(l.O, l.K, N, M)
-                mark(f"quant_mask_weight[{l.name}]")
-                sbl.sbl_quant_mask_weight(self.W[l.name], N, M,
-                                          packed=self.packed[xn][off_p:off_p + nb],
-                                          sw_rows=self.swr[xn][off_o:off_o + l.O], ws=self.ws)
+                pk = self.packed[xn][off_p:off_p + nb]
+                sr = self.swr[xn][off_o:off_o + l.O]
+                out.append((f"quant_mask_weight[{l.name}]",
+                            lambda l=l, pk=pk, sr=sr: sbl.sbl_quant_mask_weight(
+                                self.W[l.name], N, M, packed=pk, sw_rows=sr, ws=self.ws)))
                 off_p += nb
                 off_o += l.O
         for xn, lins in self.groups.items():
             O = sum(l.O for l in lins)
-            mark(f"gemm[{'+'.join(l.name for l in lins)}]")
-            sbl.sbl_gemm(self.xq[xn], self.sx[xn], self.packed[xn], self.swr[xn], O, N, M,
-                         y=self.y[xn])
-        mark("end")
+            out.append((f"gemm[{'+'.join(l.name for l in lins)}]",
+                        lambda xn=xn, O=O: sbl.sbl_gemm(self.xq[xn], self.sx[xn], self.packed[xn],
+                                                        self.swr[xn], O, N, M, y=self.y[xn])))
+        return out
+
+    cold_weights = False   # inputs of every call were just written by the step: cache-hot
 
     def call_info(self, name):
         """(bound, algorithmic units per launch, unit) of a named call."""
@@ -202,17 +186,21 @@ class DecodeStep:
         O = sum(l.O for l in self.groups[xn])
         return sbl.sbl_packed_bytes(O, K, 2, 4) + T * K + 4 * T + 4 * O + 2 * T * O
 
-    def run(self, tl=None):
-        mark = tl.mark if tl else (lambda n: None)
+    def calls(self):
+        out = []
         for li in range(self.L):
             for xn in self.groups:
-                mark(f"quant_act[{xn}]")
-                sbl.sbl_quant_act(self.x[xn], xq=self.xq[xn], sx=self.sx[xn])
                 O = sum(l.O for l in self.groups[xn])
-                mark(f"gemm[{'+'.join(l.name for l in self.groups[xn])}]")
-                sbl.sbl_gemm(self.xq[xn], self.sx[xn], self.packed[li][xn], self.swr[li][xn],
-                             O, 2, 4, y=self.y[xn])
-        mark("end")
+                out.append((f"quant_act[{xn}]",
+                            lambda xn=xn: sbl.sbl_quant_act(self.x[xn], xq=self.xq[xn],
+                                                            sx=self.sx[xn])))
+                out.append((f"gemm[{'+'.join(l.name for l in self.groups[xn])}]",
+                            lambda xn=xn, O=O, li=li: sbl.sbl_gemm(
+                                self.xq[xn], self.sx[xn], self.packed[li][xn], self.swr[li][xn],
+                                O, 2, 4, y=self.y[xn])))
+        return out
+
+    cold_weights = True    # 30 layers of packed weights exceed the last-level cache
 
     def call_info(self, name):
         if name.startswith("gemm["):
@@ -224,21 +212,30 @@ class DecodeStep:
 
 
 # ------------------------------------------------------------------ timing --
-def time_steps(step, steps, warmup, eager):
+def run_all(calls):
+    for _, f in calls:
+        f()
+
+
+def capture(fn):
+    """Capture fn's launches into a HIP graph (after one eager warm-up run on a
+    side stream, as graph capture requires)."""
     stream = torch.cuda.current_stream()
-    if eager:
-        run = step.run
-    else:
-        s = torch.cuda.Stream()
-        s.wait_stream(stream)
-        with torch.cuda.stream(s):
-            step.run()          # warm the allocator / code objects outside capture
-        stream.wait_stream(s)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step.run()
-        run = graph.replay
+    s = torch.cuda.Stream()
+    s.wait_stream(stream)
+    with torch.cuda.stream(s):
+        fn()
+    stream.wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    return graph
+
+
+def time_steps(step, steps, warmup, eager):
+    calls = step.calls()
+    run = (lambda: run_all(calls)) if eager else capture(lambda: run_all(calls)).replay
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -251,14 +248,39 @@ def time_steps(step, steps, warmup, eager):
     return start.elapsed_time(end) / steps
 
 
-def breakdown(step, steps):
-    """Per-call device time: events around every library call, eager launches,
-    over `steps` further steps (the graph-timed region above is not perturbed)."""
-    tl = Timeline()
-    for _ in range(steps):
-        step.run(tl)
-    d = tl.durations_ms()
-    return {k: float(np.mean(v)) for k, v in d.items()}, {k: len(v) for k, v in d.items()}
+def per_call_times(step, reps):
+    """Device time per launch of every named call, from HIP events on the
+    library's stream around graph replays of that call alone: for each name, a
+    graph of all of the step's launches of that name in step order (decode:
+    one launch per layer, distinct weights), repeated so that a replay holds
+    at least 8 launches. Where the step streams weights larger than the
+    last-level cache, a 1 GiB write precedes every replay (outside the events)
+    so that the weights come from HBM, as they do inside the step."""
+    calls = step.calls()
+    names = list(dict.fromkeys(n for n, _ in calls))
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0") if step.cold_weights \
+        else None
+    out, per_step = {}, {}
+    for name in names:
+        fs = [f for n, f in calls if n == name]
+        per_step[name] = len(fs)
+        rep = max(1, -(-8 // len(fs)))
+        graph = capture(lambda: [f() for _ in range(rep) for f in fs])
+        launches = rep * len(fs)
+        graph.replay()
+        ms = []
+        for _ in range(reps):
+            if flush is not None:
+                flush.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            graph.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b) / launches)
+        out[name] = float(np.median(ms))
+        del graph
+    return out, per_step
 
 
 def cpu_baseline(wl_name, N, M, seconds, decode_T=None):
@@ -310,8 +332,44 @@ def _cpu_model():
     return "unknown"
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen05b_ffn.txt")
+GEMM_SRC = os.path.join(ROOT, "sparse_linear_layers_bitlinear_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic(kernel_call):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, scaled by the same counters on a plain
+    copy of known size. None if absent, for another kernel, or taken on a
+    different version of the kernel source."""
+    import hashlib
+    try:
+        kv = dict(line.split("=", 1) for line in open(TRAFFIC_FILE).read().split("\n")
+                  if "=" in line and not line.startswith("#"))
+        src = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+        if kv.get("call", "").strip() != kernel_call or kv.get("gemm_src_sha256", "").strip() != src:
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n,
+                      "bytes_written_per_copy": n, "copies": 3}))
+
+
 def main():
     a = parse()
+    if a.calibrate_copy:
+        calibrate_copy()
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
                           "n_gpus": a.gpus}))
@@ -326,8 +384,7 @@ def main():
     else:
         step = PrefillStep(a.workload, N, M)
     ms = time_steps(step, a.steps, a.warmup, a.eager)
-    per_call, counts = breakdown(step, a.steps)
-    calls_per_step = {k: counts[k] // a.steps for k in counts}
+    per_call, calls_per_step = per_call_times(step, max(5, min(a.steps, 20)))
     share = {k: per_call[k] * calls_per_step[k] for k in per_call}
     dom = max(share, key=share.get)
     bound, units, kind = step.call_info(dom)
@@ -339,7 +396,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom) if a.workload == "qwen05b_ffn" else None
     roof["kernel"] = dom
     roof["avg_ms"] = round(per_call[dom], 5)
 
@@ -364,6 +421,7 @@ def main():
         "dtype": "int8xternary->int32 (bf16 in/out)", "data": "synthetic",
         "config": config, "roofline": roof,
         "breakdown_ms": {k: round(share[k], 5) for k in share},
+        "breakdown_note": "per-step device ms of each call, from graph replays of that call alone",
         "timing": "eager launches" if a.eager else "HIP graph replay",
     }
     if not a.no_cpu_baseline:
