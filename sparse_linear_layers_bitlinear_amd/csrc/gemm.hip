@@ -535,6 +535,410 @@ void k_gemm_dma(const int8_t* __restrict__ xq, const float* __restrict__ sx,
 }
 
 // ---------------------------------------------------------------------------
+// Prefill kernel with register-resident W fragments.
+//
+// LDS bandwidth, not the matrix cores, limits a kernel that stages both
+// operands through LDS: a 64x64 wave tile reads 8 KB of fragments per 16
+// MFMAs. Here only xq goes through LDS; the packed W rows go from global
+// memory straight into VGPRs in MFMA layout (8 bytes of 2-bit codes, or one
+// 2:4 chunk, per lane and K-step) and are expanded in registers. The waves of
+// a K-group split the tile along O only, so each staged xq fragment is read
+// by all of them, and no W byte is shared between waves.
+//
+// A K-step covers 128 dense k. Lane (r, g) of fragment i loads 8 bytes at
+// byte 32*s + 8*g of W row o0 + 16*i + r:
+//   dense form: code words 8s+2g and 8s+2g+1, i.e. k in [128s+32g, +32);
+//     sub-step j in {0, 1} feeds k [128s + 32g + 16j, +16) to lane group g of
+//     v_mfma_i32_16x16x64_i8, so B lane (t, g) reads xq[t][128s+32g+16j, +16);
+//   2:4 index form: chunk 4s+g (codes word, index word), exactly the sparse
+//     operand of v_smfmac_i32_16x16x128_i8; B lane (t, g) reads k [16g, +16)
+//     and [64+16g, +16) of the step.
+// W loads are issued NA-1 K-steps ahead into a ring of NA register slots;
+// xq for step s+3 is loaded into registers at the end of step s and stored to
+// a double-buffered LDS tile two steps later.
+//
+// KS > 1 splits the K-steps of one output tile between KS groups of WO waves
+// (each group with its own xq tiles); their int32 accumulators are summed
+// through LDS before the epilogue. Integer sums are exact, so the split does
+// not change any result.
+//
+// The grid is persistent: workgroup b takes tiles b, b + G, b + 2G, ... The
+// loads of a tile's first K-steps are issued before the previous tile's
+// epilogue, so their latency hides behind it. The bf16 epilogue stages the
+// dequantized tile in LDS and writes each output row segment with contiguous
+// 8-byte lanes (BM * 2 bytes per row and instruction).
+// ---------------------------------------------------------------------------
+constexpr int kPitchR = 144;   // LDS bytes per staged xq row (128 k + 16 pad)
+
+template <int WO, int KS, int FI, int FJ, int NA>
+struct RaCfg {
+  static constexpr int NTQ = 64 * WO, NT = NTQ * KS, NW = WO * KS;
+  static constexpr int BM = WO * 16 * FI, BN = 16 * FJ;
+  static constexpr int BUF = BN * kPitchR;
+  static constexpr int PO = BM * 2 + 8;          // LDS bytes per staged output row
+  static constexpr size_t LDS_B = (size_t)KS * 2 * BUF;
+  static constexpr size_t LDS_RED = KS > 1 ? (size_t)WO * FI * FJ * 64 * 16 : 0;
+  static constexpr size_t LDS_OUT = (size_t)BN * PO;
+  static constexpr size_t M1 = LDS_B > LDS_RED ? LDS_B : LDS_RED;
+  static constexpr size_t SCALES = M1 > LDS_OUT ? M1 : LDS_OUT;   // offset of sx / sw
+  static constexpr int NSC = (BM + BN + NT - 1) / NT;            // scales per thread
+  static constexpr size_t LDS = SCALES + (size_t)(BM + BN) * 4;
+};
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + 4 GiB): loads take a per-lane 32-bit
+// offset plus a wave-uniform scalar offset, so address arithmetic costs no
+// VALU. Offsets are always in bounds by construction (no reliance on the
+// hardware range check).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF,
+                                           0x00020000);
+}
+
+template <int WO, int KS, int FI, int FJ, int NA, bool SP, bool YBF16>
+__global__ __launch_bounds__(64 * WO * KS) __attribute__((amdgpu_waves_per_eu(2)))
+void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
+               const uint8_t* __restrict__ packed, int64_t pitch, const float* __restrict__ sw,
+               int64_t sw_inc, int64_t T, int64_t O, int64_t K, void* __restrict__ y,
+               int32_t* __restrict__ acc_out) {
+  using C = RaCfg<WO, KS, FI, FJ, NA>;
+  constexpr int NT = C::NT, NTQ = C::NTQ, NW = C::NW, BM = C::BM, BN = C::BN;
+  constexpr int SEGS = BN * 8;                       // 16-byte xq segments per step
+  constexpr int NSB = (SEGS + NTQ - 1) / NTQ;
+  constexpr int U = NA == 3 ? 6 : 4;                 // K-loop unroll (static slots)
+  static_assert(NA >= 2 && NA <= 4, "W register ring");
+  static_assert(NTQ % 8 == 0, "staging layout");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float* const sxs = (float*)(smem + C::SCALES);     // [BN] sx of the tile's tokens
+  float* const sws = sxs + BN;                       // [BM] sw of the tile's rows
+
+  // Every global load below is unconditional and in bounds (row and step
+  // indices are clamped), so no lane-divergent branch stands between a
+  // prefetch and its use and the compiler's wait counts stay exact.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wo = wave % WO, q = wave / WO, tq = tid - q * NTQ;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t ntm = cdiv(O, BM), ntn = cdiv(T, BN), ntiles = ntm * ntn;
+  const int Oi = (int)O, Ti = (int)T, Ki = (int)K, pitchi = (int)pitch;
+  const int ns = (Ki + 127) >> 7;                    // K-steps of 128 (ns >= 1)
+  const int nsq = (ns + KS - 1) / KS;
+  const int sb = q * nsq, se = min(ns, sb + nsq);    // this group's steps
+  const int slast = max(se - 1, 0);                  // clamp for loads
+  const int cb16 = 16 * (tq & 7);                    // xq segment column of this thread
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(packed), rbx = buffer_rsrc(xq);
+
+  int o0 = 0, t0 = 0;
+  uint32_t avo[FI];                                  // W row offsets (+ 8g)
+  uint32_t bvo[NSB];                                 // xq row offsets (+ segment column)
+  int bdst[NSB];
+  float scr[C::NSC];
+  // W rows past O and xq rows past T are clamped to the last valid row: they
+  // only feed accumulators that are never stored. For s < ns the 8 bytes at
+  // 32s + 8g lie inside the row record; in the dense form units past the code
+  // words hold mask bits, which meet xq columns k >= K (zero in LDS).
+  auto setup = [&](int64_t tile) {
+    int64_t tm, tn;
+    tile_of(tile, ntiles, ntm, ntn, tm, tn);
+    o0 = (int)(tm * BM);
+    t0 = (int)(tn * BN);
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+      avo[i] = (uint32_t)min(o0 + wo * 16 * FI + 16 * i + r16, Oi - 1) * (uint32_t)pitchi + 8 * g;
+#pragma unroll
+    for (int u = 0; u < NSB; ++u) {
+      const int rb = min((tq >> 3) + (NTQ / 8) * u, BN - 1);
+      bvo[u] = (uint32_t)min(t0 + rb, Ti - 1) * (uint32_t)Ki + cb16;
+      bdst[u] = rb * kPitchR + cb16;
+    }
+#pragma unroll
+    for (int c = 0; c < C::NSC; ++c) {
+      const int e = min(tid + NT * c, BM + BN - 1);
+      scr[c] = e < BN ? sx[min(t0 + e, Ti - 1)] : sw[(int64_t)min(o0 + e - BN, Oi - 1) * sw_inc];
+    }
+  };
+  auto aload = [&](int s, uint2 (&d)[FI]) {
+    const int soff = 32 * min(s, slast);
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(ra, avo[i], soff, 0);
+      d[i] = make_uint2(v.x, v.y);
+    }
+  };
+  // xq of step s: 16 bytes per segment. Only the final K-step can reach past
+  // K; there the column is clamped (the data is zeroed at the store).
+  auto bload = [&](int s, uint4 (&r)[NSB]) {
+    const int sc = min(s, slast);
+    const int kb = 128 * sc;
+    if (kb + 128 <= Ki) {
+#pragma unroll
+      for (int u = 0; u < NSB; ++u) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rbx, bvo[u], kb, 0);
+        r[u] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+    } else {
+      const int over = max(kb + cb16 - (Ki - 16), 0);   // lanes whose segment passes K
+#pragma unroll
+      for (int u = 0; u < NSB; ++u) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rbx, bvo[u] - over, kb, 0);
+        r[u] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+    }
+  };
+  uint8_t* const bq = smem + (size_t)q * 2 * C::BUF;
+  // store the xq of step s; columns k >= K become zero (final step only)
+  auto bstore = [&](int s, int buf, const uint4 (&r)[NSB]) {
+    uint8_t* b = bq + buf * C::BUF;
+    if (128 * s + 128 <= Ki) {
+#pragma unroll
+      for (int u = 0; u < NSB; ++u)
+        if (NSB * NTQ == SEGS || tq + NTQ * u < SEGS) *(uint4*)(b + bdst[u]) = r[u];
+    } else {
+      const uint32_t m = (uint32_t)((128 * s + cb16 - Ki) >> 31);   // all ones if k < K
+#pragma unroll
+      for (int u = 0; u < NSB; ++u)
+        if (NSB * NTQ == SEGS || tq + NTQ * u < SEGS)
+          *(uint4*)(b + bdst[u]) = make_uint4(r[u].x & m, r[u].y & m, r[u].z & m, r[u].w & m);
+    }
+  };
+
+  auto expand = [](uint32_t w) -> v4i {
+    return v4i{(int)expand_codes(w, 0), (int)expand_codes(w, 1), (int)expand_codes(w, 2),
+               (int)expand_codes(w, 3)};
+  };
+  v4i acc[FI][FJ];
+  // exc: the expanded W fragment the next MFMAs consume. Each fragment is
+  // expanded while the MFMAs of the previous one run (the last fragment of a
+  // step expands the first of the next step), so the VALU work issues under
+  // the matrix-core work instead of in front of it.
+  v4i exc;
+
+  // One K-step from LDS buffer buf with W slot a (an: the next step's slot).
+  auto compute = [&](int buf, const uint2 (&a)[FI], const uint2 (&an)[FI]) {
+    const uint8_t* b = bq + buf * C::BUF + r16 * kPitchR;
+    if constexpr (SP) {
+      v8i bf[FJ];
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        const v4i lo = *(const v4i*)(b + 16 * j * kPitchR + 16 * g);
+        const v4i hi = *(const v4i*)(b + 16 * j * kPitchR + 64 + 16 * g);
+        bf[j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < FI; ++i) {
+        const v4i exn = expand(i + 1 < FI ? a[i + 1].x : an[0].x);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+          acc[i][j] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(exc, bf[j], acc[i][j], (int)a[i].y,
+                                                               0, 0);
+        exc = exn;
+      }
+#pragma unroll
+      for (int m = 0; m < FI * FJ; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, (11 + FJ - 1) / FJ, 0);  // VALU share
+      }
+    } else {
+      v4i bf[FJ];
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) bf[j] = *(const v4i*)(b + 16 * j * kPitchR + 32 * g);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < FI; ++i) {
+          const uint32_t wn = i + 1 < FI ? (h ? a[i + 1].y : a[i + 1].x) : (h ? an[0].x : a[0].y);
+          const v4i exn = expand(wn);
+#pragma unroll
+          for (int j = 0; j < FJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(exc, bf[j], acc[i][j], 0, 0, 0);
+          exc = exn;
+        }
+        if (h == 0) {
+          // xq fragments of sub-step 1 (the registers free up as the MFMAs issue)
+#pragma unroll
+          for (int j = 0; j < FJ; ++j) bf[j] = *(const v4i*)(b + 16 * j * kPitchR + 32 * g + 16);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 2 * FI * FJ; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, (11 + FJ - 1) / FJ, 0);
+      }
+    }
+  };
+
+  // W for steps sb..sb+NA-2 in the ring. xq: with two register sets (small
+  // wave tiles) step s+3 is loaded at the end of step s and stored two steps
+  // later; with one set, step s+1 is loaded at the start of step s.
+  constexpr int NBS = FI * FJ >= 32 ? 1 : 2;
+  uint2 ar[NA][FI];
+  uint4 rb[NBS][NSB];
+  auto prologue = [&]() {
+#pragma unroll
+    for (int p = 0; p < NA - 1; ++p) aload(sb + p, ar[p]);
+    bload(sb, rb[0]);
+    if constexpr (NBS == 2) bload(sb + 1, rb[1]);
+  };
+
+  int64_t tile = blockIdx.x;
+  setup(tile);
+  prologue();
+  for (;;) {
+    bstore(sb, 0, rb[0]);                             // xq of step sb into LDS
+    if constexpr (NBS == 2) bload(sb + 2, rb[0]);
+    exc = expand(ar[0][0].x);                         // first W fragment
+#pragma unroll
+    for (int i = 0; i < FI; ++i)
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    __syncthreads();
+
+    for (int it = 0; it < nsq; it += U) {
+#pragma unroll
+      for (int t = 0; t < U; ++t) {
+        const int s = sb + it + t;
+        aload(s + NA - 1, ar[(t + NA - 1) % NA]);      // into the slot of step s-1
+        if constexpr (NBS == 1) bload(s + 1, rb[0]);
+        if (s < se) compute(t & 1, ar[t % NA], ar[(t + 1) % NA]);
+        if constexpr (NBS == 1) {
+          bstore(s + 1, (t + 1) & 1, rb[0]);
+        } else {
+          // xq of step s+1 is in the register set of parity (t+1)&1
+          bstore(s + 1, (t + 1) & 1, rb[(t + 1) & 1]);
+          bload(s + 3, rb[(t + 1) & 1]);
+        }
+        __syncthreads();
+      }
+    }
+
+    // this tile's scales to LDS; then the next tile's first loads go out
+    const int eo0 = o0, et0 = t0;
+#pragma unroll
+    for (int c = 0; c < C::NSC; ++c) {
+      const int e = tid + NT * c;
+      if (e < BM + BN) sxs[e] = scr[c];              // sws follows sxs
+    }
+    const int64_t next = tile + gridDim.x;
+    const bool more = next < ntiles;
+    if (more) {
+      setup(next);
+      prologue();
+    }
+
+    if constexpr (KS > 1) {
+      // sum the K-groups' accumulators into group 0 (through the xq area)
+      v4i* red = (v4i*)smem;
+#pragma unroll 1
+      for (int r = 1; r < KS; ++r) {
+        if (q == r) {
+#pragma unroll
+          for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) red[((wo * FI + i) * FJ + j) * 64 + lane] = acc[i][j];
+        }
+        __syncthreads();
+        if (q == 0) {
+#pragma unroll
+          for (int i = 0; i < FI; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) acc[i][j] += red[((wo * FI + i) * FJ + j) * 64 + lane];
+        }
+        __syncthreads();
+      }
+    } else {
+      __syncthreads();                                // scales visible
+    }
+
+    if (YBF16 && acc_out == nullptr) {
+      // dequantize into the LDS output tile (bf16), then write whole row segments
+      uint8_t* const ot = smem;
+      if (q == 0) {
+        float4 w4[FI];
+        float st[FJ];
+#pragma unroll
+        for (int i = 0; i < FI; ++i) w4[i] = *(const float4*)(sws + wo * 16 * FI + 16 * i + 4 * g);
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) st[j] = sxs[16 * j + r16];
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+          const int tl = 16 * j + r16;
+#pragma unroll
+          for (int i = 0; i < FI; ++i) {
+            const int ol = wo * 16 * FI + 16 * i + 4 * g;
+            const float v0 = ((float)acc[i][j][0] * st[j]) * w4[i].x;
+            const float v1 = ((float)acc[i][j][1] * st[j]) * w4[i].y;
+            const float v2 = ((float)acc[i][j][2] * st[j]) * w4[i].z;
+            const float v3 = ((float)acc[i][j][3] * st[j]) * w4[i].w;
+            *(uint2*)(ot + tl * C::PO + 2 * ol) =
+                make_uint2(f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16),
+                           f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16));
+          }
+        }
+      }
+      __syncthreads();
+      constexpr int RW = (BN + NW - 1) / NW;          // rows per wave
+      constexpr int RC = RW < 8 ? RW : 8;             // rows in flight per wave
+      constexpr int CPR = BM / 4;                     // 8-byte chunks per row
+      constexpr int CL = (CPR + 63) / 64;             // chunks per lane and row
+      const bool fast = (Oi & 3) == 0 && eo0 + BM <= Oi;
+#pragma unroll 1
+      for (int m0 = 0; m0 < RW; m0 += RC) {
+        uint2 v[RC][CL];
+#pragma unroll
+        for (int m = 0; m < RC; ++m)
+#pragma unroll
+          for (int c = 0; c < CL; ++c) {
+            const int tl = min(wave + NW * (m0 + m), BN - 1), ch = min(lane + 64 * c, CPR - 1);
+            v[m][c] = *(const uint2*)(ot + tl * C::PO + 8 * ch);
+          }
+#pragma unroll
+        for (int m = 0; m < RC; ++m) {
+          const int tl = wave + NW * (m0 + m), t = et0 + tl;
+          if (m0 + m >= RW || tl >= BN || t >= Ti) continue;
+          uint16_t* yr = (uint16_t*)y + (int64_t)t * Oi + eo0;
+#pragma unroll
+          for (int c = 0; c < CL; ++c) {
+            const int ch = lane + 64 * c;
+            if (ch >= CPR) continue;
+            if (fast) {
+              *(uint2*)(yr + 4 * ch) = v[m][c];
+            } else {
+              const uint16_t h[4] = {(uint16_t)(v[m][c].x & 0xFFFF), (uint16_t)(v[m][c].x >> 16),
+                                     (uint16_t)(v[m][c].y & 0xFFFF), (uint16_t)(v[m][c].y >> 16)};
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (eo0 + 4 * ch + r < Oi) yr[4 * ch + r] = h[r];
+            }
+          }
+        }
+      }
+      __syncthreads();                                // output tile area free again
+    } else {
+      if (q == 0) {
+        // fp32 output or int32 accumulators requested: store from registers
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+          const int t = et0 + 16 * j + r16;
+          if (t >= Ti) continue;
+          const float s_t = sxs[16 * j + r16];
+#pragma unroll
+          for (int i = 0; i < FI; ++i) {
+            const int o = eo0 + wo * 16 * FI + 16 * i + 4 * g;
+            if (o >= Oi) continue;
+            store_tile<YBF16>(y, acc_out, acc[i][j], t, o, Oi, s_t, sw, (int)sw_inc);
+          }
+        }
+      }
+      __syncthreads();
+    }
+    if (!more) break;
+    tile = next;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Decode (T <= 16): bandwidth-oriented variant. One workgroup per 16-row tile
 // of W; its 4 wavefronts split the K-steps into contiguous ranges and each
 // issues the loads of kGemvUnroll steps before consuming them, so a wave keeps
@@ -626,7 +1030,18 @@ static hipError_t launch_gemv(const int8_t* xq, const float* sx, const uint8_t* 
 enum TileCfg { kT256x256 = 0, kT256x128 = 1, kT128x256 = 2, kT128x128 = 3, kT256x32 = 4,
                kT128x32 = 5, kT256x256w8 = 6, kT128x256w8 = 7, kT256x128w8 = 8,
                kT256x256w8t = 9, kDma128x256 = 10, kDma256x128 = 11, kDma128x128 = 12,
-               kDma256x256 = 13, kT64x128 = 14, kNumCfg = 15 };
+               kDma256x256 = 13, kT64x128 = 14,
+               // register-W kernel: WO x KS waves, wave tile (16 FI) x (16 FJ), ring NA
+               kR256x64 = 15,      // WO 4, KS 1, FI 4, FJ 4
+               kR256x128 = 16,     // WO 4, KS 1, FI 4, FJ 8 (NA 2)
+               kR512x64 = 17,      // WO 4, KS 1, FI 8, FJ 4 (NA 2)
+               kR128x128 = 18,     // WO 2, KS 1, FI 4, FJ 8 (NA 2)
+               kR256x64k2 = 19,    // WO 4, KS 2, FI 4, FJ 4
+               kR128x64k2 = 20,    // WO 2, KS 2, FI 4, FJ 4
+               kR128x64k4 = 21,    // WO 2, KS 4, FI 4, FJ 4
+               kR128x128k2 = 22,   // WO 2, KS 2, FI 4, FJ 8 (NA 2)
+               kR512x64w8 = 23,    // WO 8, KS 1, FI 4, FJ 4
+               kNumCfg = 24 };
 
 struct Args {
   const int8_t* xq; const float* sx; const uint8_t* packed; int64_t pitch; const float* sw;
@@ -661,9 +1076,53 @@ static hipError_t launch_dma(const Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int WO, int KS, int FI, int FJ, int NA, bool SP, bool KA16, bool YBF16>
+static hipError_t launch_ra(const Args& a, hipStream_t s) {
+  using C = RaCfg<WO, KS, FI, FJ, NA>;
+  // 16-byte xq segments and 32-bit buffer offsets
+  if (!KA16 || a.T * a.K >= (int64_t(1) << 31))
+    return launch_cfg<128, 128, 2, 2, SP, KA16, YBF16>(a, s);
+  auto kern = k_gemm_ra<WO, KS, FI, FJ, NA, SP, YBF16>;
+  if (C::LDS > 65536) {
+    static bool set = false;
+    if (!set) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
+      if (e != hipSuccess) return e;
+      set = true;
+    }
+  }
+  // persistent grid: as many workgroups as fit on the chip at once (a
+  // multiple of the 8 XCDs, so each workgroup's tiles stay on one XCD's range)
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)kern, C::NT,
+                                                                C::LDS);
+    if (e != hipSuccess) return e;
+    per_cu = n > 0 ? n : 1;
+  }
+  const int64_t ntiles = cdiv(a.O, C::BM) * cdiv(a.T, C::BN);
+  int64_t nb = (int64_t)per_cu * device_info().cus;
+  if (nb >= ntiles) nb = ntiles;
+  else nb = nb / kXcds * kXcds;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(C::NT), C::LDS, s, a.xq, a.sx, a.packed,
+                     a.pitch, a.sw, a.sw_inc, a.T, a.O, a.K, a.y, a.acc);
+  return hipGetLastError();
+}
+
 template <bool SP, bool KA16, bool YBF16>
 static hipError_t launch_sel(int cfg, const Args& a, hipStream_t s) {
   switch (cfg) {
+    case kR256x64: return launch_ra<4, 1, 4, 4, 4, SP, KA16, YBF16>(a, s);
+    case kR256x128: return launch_ra<4, 1, 4, 8, 2, SP, KA16, YBF16>(a, s);
+    case kR512x64: return launch_ra<4, 1, 8, 4, 2, SP, KA16, YBF16>(a, s);
+    case kR128x128: return launch_ra<2, 1, 4, 8, 2, SP, KA16, YBF16>(a, s);
+    case kR256x64k2: return launch_ra<4, 2, 4, 4, 4, SP, KA16, YBF16>(a, s);
+    case kR128x64k2: return launch_ra<2, 2, 4, 4, 4, SP, KA16, YBF16>(a, s);
+    case kR128x64k4: return launch_ra<2, 4, 4, 4, 4, SP, KA16, YBF16>(a, s);
+    case kR128x128k2: return launch_ra<2, 2, 4, 8, 2, SP, KA16, YBF16>(a, s);
+    case kR512x64w8: return launch_ra<8, 1, 4, 4, 4, SP, KA16, YBF16>(a, s);
     case kT64x128: return launch_cfg<64, 128, 2, 2, SP, KA16, YBF16>(a, s);
     case kDma128x256: return launch_dma<128, 256, 2, 4, SP, YBF16, SP ? 3 : 4>(a, s);
     case kDma256x128: return launch_dma<256, 128, 4, 2, SP, YBF16, SP ? 4 : 5>(a, s);
@@ -683,9 +1142,14 @@ static hipError_t launch_sel(int cfg, const Args& a, hipStream_t s) {
 }
 
 // Tile choice for T > 32, from measured sweeps over the Qwen2.5-shaped FFN
-// projections on MI355X: 2:4 runs best on 256(O)x128(T) tiles; dense N:M on
-// 128x256 (8 waves), on 256x256 (8 waves) when K is long, and on smaller
-// tiles when O is too small to give every CU a workgroup.
+// projections on MI355X (2048-8192 tokens, K 896-11008):
+//  - too few 256x64 tiles to give every CU one: 128x64 tiles with the K-steps
+//    split between two wave groups (register-W kernel);
+//  - dense N:M, K >= 2048 and at least two 256x128 tiles per CU: 256x128
+//    (wave tile 64x128, half the code-expansion work per MFMA);
+//  - dense N:M otherwise: 256x64;
+//  - 2:4: 256x64 for short K, the LDS-staged 256x128 (8 waves) for medium K,
+//    512x64 (8 waves) for long K.
 static int choose_cfg(int64_t T, int64_t O, int64_t K, bool sp) {
   // tuning override (read on every call so tests can force each configuration)
   const char* ev = std::getenv("SBL_GEMM_TILE");
@@ -693,12 +1157,16 @@ static int choose_cfg(int64_t T, int64_t O, int64_t K, bool sp) {
   if (forced >= 0 && forced < kNumCfg) return forced;
   if (T <= 32) return O >= 8192 ? kT256x32 : kT128x32;
   const int cus = device_info().cus;
-  const int64_t t128 = cdiv(O, 128) * cdiv(T, 128);
-  if (t128 < cus) return kT64x128;          // too few tiles: smaller ones fill the chip
-  if (t128 < 2 * cus) return kT128x128;
-  if (sp) return kT256x128w8;
-  if (K >= 8192) return kT256x256w8;
-  return kT128x256w8;
+  const int64_t t64 = cdiv(O, 256) * cdiv(T, 64);
+  const int64_t t128 = cdiv(O, 256) * cdiv(T, 128);
+  if (t64 < cus) return kR128x64k2;
+  if (sp) {
+    if (K >= 4096) return kR512x64w8;
+    if (K >= 1536) return kT256x128w8;
+    return kR256x64;
+  }
+  if (K >= 2048 && t128 >= 2 * cus) return kR256x128;
+  return kR256x64;
 }
 
 hipError_t launch_gemm(const int8_t* xq, const float* sx, const void* packed, const float* sw,

@@ -340,12 +340,13 @@ def test_decode_bitnet_layer(S, T):
         assert_f32_close(host(y), ref["y"])
 
 
-@pytest.mark.parametrize("cfg", list(range(15)))
+@pytest.mark.parametrize("cfg", list(range(24)))
 def test_gemm_every_tile_config(S, cfg, monkeypatch):
     """Each workgroup-tile configuration of the GEMM, forced, on ragged shapes."""
     monkeypatch.setenv("SBL_GEMM_TILE", str(cfg))
     for (N, M) in [(6, 8), (2, 4), (2, 8)]:
-        for (T, O, K) in [(70, 300, 520), (300, 520, 1024), (17, 1000, 264), (200, 136, 1280)]:
+        for (T, O, K) in [(70, 300, 520), (300, 520, 1024), (17, 1000, 264), (200, 136, 1280),
+                          (40, 260, 64)]:
             if K % M:
                 continue
             log_case("gemm tile", cfg, N, M, T, O, K)
