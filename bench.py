@@ -8,6 +8,7 @@ A step is one pass of the whole forward hot path over one batch:
     per-token int8 quantization of each FFN input, absmean + N:M mask +
     RoundClip + pack of every master weight, the int8 x ternary GEMMs with
     dequant epilogue (gate and up fused into one GEMM over concatenated rows);
+    all projections' weights are prepared by one batched call;
   decode workload (BitNet-2B4T-shaped layer, prepacked 2:4 weights): for each
     of L distinct layer copies, int8 quantization of the layer inputs and the
     q|k|v, o, gate|up and down GEMMs.
@@ -83,8 +84,20 @@ class PrefillStep:
                                           device=dev)
             self.swr[xn] = torch.empty(O, dtype=torch.float32, device=dev)
             self.y[xn] = torch.empty((self.T, O), dtype=torch.bfloat16, device=dev)
-        nws = max(sbl.sbl_quant_mask_weight_workspace(l.O, l.K) for l in wl.linears)
-        self.ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+        # all projections' weights are prepared by one batched call
+        self.ws = torch.empty(sbl.sbl_quant_mask_weight_batch_workspace(len(wl.linears)),
+                              dtype=torch.uint8, device=dev)
+        self.prep_items = []
+        for xn, lins in self.groups.items():
+            off_p, off_o = 0, 0
+            for l in lins:
+                nb = sbl.sbl_packed_bytes(l.O, l.K, N, M)
+                self.prep_items.append({
+                    "w": self.W[l.name], "packed": self.packed[xn][off_p:off_p + nb],
+                    "sw_rows": self.swr[xn][off_o:off_o + l.O],
+                    "gamma_sw": torch.empty(2, dtype=torch.float32, device=dev)})
+                off_p += nb
+                off_o += l.O
         self.ops = sum(2.0 * self.T * l.O * l.K for l in wl.linears)
 
     def calls(self):
@@ -94,17 +107,8 @@ class PrefillStep:
         for xn in self.groups:
             out.append((f"quant_act[{xn}]",
                         lambda xn=xn: sbl.sbl_quant_act(self.x[xn], xq=self.xq[xn], sx=self.sx[xn])))
-        for xn, lins in self.groups.items():
-            off_p, off_o = 0, 0
-            for l in lins:
-                nb = sbl.sbl_packed_bytes(l.O, l.K, N, M)
-                pk = self.packed[xn][off_p:off_p + nb]
-                sr = self.swr[xn][off_o:off_o + l.O]
-                out.append((f"quant_mask_weight[{l.name}]",
-                            lambda l=l, pk=pk, sr=sr: sbl.sbl_quant_mask_weight(
-                                self.W[l.name], N, M, packed=pk, sw_rows=sr, ws=self.ws)))
-                off_p += nb
-                off_o += l.O
+        out.append((f"quant_mask_weight[{'+'.join(l.name for l in self.wl.linears)}]",
+                    lambda: sbl.sbl_quant_mask_weight_batch(self.prep_items, N, M, ws=self.ws)))
         for xn, lins in self.groups.items():
             O = sum(l.O for l in lins)
             out.append((f"gemm[{'+'.join(l.name for l in lins)}]",
@@ -113,6 +117,20 @@ class PrefillStep:
         return out
 
     cold_weights = False   # inputs of every call were just written by the step: cache-hot
+
+    def run(self):
+        """One step: act quant of the FFN input, one batched preparation of every
+        weight, the grouped GEMMs in order (a later group's input, e.g. the down
+        projection's, would come from the earlier GEMM in a real FFN)."""
+        calls = self.calls()
+        order = [c for c in calls if c[0].startswith("quant_mask_weight")]
+        for xn in self.groups:
+            order += [c for c in calls if c[0] in (f"quant_act[{xn}]",) or
+                      (c[0].startswith("gemm[") and c[0] == self._gemm_name(xn))]
+        run_all(order)
+
+    def _gemm_name(self, xn):
+        return f"gemm[{'+'.join(l.name for l in self.groups[xn])}]"
 
     def call_info(self, name):
         """(bound, algorithmic units per launch, unit) of a named call."""
@@ -125,8 +143,10 @@ class PrefillStep:
         if name.startswith("quant_act["):
             K = self.K_of[name[10:-1]]
             return "hbm", 2.0 * T * K + T * K + 4.0 * T, "bytes"
-        l = [l for l in self.wl.linears if name == f"quant_mask_weight[{l.name}]"][0]
-        return "hbm", 8.0 * l.O * l.K + sbl.sbl_packed_bytes(l.O, l.K, self.N, self.M), "bytes"
+        # weight preparation: W read twice (absmean pass, mask/code pass), packed written
+        return "hbm", sum(2.0 * l.O * l.K * self.W[l.name].element_size() +
+                          sbl.sbl_packed_bytes(l.O, l.K, self.N, self.M)
+                          for l in self.wl.linears), "bytes"
 
 
 # ----------------------------------------------------------------- decode --
@@ -202,6 +222,11 @@ class DecodeStep:
 
     cold_weights = True    # 30 layers of packed weights exceed the last-level cache
 
+    def run(self):
+        """One step: the layers' calls in order (each depends on the previous
+        one in a real decoder)."""
+        run_all(self.calls())
+
     def call_info(self, name):
         if name.startswith("gemm["):
             xn = [k for k, ls in self.groups.items()
@@ -234,8 +259,7 @@ def capture(fn):
 
 
 def time_steps(step, steps, warmup, eager):
-    calls = step.calls()
-    run = (lambda: run_all(calls)) if eager else capture(lambda: run_all(calls)).replay
+    run = step.run if eager else capture(step.run).replay
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()

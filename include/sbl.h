@@ -120,6 +120,46 @@ sbl_status sbl_quant_mask_weight(const void* w, sbl_dtype wdt, int64_t O, int64_
                                  float* gamma_sw, float* sw_rows, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
 
+/*
+ * One weight tensor of sbl_quant_mask_weight_batch. Every pointer is a
+ * device pointer with the meaning, layout and optionality of the argument of
+ * the same name of sbl_quant_mask_weight; O and K likewise.
+ */
+typedef struct sbl_weight_prep {
+  const void* w;
+  int64_t O;
+  int64_t K;
+  int8_t* w_eff;
+  uint8_t* mask;
+  void* packed;
+  float* gamma_sw;
+  float* sw_rows;
+} sbl_weight_prep;
+
+#define SBL_MAX_PREP_BATCH 8
+
+/* Workspace bytes sbl_quant_mask_weight_batch needs for count tensors. */
+sbl_status sbl_quant_mask_weight_batch_workspace(int count, size_t* bytes);
+
+/*
+ * a2 + a3 + a4 for count (1..SBL_MAX_PREP_BATCH) independent weight tensors
+ * of one dtype and one N:M pattern -- e.g. all projections of a layer -- in
+ * three kernel launches in total instead of three per tensor. The same
+ * passages of the Sparse-BitNet summary apply per tensor; each tensor gets
+ * exactly the outputs sbl_quant_mask_weight gives it (its own gamma and sw,
+ * mask, codes, packing).
+ * items: host array of count descriptors, read during the call only.
+ * Tensors may have different O and K; no output may overlap another
+ * tensor's input or output.
+ * ws: device workspace of at least sbl_quant_mask_weight_batch_workspace
+ *   bytes; no initialisation needed, scratch after the call.
+ * Errors: as sbl_quant_mask_weight, checked for every item before anything
+ * is enqueued; count out of range -> SBL_ERR_SHAPE.
+ */
+sbl_status sbl_quant_mask_weight_batch(const sbl_weight_prep* items, int count, sbl_dtype wdt,
+                                       int N, int M, float eps_w, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
 /* Size in bytes of the packed format for an [O, K] N:M tensor (O * pitch). */
 sbl_status sbl_packed_bytes(int64_t O, int64_t K, int N, int M, size_t* bytes);
 

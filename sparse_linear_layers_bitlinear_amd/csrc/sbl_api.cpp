@@ -9,6 +9,8 @@
 #include <cstdlib>
 #include <mutex>
 
+static_assert(sbl::kMaxPrepBatch == SBL_MAX_PREP_BATCH, "batch limit of the ABI");
+
 namespace sbl {
 
 static bool log_enabled() {
@@ -131,9 +133,43 @@ sbl_status sbl_quant_mask_weight(const void* w, sbl_dtype wdt, int64_t O, int64_
   for (const void* p : {w, (const void*)w_eff, (const void*)mask, (const void*)packed,
                         (const void*)gamma_sw, (const void*)sw_rows, (const void*)ws})
     if (p && !aligned16(p)) return SBL_ERR_ALIGN;
-  return hip_status(launch_quant_mask_weight(w, wdt == SBL_BF16, O, K, N, M, eps_w, w_eff, mask,
-                                             packed, gamma_sw, sw_rows, ws, stream),
+  const PrepTensor t{w, O, K, w_eff, mask, packed, gamma_sw, sw_rows};
+  return hip_status(launch_quant_mask_weight(&t, 1, wdt == SBL_BF16, N, M, eps_w, ws, stream),
                     "quant_mask_weight");
+}
+
+sbl_status sbl_quant_mask_weight_batch_workspace(int count, size_t* bytes) {
+  if (!bytes) return SBL_ERR_NULL;
+  if (count < 1 || count > SBL_MAX_PREP_BATCH) return SBL_ERR_SHAPE;
+  *bytes = prep_workspace_bytes(count);
+  return SBL_OK;
+}
+
+sbl_status sbl_quant_mask_weight_batch(const sbl_weight_prep* items, int count, sbl_dtype wdt,
+                                       int N, int M, float eps_w, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  if (!items) return SBL_ERR_NULL;
+  if (count < 1 || count > SBL_MAX_PREP_BATCH) return SBL_ERR_SHAPE;
+  if (!dtype_ok(wdt)) return SBL_ERR_DTYPE;
+  if (!eps_ok(eps_w)) return SBL_ERR_VALUE;
+  PrepTensor t[SBL_MAX_PREP_BATCH];
+  for (int i = 0; i < count; ++i) {
+    const sbl_weight_prep& it = items[i];
+    sbl_status st = check_wshape(it.O, it.K, N, M);
+    if (st != SBL_OK) return st;
+    if (it.O < 1 || it.O * it.K >= (int64_t(1) << 31)) return SBL_ERR_SHAPE;
+    if (!it.w || !it.gamma_sw) return SBL_ERR_NULL;
+    for (const void* p : {it.w, (const void*)it.w_eff, (const void*)it.mask,
+                          (const void*)it.packed, (const void*)it.gamma_sw,
+                          (const void*)it.sw_rows})
+      if (p && !aligned16(p)) return SBL_ERR_ALIGN;
+    t[i] = PrepTensor{it.w, it.O, it.K, it.w_eff, it.mask, it.packed, it.gamma_sw, it.sw_rows};
+  }
+  if (!ws) return SBL_ERR_WORKSPACE;
+  if (ws_bytes < prep_workspace_bytes(count)) return SBL_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SBL_ERR_ALIGN;
+  return hip_status(launch_quant_mask_weight(t, count, wdt == SBL_BF16, N, M, eps_w, ws, stream),
+                    "quant_mask_weight_batch");
 }
 
 sbl_status sbl_packed_bytes(int64_t O, int64_t K, int N, int M, size_t* bytes) {
@@ -223,8 +259,8 @@ sbl_status sbl_linear_fwd(const void* x, sbl_dtype xdt, const void* w_master, sb
   int64_t inc = sw_inc;
   if (!pre) {
     void* pk = base + L.packed;
-    e = launch_quant_mask_weight(w_master, wdt == SBL_BF16, O, K, N, M, eps_w, nullptr, nullptr,
-                                 pk, gsw, nullptr, base + L.prep, stream);
+    const PrepTensor t{w_master, O, K, nullptr, nullptr, pk, gsw, nullptr};
+    e = launch_quant_mask_weight(&t, 1, wdt == SBL_BF16, N, M, eps_w, base + L.prep, stream);
     if (e != hipSuccess) return hip_status(e, "linear_fwd/quant_mask_weight");
     packed = pk;
     sw = gsw + 1;

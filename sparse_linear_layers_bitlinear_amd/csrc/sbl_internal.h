@@ -21,13 +21,31 @@ __host__ __device__ inline int64_t row_pitch(int64_t K, int N, int M) {
 // 32-wide chunks per packed row record (both forms cover ceil(K/128)*4 chunks)
 __host__ __device__ inline int64_t row_chunks(int64_t K) { return cdiv(K, 128) * 4; }
 
-// Max workgroups of the absmean partial pass; fixes the workspace size.
+// Max workgroups of the absmean partial pass (over a whole batch of
+// weights); fixes the workspace size.
 constexpr int kAbsmeanMaxBlocks = 1024;
-// Workspace of the weight-prep path: partial exponent bins + device scalars.
+// Most weight tensors one batched preparation handles.
+constexpr int kMaxPrepBatch = 8;
+// Workspace of the weight-prep path: partial exponent bins of every block,
+// then the 16 summed bins of each weight (two fit the single-weight size).
 constexpr size_t kPrepScalarBytes = 256;
-inline size_t prep_workspace_bytes() {
-  return (size_t)kAbsmeanMaxBlocks * 16 * sizeof(unsigned long long) + kPrepScalarBytes;
+inline size_t prep_workspace_bytes(int count = 1) {
+  const size_t bins = (size_t)count * 16 * sizeof(unsigned long long);
+  return (size_t)kAbsmeanMaxBlocks * 16 * sizeof(unsigned long long) +
+         (bins > kPrepScalarBytes ? (bins + 255) / 256 * 256 : kPrepScalarBytes);
 }
+
+// One weight tensor of a (batched) preparation, as the library's launcher
+// receives it.
+struct PrepTensor {
+  const void* w;
+  int64_t O, K;
+  int8_t* w_eff;      // optional
+  uint8_t* mask;      // optional
+  void* packed;       // optional
+  float* gamma_sw;    // required, device float[2]
+  float* sw_rows;     // optional
+};
 
 struct DeviceInfo {
   int cus = 256;
@@ -38,9 +56,9 @@ const DeviceInfo& device_info();  // cached per device
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t T, int64_t K, int64_t ldx,
                             float eps, int8_t* xq, float* sx, hipStream_t s);
 
-hipError_t launch_quant_mask_weight(const void* w, bool bf16, int64_t O, int64_t K, int N, int M,
-                                    float eps, int8_t* w_eff, uint8_t* mask, void* packed,
-                                    float* gamma_sw, float* sw_rows, void* ws, hipStream_t s);
+// count in [1, kMaxPrepBatch]; every tensor of the batch shares dtype and N:M
+hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf16, int N, int M,
+                                    float eps, void* ws, hipStream_t s);
 
 hipError_t launch_pack(const int8_t* w_eff, const uint8_t* mask, int64_t O, int64_t K, int N,
                        int M, void* packed, hipStream_t s);

@@ -8,13 +8,16 @@
 //
 // Pipeline (all on the caller's stream, no host sync):
 //   k_absmean_partial  grid-stride over W; exact sum of |W| as integer
-//                      mantissa bins per 32-exponent window (order-free)
-//   k_absmean_finalize one workgroup: bins -> exact big integer -> RN fp64
-//                      -> / n -> fp32 gamma, sw = gamma + eps, and the
-//                      RoundClip threshold t (smallest |w| whose code is +-1)
-//   k_qmp              one thread per 32-wide chunk of a row, W staged
-//                      through LDS with coalesced 16-byte loads; rank-based
-//                      top-N-of-M mask, code = sign(w) * (|w| >= t), packing.
+//                      mantissa bins per 32-exponent window (order-free),
+//                      one vector of bins per block
+//   k_absmean_reduce   one workgroup sums the vectors into 16 bins
+//   k_qmp              a fifth wave per block turns the bins into an exact big
+//                      integer -> RN fp64 -> / n -> fp32 gamma, sw = gamma +
+//                      eps, and the RoundClip threshold t (smallest |w| whose
+//                      code is +-1); meanwhile one thread per 32-wide chunk of
+//                      a row stages W through LDS with coalesced 16-byte
+//                      loads and ranks it: top-N-of-M mask; then
+//                      code = sign(w) * (|w| >= t), packing.
 #include "sbl_internal.h"
 #include "device_util.cuh"
 
@@ -38,76 +41,215 @@ __device__ __forceinline__ void add96(uint32_t& a0, uint32_t& a1, uint32_t& a2, 
   a2 += (uint32_t)(mid >> 32);
 }
 
+// Register accumulator of one window. Window 3 holds every |w| in
+// [2^-31, 2) (e' in [96, 127]), where practically all weights lie; any other
+// term goes to the LDS bins, so the choice costs nothing in exactness.
+constexpr uint32_t kAbsWindow = 3;
 struct AbsSlot {
-  uint32_t tag = 0xFFFFFFFFu, a0 = 0, a1 = 0, a2 = 0;
+  uint32_t tag = kAbsWindow, a0 = 0, a1 = 0, a2 = 0;
 };
 
+// Term of |w| (bits u with the sign cleared): window tag and the 64-bit
+// integer m << (e' & 31), where m is the significand with the hidden bit for
+// normals (u - ((e' - 1) << 23) with e' = max(e, 1)). Zero gives v = 0.
+__device__ __forceinline__ void abs_term(uint32_t u, uint32_t& tag, uint64_t& v) {
+  const uint32_t ee = max(u >> 23, 1u);
+  const uint32_t m = u - ((ee - 1u) << 23);
+  tag = ee >> 5;
+  v = (uint64_t)m << (ee & 31u);
+}
+
+// Accumulate one |w| (any sign bit): terms of the slot's window go to the
+// 96-bit register accumulator with no branch (zeros add nothing, whatever
+// their window); others (rare for weights) are added to the LDS bins.
 __device__ __forceinline__ void abs_accumulate(AbsSlot& st, unsigned long long* bins, uint32_t u) {
-  u &= 0x7FFFFFFFu;
-  if (u == 0) return;
-  const uint32_t e = u >> 23;
-  const uint32_t m = (u & 0x7FFFFFu) | (e ? 0x800000u : 0u);
-  const uint32_t ee = e ? e : 1u;
-  const uint32_t tag = ee >> 5;
-  const uint64_t v = (uint64_t)m << (ee & 31u);
-  if (st.tag == 0xFFFFFFFFu) st.tag = tag;
-  if (tag == st.tag) {
-    add96(st.a0, st.a1, st.a2, v);
-  } else {
+  uint32_t tag;
+  uint64_t v;
+  abs_term(u & 0x7FFFFFFFu, tag, v);
+  const bool here = tag == st.tag || v == 0;
+  const uint64_t vh = here ? v : 0;
+  add96(st.a0, st.a1, st.a2, vh);
+  if (!here) {
     atomicAdd(&bins[2 * tag], (unsigned long long)(uint32_t)v);
     atomicAdd(&bins[2 * tag + 1], (unsigned long long)(v >> 32));
   }
 }
 
+// ---------------------------------------------------------------------------
+// Batches: every kernel below serves up to kMaxPrepBatch weight tensors in
+// one launch; a block finds its tensor from its index. The descriptor is a
+// kernel argument (by value), so the launches can be captured in a graph.
+// ---------------------------------------------------------------------------
+struct PrepItemK {
+  const void* w;
+  int8_t* w_eff;
+  uint8_t* mask;
+  uint8_t* packed;
+  float* gamma_sw;
+  float* sw_rows;
+  int64_t O, K;
+  int32_t C, pitch, code_chunks, mask_off;   // packed-record geometry
+  int32_t part0, nparts;                     // its partial vectors (= its partial-pass blocks)
+  int32_t blk1, blk3;                        // its first block in the partial / mask pass
+};
+struct PrepBatchK {
+  int32_t count, pad;
+  PrepItemK it[kMaxPrepBatch];
+};
+
+// Tensor of block `blk` given each tensor's first block (wave-uniform), and
+// that tensor's descriptor, selected with constant indices only.
+__device__ __forceinline__ int prep_index(const PrepBatchK& b, int blk, bool mask_pass) {
+  int i = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxPrepBatch; ++j)
+    if (j < b.count && blk >= (mask_pass ? b.it[j].blk3 : b.it[j].blk1)) i = j;
+  return i;
+}
+__device__ __forceinline__ PrepItemK prep_item(const PrepBatchK& b, int i) {
+  PrepItemK r = b.it[0];
+#pragma unroll
+  for (int j = 1; j < kMaxPrepBatch; ++j)
+    if (j == i) r = b.it[j];
+  return r;
+}
+
+// Slow path: add |w| to the LDS bins if it lies outside window 3.
+__device__ __forceinline__ void abs_accumulate_other(unsigned long long* bins, uint32_t u) {
+  uint32_t tag;
+  uint64_t v;
+  abs_term(u & 0x7FFFFFFFu, tag, v);
+  if (tag != kAbsWindow && v != 0) {
+    atomicAdd(&bins[2 * tag], (unsigned long long)(uint32_t)v);
+    atomicAdd(&bins[2 * tag + 1], (unsigned long long)(v >> 32));
+  }
+}
+
+// One vector of 16 bins per block. Each thread walks its vectors in batches
+// of kAbsBatch 16-byte loads, with the next batch in flight while the
+// current one is accumulated.
+//
+// Fast path (branch-free): |w| with e in [96, 127] -- window 3, where
+// practically every weight lies -- adds (m | 2^23) << (e & 31) to the 96-bit
+// register slot; zeros add nothing; any other term only marks its lane. A
+// marked lane re-reads its vectors afterwards and adds exactly those other
+// terms to the LDS bins (the exact sum is order-free, so the split is exact).
+constexpr int kAbsThreads = 256;
+constexpr int kAbsBatch = 8;
+constexpr int kAbsBlocks = 1024;  // partial vectors (at most)
+static_assert(kAbsBlocks <= kAbsmeanMaxBlocks && 16 * 8 <= kPrepScalarBytes,
+              "partials and summed bins must fit the weight-prep workspace");
+
+// window-3 term of a sign-cleared |w| (0 outside window 3); `other` set if
+// the value is nonzero and outside window 3
+__device__ __forceinline__ uint64_t abs_term3(uint32_t u, bool& other) {
+  const bool in3 = (u >> 28) == 3u;                          // e in [96, 127]
+  other |= !in3 && u != 0u;
+  const uint32_t m = in3 ? ((u & 0x7FFFFFu) | 0x800000u) : 0u;
+  return (uint64_t)m << ((u >> 23) & 31u);
+}
+
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_absmean_partial(const void* __restrict__ wv, int64_t n,
-                                                         unsigned long long* __restrict__ partials) {
+__global__ __launch_bounds__(kAbsThreads) void k_absmean_partial(const PrepBatchK batch,
+                                                                 unsigned long long* __restrict__ partials_all) {
+  const int item = prep_index(batch, blockIdx.x, false);
+  const PrepItemK pi = prep_item(batch, item);
+  const void* __restrict__ wv = pi.w;
+  const int64_t n = pi.O * pi.K;
+  const uint32_t lb = blockIdx.x - pi.blk1, nblk = pi.nparts;      // block within the tensor
+  unsigned long long* __restrict__ partials = partials_all + (int64_t)pi.part0 * 16;
   __shared__ unsigned long long bins[16];
   if (threadIdx.x < 16) bins[threadIdx.x] = 0;
   __syncthreads();
-  AbsSlot st;
+  uint32_t a0 = 0, a1 = 0, a2 = 0;                  // window-3 slot
+  bool other = false;
   constexpr int V = BF16 ? 8 : 4;  // elements per 16-byte load
-  constexpr int U = 8;             // loads in flight per thread
-  const int64_t nvec = n / V;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  auto consume = [&](const uint4& d) {
-    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+  constexpr int U = kAbsBatch;
+  // 32-bit indexing: n < 2^31. The trip count is uniform over the block
+  // (its first thread has the most vectors) and every load is unconditional:
+  // a lane past its own last vector re-reads that vector (distinct per lane)
+  // and drops the terms, so no lane-divergent branch guards a prefetch.
+  const uint32_t nvec = (uint32_t)(n / V);
+  const uint32_t stride = nblk * blockDim.x;
+  const uint32_t i0 = lb * blockDim.x + threadIdx.x;
+  const uint4* src = (const uint4*)wv;
+  auto consume = [&](const uint4& d, bool ok) {
+    const uint32_t w[4] = {ok ? d.x : 0u, ok ? d.y : 0u, ok ? d.z : 0u, ok ? d.w : 0u};
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       if constexpr (BF16) {
-        abs_accumulate(st, bins, (w[h] & 0xFFFFu) << 16);
-        abs_accumulate(st, bins, w[h] & 0xFFFF0000u);
+        add96(a0, a1, a2, abs_term3((w[h] << 16) & 0x7FFFFFFFu, other));
+        add96(a0, a1, a2, abs_term3(w[h] & 0x7FFF0000u, other));
       } else {
-        abs_accumulate(st, bins, w[h]);
+        add96(a0, a1, a2, abs_term3(w[h] & 0x7FFFFFFFu, other));
       }
     }
   };
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + (U - 1) * stride < nvec; i += U * stride) {
-    uint4 d[U];
+  const uint32_t b0 = lb * blockDim.x;
+  const uint32_t trips = b0 < nvec ? (nvec - b0 + stride - 1) / stride : 0;   // uniform
+  const uint32_t cnt = i0 < nvec ? (nvec - i0 + stride - 1) / stride : 0;
+  if (trips > 0) {
+    const uint32_t last = min(i0 + (cnt > 0 ? cnt - 1 : 0) * stride, nvec - 1);
+    auto load = [&](uint32_t k0, uint4 (&d)[U]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) d[u] = *((const uint4*)wv + i + u * stride);
+      for (int u = 0; u < U; ++u) d[u] = src[min(i0 + (k0 + u) * stride, last)];
+    };
+    uint4 d0[U], d1[U];
+    load(0, d0);
+    for (uint32_t k = 0; k < trips; k += 2 * U) {
+      load(k + U, d1);
 #pragma unroll
-    for (int u = 0; u < U; ++u) consume(d[u]);
+      for (int u = 0; u < U; ++u) consume(d0[u], k + u < cnt);
+      if (k + U >= trips) break;
+      load(k + 2 * U, d0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) consume(d1[u], k + U + u < cnt);
+    }
   }
-  for (; i < nvec; i += stride) consume(*((const uint4*)wv + i));
-  // tail elements (n % V) by block 0
-  if (blockIdx.x == 0) {
-    for (int64_t j = nvec * V + threadIdx.x; j < n; j += blockDim.x) {
+  AbsSlot st;                                       // slow path: other windows
+  st.a0 = st.a1 = st.a2 = 0;
+  if (other) {
+    for (uint32_t k = 0; k < cnt; ++k) {
+      const uint4 d = src[i0 + k * stride];
+      const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if constexpr (BF16) {
+          abs_accumulate_other(bins, w[h] << 16);
+          abs_accumulate_other(bins, w[h] & 0xFFFF0000u);
+        } else {
+          abs_accumulate_other(bins, w[h]);
+        }
+      }
+    }
+  }
+  // tail elements (n % V) by the tensor's first block
+  if (lb == 0) {
+    for (int64_t j = (int64_t)nvec * V + threadIdx.x; j < n; j += blockDim.x) {
       const uint32_t u = BF16 ? ((uint32_t)((const uint16_t*)wv)[j] << 16)
                               : ((const uint32_t*)wv)[j];
       abs_accumulate(st, bins, u);
     }
   }
-  if (st.tag != 0xFFFFFFFFu) {
+  // Fold the window-3 slots: a wave-wide sum and one atomic pair per wave
+  // (hundreds of same-address LDS atomics per block would serialize); the
+  // tail slot of block 0 per lane.
+  const unsigned long long lo = a0;
+  const unsigned long long hi = (unsigned long long)a1 | ((unsigned long long)a2 << 32);
+  const unsigned long long slo = wave_sum_u64(lo), shi = wave_sum_u64(hi);
+  if ((threadIdx.x & 63) == 0) {
+    atomicAdd(&bins[2 * kAbsWindow], slo);
+    atomicAdd(&bins[2 * kAbsWindow + 1], shi);
+  }
+  if (lb == 0 && (st.a0 | st.a1 | st.a2)) {
     atomicAdd(&bins[2 * st.tag], (unsigned long long)st.a0);
     atomicAdd(&bins[2 * st.tag + 1], (unsigned long long)st.a1 | ((unsigned long long)st.a2 << 32));
   }
   __syncthreads();
-  if (threadIdx.x < 16) partials[(int64_t)blockIdx.x * 16 + threadIdx.x] = bins[threadIdx.x];
+  if (threadIdx.x < 16) partials[(int64_t)lb * 16 + threadIdx.x] = bins[threadIdx.x];
 }
 
-// Device scalars written by the finalize kernel (inside the workspace).
+// Per-tensor scalars of the weight quantization.
 struct PrepScalars {
   float gamma;
   float sw;
@@ -129,52 +271,11 @@ __device__ float roundclip_threshold(float sw) {
   return t;
 }
 
-__global__ __launch_bounds__(256) void k_absmean_finalize(const unsigned long long* __restrict__ partials,
-                                                          int nblocks, int64_t n, float eps,
-                                                          float* __restrict__ gamma_sw,
-                                                          PrepScalars* __restrict__ scal) {
-  // thread t sums the 16 bins of blocks t, t + 256, ... (all loads independent),
-  // then a wave reduction and a 4-way combine in LDS
-  __shared__ unsigned long long red[4][16];
-  unsigned long long acc[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0;
-  for (int b = threadIdx.x; b < nblocks; b += 256) {
-    const uint4* p = (const uint4*)(partials + (int64_t)b * 16);
-    uint4 v[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = p[q];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      acc[2 * q] += (unsigned long long)v[q].x | ((unsigned long long)v[q].y << 32);
-      acc[2 * q + 1] += (unsigned long long)v[q].z | ((unsigned long long)v[q].w << 32);
-    }
-  }
-  // two-level reduction through LDS: 256 x 16 -> 16 x 16 -> 16
-  __shared__ unsigned long long part[16][257];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) part[j][threadIdx.x] = acc[j];
-  __syncthreads();
-  {
-    const int col = threadIdx.x & 15, grp = threadIdx.x >> 4;  // 16 groups of 16 rows
-    unsigned long long sum = 0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sum += part[col][grp * 16 + r];
-    __syncthreads();
-    part[col][grp] = sum;
-  }
-  __syncthreads();
-  if (threadIdx.x < 16) {
-    unsigned long long sum = 0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sum += part[threadIdx.x][r];
-    red[0][threadIdx.x] = sum;
-    red[1][threadIdx.x] = red[2][threadIdx.x] = red[3][threadIdx.x] = 0;
-  }
-  __syncthreads();
-  if (threadIdx.x != 0) return;
-
-  // Exact sum in units of 2^-150 as 32-bit limbs (registers only: constant indices).
+// 16 summed bins -> correctly rounded fp64 sum -> gamma, sw, threshold.
+// The bins are exact integers: bin 2w holds low parts and bin 2w+1 high parts
+// of window w (weight 2^(32 w - 150)).
+__device__ PrepScalars scalars_from_bins(const unsigned long long* bins, int64_t n, float eps) {
+  // exact sum in units of 2^-150 as 32-bit limbs (registers only: constant indices)
   constexpr int NL = 12;
   uint32_t L[NL];
   {
@@ -183,9 +284,7 @@ __global__ __launch_bounds__(256) void k_absmean_finalize(const unsigned long lo
     for (int i = 0; i <= NL; ++i) w[i] = 0;
 #pragma unroll
     for (int tag = 0; tag < 8; ++tag) {
-      const unsigned long long lo = red[0][2 * tag] + red[1][2 * tag] + red[2][2 * tag] + red[3][2 * tag];
-      const unsigned long long hi = red[0][2 * tag + 1] + red[1][2 * tag + 1] + red[2][2 * tag + 1] +
-                                    red[3][2 * tag + 1];
+      const unsigned long long lo = bins[2 * tag], hi = bins[2 * tag + 1];
       w[tag] += lo & 0xFFFFFFFFull;
       w[tag + 1] += (lo >> 32) + (hi & 0xFFFFFFFFull);
       w[tag + 2] += hi >> 32;
@@ -223,26 +322,67 @@ __global__ __launch_bounds__(256) void k_absmean_finalize(const unsigned long lo
     S = ldexp((double)mant, 43 - c + 32 * (top - 2) - 150);
   }
   const double q = S / (double)n;
-  const float gamma = (float)q;
-  const float sw = gamma + eps;
-  const float t = roundclip_threshold(sw);
-  gamma_sw[0] = gamma;
-  gamma_sw[1] = sw;
-  scal->gamma = gamma;
-  scal->sw = sw;
-  scal->t_bits = __float_as_uint(t);
-  scal->pad = 0;
+  PrepScalars r;
+  r.gamma = (float)q;
+  r.sw = r.gamma + eps;
+  r.t_bits = __float_as_uint(roundclip_threshold(r.sw));
+  r.pad = 0;
+  return r;
+}
+
+// Sum of the per-block partial vectors into the 16 bins (one workgroup; the
+// serial part that turns the bins into gamma and the threshold runs in the
+// mask/pack kernel, overlapped with its W staging).
+__global__ __launch_bounds__(256) void k_absmean_reduce(const PrepBatchK batch,
+                                                        const unsigned long long* __restrict__ partials_all,
+                                                        unsigned long long* __restrict__ bins_all) {
+  const PrepItemK pi = prep_item(batch, blockIdx.x);     // one block per tensor
+  const unsigned long long* __restrict__ partials = partials_all + (int64_t)pi.part0 * 16;
+  const int nparts = pi.nparts;
+  unsigned long long* __restrict__ bins_out = bins_all + (int64_t)blockIdx.x * 16;
+  unsigned long long acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0;
+  for (int b = threadIdx.x; b < nparts; b += 256) {
+    const uint4* p = (const uint4*)(partials + (int64_t)b * 16);
+    uint4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = p[q];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      acc[2 * q] += (unsigned long long)v[q].x | ((unsigned long long)v[q].y << 32);
+      acc[2 * q + 1] += (unsigned long long)v[q].z | ((unsigned long long)v[q].w << 32);
+    }
+  }
+  // 256 x 16 -> 16 x 16 -> 16 through LDS (independent accesses)
+  __shared__ unsigned long long part[16 * 257];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) part[j * 257 + threadIdx.x] = acc[j];
+  __syncthreads();
+  const int col = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  unsigned long long sum = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sum += part[col * 257 + grp * 16 + r];
+  __syncthreads();
+  part[col * 257 + grp] = sum;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    unsigned long long t = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t += part[threadIdx.x * 257 + r];
+    bins_out[threadIdx.x] = t;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Mask + RoundClip + pack. One thread per 32-wide chunk (o, c), c in
 // [0, ceil(K/128)*4), which covers every byte of a packed row record.
-// A block's 256 chunks are staged through LDS (row stride 33 words, so the
-// per-thread reads below are bank-conflict free) with 16-byte loads in which
-// consecutive lanes read consecutive addresses.
+// A block's chunks are staged through LDS (row stride 36 words: 16-byte
+// accesses on both sides, bank-conflict free) with 16-byte global loads in
+// which consecutive lanes read consecutive addresses.
 // ---------------------------------------------------------------------------
-constexpr int kChunksPerBlock = 256;
-constexpr int kLdsStride = 33;
+constexpr int kChunksPerBlock = 128;
+constexpr int kLdsStride = 36;   // words per staged chunk: 16-byte aligned, conflict-free
 
 // Keep bits of one group of M magnitudes (bit i = slot i kept):
 // rank_i = #{j : |w_j| > |w_i|} + #{j < i : |w_j| == |w_i|}; keep iff rank_i < N.
@@ -286,27 +426,61 @@ __device__ __forceinline__ uint32_t byte_slice16(uint32_t lo, uint32_t hi) {
   return v;
 }
 
+// Workgroup: one thread per chunk and one more wave that turns the summed
+// absmean bins into gamma, sw and the threshold (a serial computation) while
+// the others stage W and rank the groups; the threshold is needed only for
+// the codes.
+constexpr int kQmpThreads = kChunksPerBlock + 64;
+
 template <bool BF16, int M, bool IDX>
-__global__ __launch_bounds__(256) void k_qmp(const void* __restrict__ wv, int64_t O, int64_t K,
-                                             int N, int64_t C, const PrepScalars* __restrict__ scal,
-                                             uint8_t* __restrict__ packed, int64_t pitch,
-                                             int64_t code_chunks, int64_t mask_off,
-                                             int8_t* __restrict__ w_eff,
-                                             uint8_t* __restrict__ mask_out,
-                                             float* __restrict__ sw_rows) {
-  __shared__ uint32_t lds[kChunksPerBlock * kLdsStride];
+__global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int N,
+                                                     const unsigned long long* __restrict__ bins_all,
+                                                     float eps) {
+  const int item = prep_index(batch, blockIdx.x, true);
+  const PrepItemK pi = prep_item(batch, item);
+  const void* __restrict__ wv = pi.w;
+  const int64_t O = pi.O, K = pi.K, C = pi.C, pitch = pi.pitch;
+  const int64_t code_chunks = pi.code_chunks, mask_off = pi.mask_off;
+  int8_t* __restrict__ w_eff = pi.w_eff;
+  uint8_t* __restrict__ mask_out = pi.mask;
+  uint8_t* __restrict__ packed = pi.packed;
+  float* __restrict__ gamma_sw = pi.gamma_sw;
+  float* __restrict__ sw_rows = pi.sw_rows;
+  const unsigned long long* __restrict__ bins = bins_all + (int64_t)item * 16;
+  const uint32_t lb = blockIdx.x - pi.blk3;                // block within the tensor
+  __shared__ __attribute__((aligned(16))) uint32_t lds[kChunksPerBlock * kLdsStride];
+  __shared__ unsigned long long red[16];
+  __shared__ PrepScalars scal;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (wave == kChunksPerBlock / 64) {
+    // ---- scalar wave: the 16 summed bins -> gamma, sw, threshold ----
+    const int lane = threadIdx.x & 63;
+    if (lane < 16) red[lane] = bins[lane];
+    __builtin_amdgcn_wave_barrier();
+    __syncthreads();                                    // (1) W staged by the other waves
+    if (lane == 0) {
+      const PrepScalars sc = scalars_from_bins(red, O * K, eps);
+      scal = sc;
+      if (lb == 0) {
+        gamma_sw[0] = sc.gamma;
+        gamma_sw[1] = sc.sw;
+      }
+    }
+    __syncthreads();                                    // (2) scalars visible
+    return;
+  }
   // all chunk/row indices fit in 32 bits: O * C < 2^31 (O * K < 2^31)
   const uint32_t total = (uint32_t)(O * C), C32 = (uint32_t)C, K32 = (uint32_t)K;
-  const uint32_t base = blockIdx.x * kChunksPerBlock;
+  const uint32_t base = lb * kChunksPerBlock;
 
-  // ---- stage: raw bits of 256 chunks x 32 elements ----
+  // ---- stage: raw bits of the block's chunks x 32 elements ----
   constexpr int V = BF16 ? 8 : 4;              // elements per 16-byte piece
   constexpr int PIECES = 32 / V;               // pieces per chunk = pieces per thread
   const bool rows16 = ((K32 * (BF16 ? 2u : 4u)) % 16u) == 0;
   uint4 d[PIECES];
 #pragma unroll
   for (int q = 0; q < PIECES; ++q) {
-    const uint32_t p = threadIdx.x + 256u * q;
+    const uint32_t p = threadIdx.x + (uint32_t)kChunksPerBlock * q;
     const uint32_t ch = base + p / PIECES, pc = p % PIECES;
     d[q] = make_uint4(0, 0, 0, 0);
     if (ch < total) {
@@ -329,42 +503,50 @@ __global__ __launch_bounds__(256) void k_qmp(const void* __restrict__ wv, int64_
   }
 #pragma unroll
   for (int q = 0; q < PIECES; ++q) {
-    const uint32_t p = threadIdx.x + 256u * q;
+    const uint32_t p = threadIdx.x + (uint32_t)kChunksPerBlock * q;
     const uint32_t lc = p / PIECES, pc = p % PIECES;
     const uint32_t w[4] = {d[q].x, d[q].y, d[q].z, d[q].w};
     uint32_t* dst = lds + lc * kLdsStride + pc * V;
     if constexpr (BF16) {
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        dst[2 * h] = (w[h] & 0xFFFFu) << 16;
-        dst[2 * h + 1] = w[h] & 0xFFFF0000u;
-      }
+      *(uint4*)dst = make_uint4(w[0] << 16, w[0] & 0xFFFF0000u, w[1] << 16, w[1] & 0xFFFF0000u);
+      *(uint4*)(dst + 4) =
+          make_uint4(w[2] << 16, w[2] & 0xFFFF0000u, w[3] << 16, w[3] & 0xFFFF0000u);
     } else {
-#pragma unroll
-      for (int h = 0; h < 4; ++h) dst[h] = w[h];
+      *(uint4*)dst = d[q];
     }
   }
-  __syncthreads();
+  __syncthreads();                                    // (1) W staged
 
   const uint32_t ch = base + threadIdx.x;
-  if (ch >= total) return;
-  const uint32_t o = ch / C32, c = ch - o * C32;
+  const bool active = ch < total;
+  const uint32_t o = active ? ch / C32 : 0u, c = ch - o * C32;
   const uint32_t k0 = 32u * c;
-  const uint32_t tb = scal->t_bits;
 
-  uint32_t a[32], sgn = 0, nz = 0;
+  // the mask and the signs need no scalar: computed before barrier (2)
+  uint32_t a[32], sgn = 0, keep = 0;
+  if (active) {
+    uint32_t raw[32];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    const uint32_t u = lds[threadIdx.x * kLdsStride + e];
-    a[e] = u & 0x7FFFFFFFu;
-    sgn |= (u >> 31) << e;
-    nz |= ((tb - 1u - a[e]) >> 31) << e;          // a >= tb  (both < 2^31, tb >= 1)
+    for (int e4 = 0; e4 < 8; ++e4) {
+      const uint4 v = *(const uint4*)(lds + threadIdx.x * kLdsStride + 4 * e4);
+      raw[4 * e4] = v.x; raw[4 * e4 + 1] = v.y; raw[4 * e4 + 2] = v.z; raw[4 * e4 + 3] = v.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      a[e] = raw[e] & 0x7FFFFFFFu;
+      sgn |= (raw[e] >> 31) << e;
+    }
+#pragma unroll
+    for (int g = 0; g < 32 / M; ++g) keep |= topn_keep_bits<M>(a + g * M, N) << (g * M);
   }
-  const uint32_t valid = k0 >= K32 ? 0u : (K32 - k0 >= 32u ? 0xFFFFFFFFu : ((1u << (K32 - k0)) - 1u));
-
-  uint32_t keep = 0;
+  __syncthreads();                                    // (2) scalars from the fifth wave
+  if (!active) return;
+  const PrepScalars sc = scal;
+  const uint32_t tb = sc.t_bits;
+  uint32_t nz = 0;
 #pragma unroll
-  for (int g = 0; g < 32 / M; ++g) keep |= topn_keep_bits<M>(a + g * M, N) << (g * M);
+  for (int e = 0; e < 32; ++e) nz |= ((tb - 1u - a[e]) >> 31) << e;   // a >= tb (both < 2^31, tb >= 1)
+  const uint32_t valid = k0 >= K32 ? 0u : (K32 - k0 >= 32u ? 0xFFFFFFFFu : ((1u << (K32 - k0)) - 1u));
   const uint32_t kn = nz & keep & valid;          // nonzero code, kept
   const uint32_t kneg = kn & sgn;                 // ... and negative
 
@@ -377,7 +559,7 @@ __global__ __launch_bounds__(256) void k_qmp(const void* __restrict__ wv, int64_
       if (mask_out) mask_out[idx] = (uint8_t)((keep & valid) >> e & 1u);
     }
   }
-  if (sw_rows && c == 0) sw_rows[o] = scal->sw;
+  if (sw_rows && c == 0) sw_rows[o] = sc.sw;
 
   if (!packed) return;
   uint8_t* rec = packed + (int64_t)o * pitch;
@@ -402,49 +584,64 @@ __global__ __launch_bounds__(256) void k_qmp(const void* __restrict__ wv, int64_
   }
 }
 
-template <bool BF16>
-static hipError_t launch_qmp_typed(const void* w, int64_t O, int64_t K, int N, int M,
-                                   const PrepScalars* scal, uint8_t* packed, int8_t* w_eff,
-                                   uint8_t* mask, float* sw_rows, hipStream_t s) {
-  const int64_t C = row_chunks(K);
-  const int64_t pitch = row_pitch(K, N, M);
-  const int64_t code_chunks = dense_code_bytes(K) / 8;
-  const int64_t mask_off = dense_code_bytes(K);
-  const dim3 grid((unsigned)cdiv(O * C, kChunksPerBlock)), block(256);
-  if (index_form(N, M))
-    hipLaunchKernelGGL((k_qmp<BF16, 4, true>), grid, block, 0, s, w, O, K, N, C, scal, packed,
-                       pitch, code_chunks, mask_off, w_eff, mask, sw_rows);
-  else if (M == 4)
-    hipLaunchKernelGGL((k_qmp<BF16, 4, false>), grid, block, 0, s, w, O, K, N, C, scal, packed,
-                       pitch, code_chunks, mask_off, w_eff, mask, sw_rows);
-  else
-    hipLaunchKernelGGL((k_qmp<BF16, 8, false>), grid, block, 0, s, w, O, K, N, C, scal, packed,
-                       pitch, code_chunks, mask_off, w_eff, mask, sw_rows);
-  return hipGetLastError();
-}
-
-hipError_t launch_quant_mask_weight(const void* w, bool bf16, int64_t O, int64_t K, int N, int M,
-                                    float eps, int8_t* w_eff, uint8_t* mask, void* packed,
-                                    float* gamma_sw, float* sw_rows, void* ws, hipStream_t s) {
-  const int64_t n = O * K;
-  auto* partials = (unsigned long long*)ws;
-  auto* scal = (PrepScalars*)((char*)ws + (size_t)kAbsmeanMaxBlocks * 16 * sizeof(unsigned long long));
+hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf16, int N, int M,
+                                    float eps, void* ws, hipStream_t s) {
+  PrepBatchK b{};
+  b.count = count;
   const int V = bf16 ? 8 : 4;
-  // about 8 vectors per thread, at most 512 blocks (two per CU)
-  const int64_t want = cdiv(cdiv(n, V), 256 * 8);
-  const int nblocks = (int)(want < 1 ? 1 : (want > 512 ? 512 : want));
+  const int cap = kAbsBlocks / count;          // partial vectors per tensor, at most
+  int parts = 0, blk3 = 0;
+  for (int i = 0; i < count; ++i) {
+    const PrepTensor& t = items[i];
+    PrepItemK& k = b.it[i];
+    k.w = t.w;
+    k.w_eff = t.w_eff;
+    k.mask = t.mask;
+    k.packed = (uint8_t*)t.packed;
+    k.gamma_sw = t.gamma_sw;
+    k.sw_rows = t.sw_rows;
+    k.O = t.O;
+    k.K = t.K;
+    k.C = (int32_t)row_chunks(t.K);
+    k.pitch = (int32_t)row_pitch(t.K, N, M);
+    k.code_chunks = (int32_t)(dense_code_bytes(t.K) / 8);
+    k.mask_off = (int32_t)dense_code_bytes(t.K);
+    // about one batch of loads per thread (the exact accumulation is VALU
+    // work: spread it over many waves)
+    const int64_t want = cdiv(cdiv(t.O * t.K, V), (int64_t)kAbsThreads * kAbsBatch);
+    const int nb = (int)(want < 1 ? 1 : (want > cap ? cap : want));
+    k.part0 = parts;
+    k.nparts = nb;
+    k.blk1 = parts;
+    parts += nb;
+    k.blk3 = blk3;
+    blk3 += (int)cdiv(t.O * (int64_t)k.C, kChunksPerBlock);
+  }
+  auto* partials = (unsigned long long*)ws;
+  auto* bins = partials + (size_t)kAbsmeanMaxBlocks * 16;
   if (bf16)
-    hipLaunchKernelGGL((k_absmean_partial<true>), dim3(nblocks), dim3(256), 0, s, w, n, partials);
+    hipLaunchKernelGGL((k_absmean_partial<true>), dim3(parts), dim3(kAbsThreads), 0, s, b, partials);
   else
-    hipLaunchKernelGGL((k_absmean_partial<false>), dim3(nblocks), dim3(256), 0, s, w, n, partials);
+    hipLaunchKernelGGL((k_absmean_partial<false>), dim3(parts), dim3(kAbsThreads), 0, s, b, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_absmean_finalize, dim3(1), dim3(256), 0, s, partials, nblocks, n, eps,
-                     gamma_sw, scal);
+  hipLaunchKernelGGL(k_absmean_reduce, dim3(count), dim3(256), 0, s, b, partials, bins);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return bf16 ? launch_qmp_typed<true>(w, O, K, N, M, scal, (uint8_t*)packed, w_eff, mask, sw_rows, s)
-              : launch_qmp_typed<false>(w, O, K, N, M, scal, (uint8_t*)packed, w_eff, mask, sw_rows, s);
+  const dim3 grid((unsigned)blk3), block(kQmpThreads);
+#define SBL_QMP(BV, MV, IV) \
+  hipLaunchKernelGGL((k_qmp<BV, MV, IV>), grid, block, 0, s, b, N, bins, eps)
+  if (bf16) {
+    if (index_form(N, M)) SBL_QMP(true, 4, true);
+    else if (M == 4) SBL_QMP(true, 4, false);
+    else SBL_QMP(true, 8, false);
+  } else {
+    if (index_form(N, M)) SBL_QMP(false, 4, true);
+    else if (M == 4) SBL_QMP(false, 4, false);
+    else SBL_QMP(false, 8, false);
+  }
+#undef SBL_QMP
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -28,6 +28,17 @@ class SblError(RuntimeError):
         super().__init__(f"{fn} failed: {msg}")
 
 
+class WeightPrep(ctypes.Structure):
+    """sbl_weight_prep: one tensor of sbl_quant_mask_weight_batch."""
+    _fields_ = [("w", ctypes.c_void_p), ("O", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("w_eff", ctypes.c_void_p), ("mask", ctypes.c_void_p),
+                ("packed", ctypes.c_void_p), ("gamma_sw", ctypes.c_void_p),
+                ("sw_rows", ctypes.c_void_p)]
+
+
+SBL_MAX_PREP_BATCH = 8
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -41,6 +52,8 @@ def _load():
         "sbl_quant_act": ([P, I, I64, I64, I64, F, P, P, P], I),
         "sbl_quant_mask_weight_workspace": ([I64, I64, ctypes.POINTER(S)], I),
         "sbl_quant_mask_weight": ([P, I, I64, I64, I, I, F, P, P, P, P, P, P, S, P], I),
+        "sbl_quant_mask_weight_batch_workspace": ([I, ctypes.POINTER(S)], I),
+        "sbl_quant_mask_weight_batch": ([ctypes.POINTER(WeightPrep), I, I, I, I, F, P, S, P], I),
         "sbl_packed_bytes": ([I64, I64, I, I, ctypes.POINTER(S)], I),
         "sbl_pack": ([P, P, I64, I64, I, I, P, P], I),
         "sbl_unpack": ([P, I64, I64, I, I, P, P, P], I),
@@ -133,6 +146,43 @@ def sbl_quant_mask_weight(w: torch.Tensor, N: int, M: int, eps_w: float = 1e-5,
         _ptr(packed), _ptr(out["gamma_sw"]), _ptr(sw_rows), _ptr(ws), ws.numel(),
         _stream(dev)))
     return out
+
+
+def sbl_quant_mask_weight_batch_workspace(count: int) -> int:
+    return _size_out(_lib.sbl_quant_mask_weight_batch_workspace, count)
+
+
+def sbl_quant_mask_weight_batch(items, N: int, M: int, eps_w: float = 1e-5, ws=None):
+    """items: list of dicts with w [O, K] (one dtype for all, contiguous) and
+    optional output tensors packed, sw_rows, w_eff, mask, gamma_sw (allocated
+    here when absent: gamma_sw always, packed unless want_packed=False).
+    Returns the list of dicts with every output filled in."""
+    assert 1 <= len(items) <= SBL_MAX_PREP_BATCH
+    dev = items[0]["w"].device
+    dt = items[0]["w"].dtype
+    arr = (WeightPrep * len(items))()
+    outs = []
+    for i, it in enumerate(items):
+        w = it["w"]
+        assert w.dim() == 2 and w.is_contiguous() and w.dtype == dt
+        O, K = w.shape
+        o = dict(it)
+        if o.get("gamma_sw") is None:
+            o["gamma_sw"] = torch.empty(2, dtype=torch.float32, device=dev)
+        if o.get("packed") is None and o.get("want_packed", True):
+            o["packed"] = torch.empty(sbl_packed_bytes(O, K, N, M), dtype=torch.uint8,
+                                      device=dev)
+        for k in ("packed", "sw_rows", "w_eff", "mask"):
+            o.setdefault(k, None)
+        arr[i] = WeightPrep(_ptr(w), O, K, _ptr(o["w_eff"]), _ptr(o["mask"]), _ptr(o["packed"]),
+                            _ptr(o["gamma_sw"]), _ptr(o["sw_rows"]))
+        outs.append(o)
+    nws = sbl_quant_mask_weight_batch_workspace(len(items))
+    if ws is None:
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    _check("sbl_quant_mask_weight_batch", _lib.sbl_quant_mask_weight_batch(
+        arr, len(items), _dt(dt), N, M, eps_w, _ptr(ws), ws.numel(), _stream(dev)))
+    return outs
 
 
 def sbl_pack(w_eff: torch.Tensor, mask: torch.Tensor, N: int, M: int, packed=None):

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["sbl_quant_act", "sbl_quant_mask_weight", "sbl_pack", "sbl_unpack", "sbl_gemm",
               "sbl_linear_fwd", "sbl_packed_bytes", "sbl_quant_mask_weight_workspace",
-              "sbl_linear_fwd_workspace", "sbl_status_string", "sbl_version"]:
+              "sbl_linear_fwd_workspace", "sbl_status_string", "sbl_version",
+              "sbl_quant_mask_weight_batch", "sbl_quant_mask_weight_batch_workspace"]:
         assert n in names
 
 
@@ -126,3 +127,39 @@ def test_pack_validation(S):
     assert L.sbl_pack(None, FAKE, 4, 16, 6, 8, FAKE, None) == 1
     assert L.sbl_unpack(FAKE, 4, 16, 6, 8, MIS, FAKE, None) == 5
     assert L.sbl_pack(FAKE, FAKE, 0, 16, 6, 8, FAKE, None) == 0
+
+
+def test_weight_batch_validation(S):
+    L = S.lib
+    WP = S.WeightPrep
+    ws = 1 << 20
+
+    def items(*specs):
+        arr = (WP * max(1, len(specs)))()
+        for i, (O, K, w, g) in enumerate(specs):
+            arr[i] = WP(w, O, K, None, None, FAKE, g, None)
+        return arr
+
+    ok = (64, 256, FAKE, FAKE)
+    call = lambda arr, cnt, N=6, M=8, dt=1, eps=1e-5, wsp=FAKE, wsb=ws: \
+        L.sbl_quant_mask_weight_batch(arr, cnt, dt, N, M, eps, wsp, wsb, None)
+    assert call(None, 1) == 1                                     # no items
+    assert call(items(ok), 0) == 2                                # count < 1
+    assert call(items(*[ok] * 9), 9) == 2                         # count > max
+    assert call(items(ok), 1, dt=5) == 4                          # dtype
+    assert call(items(ok), 1, eps=0.0) == 8                       # eps
+    assert call(items(ok, (64, 252, FAKE, FAKE)), 2) == 2         # second item K % M
+    assert call(items(ok, (64, 256, FAKE, None)), 2) == 1         # second item gamma_sw
+    assert call(items(ok, (64, 256, MIS, FAKE)), 2) == 5          # second item misaligned
+    assert call(items(ok), 1, N=9) == 3                           # N:M
+    assert call(items(ok, ok, ok), 3, wsb=16) == 6                # workspace size
+    assert call(items(ok), 1, wsp=None) == 6
+    n = ctypes.c_size_t()
+    for cnt in range(1, 9):
+        assert L.sbl_quant_mask_weight_batch_workspace(cnt, ctypes.byref(n)) == 0
+        assert n.value >= cnt * 128
+    single = ctypes.c_size_t()
+    assert L.sbl_quant_mask_weight_workspace(64, 256, ctypes.byref(single)) == 0
+    assert L.sbl_quant_mask_weight_batch_workspace(1, ctypes.byref(n)) == 0 and n.value == single.value
+    assert L.sbl_quant_mask_weight_batch_workspace(0, ctypes.byref(n)) == 2
+    assert L.sbl_quant_mask_weight_batch_workspace(9, ctypes.byref(n)) == 2

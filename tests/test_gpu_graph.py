@@ -66,3 +66,75 @@ def test_graph_replays_match_eager(S, N, M, T, O, K):
         ref = o.linear_fwd(xs[i], Ws[i], N, M)
         assert np.array_equal(packed_graph.reshape(O, -1), o.pack(ref["w_eff"], ref["mask"], N, M))
         _ = torch.zeros(1000, device=dev).sum()  # unrelated eager work between replays
+
+
+def test_graph_multistream_matches_eager(S):
+    """Weight preparation of two projections on two side streams, forked from
+    and joined back into the capturing stream (the schedule the benchmark
+    times); every replay equals the eager sequential result."""
+    log_case("graph multistream", 6, 8, 96, 320, 512)
+    dev = torch.device("cuda:0")
+    N, M, T, K = 6, 8, 96, 512
+    Os = [320, 192]
+    Wa, x = make_linear_inputs(T, Os[0], K, seed=7)
+    Wb, _ = make_linear_inputs(T, Os[1], K, seed=8)
+    Ws = [to_dev(Wa), to_dev(Wb)]
+    x_in = bf16_tensor(x).clone()
+    O = sum(Os)
+    nb = [S.sbl_packed_bytes(o, K, N, M) for o in Os]
+    xq = torch.empty((T, K), dtype=torch.int8, device=dev)
+    sx = torch.empty(T, dtype=torch.float32, device=dev)
+    packed = torch.empty(sum(nb), dtype=torch.uint8, device=dev)
+    swr = torch.empty(O, dtype=torch.float32, device=dev)
+    wss = [torch.empty(S.sbl_quant_mask_weight_workspace(o, K), dtype=torch.uint8, device=dev)
+           for o in Os]
+    y = torch.empty((T, O), dtype=torch.float32, device=dev)
+    sides = [torch.cuda.Stream(), torch.cuda.Stream()]
+
+    def prep(i):
+        off_p, off_o = sum(nb[:i]), sum(Os[:i])
+        S.sbl_quant_mask_weight(Ws[i], N, M, packed=packed[off_p:off_p + nb[i]],
+                                sw_rows=swr[off_o:off_o + Os[i]], ws=wss[i])
+
+    def step():
+        main = torch.cuda.current_stream()
+        for i, side in enumerate(sides):
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                prep(i)
+        S.sbl_quant_act(x_in, xq=xq, sx=sx)
+        for side in sides:
+            main.wait_stream(side)
+        S.sbl_gemm(xq, sx, packed, swr, O, N, M, out_dtype=torch.float32, y=y)
+
+    def eager_sequential():
+        prep(0)
+        prep(1)
+        S.sbl_quant_act(x_in, xq=xq, sx=sx)
+        S.sbl_gemm(xq, sx, packed, swr, O, N, M, out_dtype=torch.float32, y=y)
+        torch.cuda.synchronize()
+        return host(y).copy(), host(packed).copy()
+
+    y_ref, p_ref = eager_sequential()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        y.zero_()
+        packed.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y), y_ref)
+        assert np.array_equal(host(packed), p_ref)
+        _ = torch.zeros(1000, device=dev).sum()
+    for i, Wi in enumerate([Wa, Wb]):
+        r = o.quant_mask_weight(Wi, N, M)
+        off_p = sum(nb[:i])
+        assert np.array_equal(p_ref[off_p:off_p + nb[i]].reshape(Os[i], -1),
+                              o.pack(r[0], r[1], N, M))

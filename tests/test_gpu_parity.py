@@ -120,6 +120,56 @@ def test_quant_mask_weight_parity(S, N, M, O, K, dt):
     assert np.all(f32_bits(host(r["sw_rows"])) == f32_bits(sw))
 
 
+@pytest.mark.parametrize("N,M", [(6, 8), (2, 4), (3, 8), (1, 4)])
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+def test_quant_mask_weight_batch_parity(S, N, M, dt):
+    """Several tensors of different shapes (and scales, so every gamma
+    differs) in one batched preparation: each equals the oracle and the
+    single-tensor call bit for bit."""
+    shapes = [(128, 256), (37, 264), (300, 1032), (5, 8), (64, 4096)]
+    shapes = [(O, K) for O, K in shapes if K % M == 0]
+    log_case("quant_mask_weight batch", N, M, dt, shapes)
+    Ws, items = [], []
+    for i, (O, K) in enumerate(shapes):
+        W, _ = make_linear_inputs(1, O, K, seed=1000 + 17 * i + N, w_scale=0.01 * (i + 1))
+        if dt == "bf16":
+            W = bf16_round(W)
+        Ws.append(W)
+        items.append({"w": bf16_tensor(W) if dt == "bf16" else to_dev(W),
+                      "w_eff": torch.empty((O, K), dtype=torch.int8, device="cuda:0"),
+                      "mask": torch.empty((O, K), dtype=torch.uint8, device="cuda:0"),
+                      "sw_rows": torch.empty(O, dtype=torch.float32, device="cuda:0")})
+    outs = S.sbl_quant_mask_weight_batch(items, N, M)
+    for W, it, r in zip(Ws, items, outs):
+        O, K = W.shape
+        w_eff, mask, gamma, sw = o.quant_mask_weight(W, N, M)
+        gs = host(r["gamma_sw"])
+        assert f32_bits(gs[0]) == f32_bits(gamma) and f32_bits(gs[1]) == f32_bits(sw)
+        assert np.array_equal(host(r["mask"]), mask)
+        assert np.array_equal(host(r["w_eff"]), w_eff)
+        assert np.array_equal(host(r["packed"]).reshape(O, -1), o.pack(w_eff, mask, N, M))
+        assert np.all(f32_bits(host(r["sw_rows"])) == f32_bits(sw))
+        one = S.sbl_quant_mask_weight(it["w"], N, M)
+        assert np.array_equal(host(one["packed"]), host(r["packed"]))
+        assert np.array_equal(host(one["gamma_sw"]), gs)
+
+
+def test_quant_mask_weight_batch_full_size(S):
+    """The three projections of the Qwen2.5-0.5B FFN prepared in one batch
+    (K differs between them), as the benchmark step does."""
+    from sparse_linear_layers_bitlinear_amd.workloads import WORKLOADS, make_workload
+    log_case("quant_mask_weight batch full", "qwen05b_ffn")
+    wl = WORKLOADS["qwen05b_ffn"]
+    W, _ = make_workload("qwen05b_ffn")
+    items = [{"w": to_dev(W[l.name])} for l in wl.linears]
+    outs = S.sbl_quant_mask_weight_batch(items, wl.N, wl.M)
+    for l, r in zip(wl.linears, outs):
+        w_eff, mask, gamma, sw = o.quant_mask_weight(W[l.name], wl.N, wl.M)
+        gs = host(r["gamma_sw"])
+        assert f32_bits(gs[0]) == f32_bits(gamma) and f32_bits(gs[1]) == f32_bits(sw)
+        assert np.array_equal(host(r["packed"]).reshape(l.O, -1), o.pack(w_eff, mask, wl.N, wl.M))
+
+
 def test_roundclip_boundary(S):
     """Weights within a few ulps of the zero/one rounding boundary sw/2 (and
     exact ties, which round to even = 0)."""
