@@ -405,6 +405,42 @@ __device__ __forceinline__ uint32_t topn_keep_bits(const uint32_t* a, int N) {
   return keep;
 }
 
+// Keep bits of a group of 8 when only D = 8 - N in {1, 2} slots are dropped:
+// the D lowest in keep priority, where slot j ranks below an earlier slot i
+// iff |w_j| <= |w_i| (equal magnitudes keep the lower index) -- the same set
+// the rank rule above drops. One scan in index order tracks the lowest (and
+// second lowest) slot as a one-hot mask: 3 (D = 1) or 6 (D = 2) operations
+// per slot instead of 3 per pair.
+template <int D>
+__device__ __forceinline__ uint32_t drop_low_keep_bits8(const uint32_t* a) {
+  uint32_t v1, b1, v2 = 0, b2 = 0;
+  int j0;
+  if constexpr (D == 1) {
+    v1 = a[0];
+    b1 = 1u;
+    j0 = 1;
+  } else {
+    const bool c = a[1] <= a[0];            // slot 1 below slot 0
+    v1 = c ? a[1] : a[0];
+    b1 = c ? 2u : 1u;
+    v2 = c ? a[0] : a[1];
+    b2 = c ? 1u : 2u;
+    j0 = 2;
+  }
+#pragma unroll
+  for (int j = j0; j < 8; ++j) {
+    const bool c1 = a[j] <= v1;
+    if constexpr (D == 2) {
+      const bool c2 = a[j] <= v2;
+      v2 = c1 ? v1 : (c2 ? a[j] : v2);
+      b2 = c1 ? b1 : (c2 ? (1u << j) : b2);
+    }
+    v1 = c1 ? a[j] : v1;
+    b1 = c1 ? (1u << j) : b1;
+  }
+  return 0xFFu & ~(b1 | b2);
+}
+
 // Byte-slice 16 two-bit fields: bit u of lo (u = 4b + a) -> bit 8a + 2b, and
 // the same for hi one position up; i.e. a 4x4 transpose of 2-bit cells.
 __device__ __forceinline__ uint32_t byte_slice16(uint32_t lo, uint32_t hi) {
@@ -432,7 +468,10 @@ __device__ __forceinline__ uint32_t byte_slice16(uint32_t lo, uint32_t hi) {
 // the codes.
 constexpr int kQmpThreads = kChunksPerBlock + 64;
 
-template <bool BF16, int M, bool IDX>
+// SEL: how the mask is found -- 0: rank rule (any N); for M = 8 also
+// 1: drop the lowest slot (N = 7), 2: drop the two lowest (N = 6), 3: keep
+// all (N = 8).
+template <bool BF16, int M, bool IDX, int SEL>
 __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int N,
                                                      const unsigned long long* __restrict__ bins_all,
                                                      float eps) {
@@ -537,7 +576,14 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
       sgn |= (raw[e] >> 31) << e;
     }
 #pragma unroll
-    for (int g = 0; g < 32 / M; ++g) keep |= topn_keep_bits<M>(a + g * M, N) << (g * M);
+    for (int g = 0; g < 32 / M; ++g) {
+      uint32_t kb;
+      if constexpr (SEL == 1) kb = drop_low_keep_bits8<1>(a + g * M);
+      else if constexpr (SEL == 2) kb = drop_low_keep_bits8<2>(a + g * M);
+      else if constexpr (SEL == 3) kb = 0xFFu;
+      else kb = topn_keep_bits<M>(a + g * M, N);
+      keep |= kb << (g * M);
+    }
   }
   __syncthreads();                                    // (2) scalars from the fifth wave
   if (!active) return;
@@ -629,17 +675,23 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)blk3), block(kQmpThreads);
-#define SBL_QMP(BV, MV, IV) \
-  hipLaunchKernelGGL((k_qmp<BV, MV, IV>), grid, block, 0, s, b, N, bins, eps)
+#define SBL_QMP(BV, MV, IV, SV) \
+  hipLaunchKernelGGL((k_qmp<BV, MV, IV, SV>), grid, block, 0, s, b, N, bins, eps)
+#define SBL_QMP8(BV)                        \
+  if (N == 8) SBL_QMP(BV, 8, false, 3);     \
+  else if (N == 7) SBL_QMP(BV, 8, false, 1); \
+  else if (N == 6) SBL_QMP(BV, 8, false, 2); \
+  else SBL_QMP(BV, 8, false, 0)
   if (bf16) {
-    if (index_form(N, M)) SBL_QMP(true, 4, true);
-    else if (M == 4) SBL_QMP(true, 4, false);
-    else SBL_QMP(true, 8, false);
+    if (index_form(N, M)) SBL_QMP(true, 4, true, 0);
+    else if (M == 4) SBL_QMP(true, 4, false, 0);
+    else SBL_QMP8(true);
   } else {
-    if (index_form(N, M)) SBL_QMP(false, 4, true);
-    else if (M == 4) SBL_QMP(false, 4, false);
-    else SBL_QMP(false, 8, false);
+    if (index_form(N, M)) SBL_QMP(false, 4, true, 0);
+    else if (M == 4) SBL_QMP(false, 4, false, 0);
+    else SBL_QMP8(false);
   }
+#undef SBL_QMP8
 #undef SBL_QMP
   return hipGetLastError();
 }

@@ -219,6 +219,25 @@ def test_absmean_extreme_ranges(S):
             assert np.array_equal(host(r["w_eff"]), w_eff), name
 
 
+@pytest.mark.parametrize("M", [8, 4])
+def test_mask_every_tie_pattern(S, M):
+    """Every group of M magnitudes drawn from {0, 1, 2} (M = 8: 6561 groups)
+    or {0, 1, 2, 3} (M = 4: 256 groups), with random signs and signed zeros,
+    for every N: the GPU mask (and codes) equal the oracle's rank rule."""
+    log_case("mask tie patterns", M)
+    levels = 3 if M == 8 else 4
+    pats = np.array(np.meshgrid(*[np.arange(levels)] * M, indexing="ij")).reshape(M, -1).T
+    rng = np.random.default_rng(11)
+    sign = np.where(rng.random(pats.shape) < 0.5, -1.0, 1.0)
+    W = (pats * sign).astype(F32) * F32(0.01)
+    W = W.reshape(-1, (81 if M == 8 else 16) * M)   # 81 (16) groups per row
+    for N in range(1, M + 1):
+        r = S.sbl_quant_mask_weight(to_dev(W), N, M, want_w_eff=True, want_mask=True)
+        w_eff, mask, gamma, sw = o.quant_mask_weight(W, N, M)
+        assert np.array_equal(host(r["mask"]), mask), N
+        assert np.array_equal(host(r["w_eff"]), w_eff), N
+
+
 def test_weight_prep_errors(S):
     log_case("quant_mask_weight errors")
     w = torch.zeros((4, 12), dtype=torch.float32, device="cuda:0")
