@@ -144,6 +144,29 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nb, int64_t ntm, in
   tn = in / rows;
 }
 
+// 32-bit form of tile_of (tile counts below 2^31).
+__device__ __forceinline__ void tile_of32(uint32_t bid, uint32_t nb, uint32_t ntm, uint32_t ntn,
+                                          int& tm, int& tn) {
+  const uint32_t xcd = bid % kXcds, local = bid / kXcds;
+  const uint32_t per = nb / kXcds, rem = nb % kXcds;
+  const uint32_t pid = xcd < rem ? xcd * (per + 1) + local
+                                 : rem * (per + 1) + (xcd - rem) * per + local;
+  const uint32_t gsz = (uint32_t)kGroupM * ntn;
+  const uint32_t g = pid / gsz, first = g * kGroupM;
+  const uint32_t rows = (ntm - first) < (uint32_t)kGroupM ? (ntm - first) : (uint32_t)kGroupM;
+  const uint32_t in = pid - g * gsz;
+  tn = (int)(in / rows);
+  tm = (int)(first + (in - (uint32_t)tn * rows));
+}
+
+// Two fp32 values -> packed bf16 pair, round to nearest even (one
+// v_cvt_pk_bf16_f32; finite inputs).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 // ---------------------------------------------------------------------------
 // One kernel for both forms. SP = false: dense form, BK = 64,
 // v_mfma_i32_16x16x64_i8. SP = true: 2:4 index form, BK = 128,
@@ -621,7 +644,7 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wo = wave % WO, q = wave / WO, tq = tid - q * NTQ;
   const int g = lane >> 4, r16 = lane & 15;
-  const int64_t ntm = cdiv(O, BM), ntn = cdiv(T, BN), ntiles = ntm * ntn;
+  const uint32_t ntm = (uint32_t)cdiv(O, BM), ntn = (uint32_t)cdiv(T, BN), ntiles = ntm * ntn;
   const int Oi = (int)O, Ti = (int)T, Ki = (int)K, pitchi = (int)pitch;
   const int ns = (Ki + 127) >> 7;                    // K-steps of 128 (ns >= 1)
   const int nsq = (ns + KS - 1) / KS;
@@ -639,11 +662,11 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
   // only feed accumulators that are never stored. For s < ns the 8 bytes at
   // 32s + 8g lie inside the row record; in the dense form units past the code
   // words hold mask bits, which meet xq columns k >= K (zero in LDS).
-  auto setup = [&](int64_t tile) {
-    int64_t tm, tn;
-    tile_of(tile, ntiles, ntm, ntn, tm, tn);
-    o0 = (int)(tm * BM);
-    t0 = (int)(tn * BN);
+  auto setup = [&](uint32_t tile) {
+    int tm, tn;
+    tile_of32(tile, ntiles, ntm, ntn, tm, tn);
+    o0 = tm * BM;
+    t0 = tn * BN;
 #pragma unroll
     for (int i = 0; i < FI; ++i)
       avo[i] = (uint32_t)min(o0 + wo * 16 * FI + 16 * i + r16, Oi - 1) * (uint32_t)pitchi + 8 * g;
@@ -756,7 +779,10 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
           exc = exn;
         }
         if (h == 0) {
-          // xq fragments of sub-step 1 (the registers free up as the MFMAs issue)
+          // xq fragments of sub-step 1 (the registers free up as the MFMAs
+          // issue; wide wave tiles keep the loads behind this point so that
+          // the two sub-steps' fragments never hold registers at once)
+          if constexpr (FJ >= 8) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int j = 0; j < FJ; ++j) bf[j] = *(const v4i*)(b + 16 * j * kPitchR + 32 * g + 16);
         }
@@ -782,7 +808,7 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
     if constexpr (NBS == 2) bload(sb + 1, rb[1]);
   };
 
-  int64_t tile = blockIdx.x;
+  uint32_t tile = blockIdx.x;
   setup(tile);
   prologue();
   for (;;) {
@@ -794,6 +820,13 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
 #pragma unroll
       for (int j = 0; j < FJ; ++j) acc[i][j] = v4i{0, 0, 0, 0};
     __syncthreads();
+    // this tile's scales to LDS (loaded with the tile's first operands, so
+    // waiting for them here costs nothing; read after the loop's barriers)
+#pragma unroll
+    for (int c = 0; c < C::NSC; ++c) {
+      const int e = tid + NT * c;
+      if (e < BM + BN) sxs[e] = scr[c];              // sws follows sxs
+    }
 
     for (int it = 0; it < nsq; it += U) {
 #pragma unroll
@@ -813,14 +846,9 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
       }
     }
 
-    // this tile's scales to LDS; then the next tile's first loads go out
+    // the next tile's first loads go out before this tile's epilogue
     const int eo0 = o0, et0 = t0;
-#pragma unroll
-    for (int c = 0; c < C::NSC; ++c) {
-      const int e = tid + NT * c;
-      if (e < BM + BN) sxs[e] = scr[c];              // sws follows sxs
-    }
-    const int64_t next = tile + gridDim.x;
+    const uint32_t next = tile + gridDim.x;
     const bool more = next < ntiles;
     if (more) {
       setup(next);
@@ -847,8 +875,6 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
         }
         __syncthreads();
       }
-    } else {
-      __syncthreads();                                // scales visible
     }
 
     if (YBF16 && acc_out == nullptr) {
@@ -871,9 +897,8 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
             const float v1 = ((float)acc[i][j][1] * st[j]) * w4[i].y;
             const float v2 = ((float)acc[i][j][2] * st[j]) * w4[i].z;
             const float v3 = ((float)acc[i][j][3] * st[j]) * w4[i].w;
-            *(uint2*)(ot + tl * C::PO + 2 * ol) =
-                make_uint2(f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16),
-                           f32_to_bf16_bits(v2) | (f32_to_bf16_bits(v3) << 16));
+            *(uint2*)(ot + tl * C::PO + 2 * ol) = make_uint2(pack_bf16x2(v0, v1),
+                                                             pack_bf16x2(v2, v3));
           }
         }
       }
@@ -882,34 +907,62 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
       constexpr int RC = RW < 8 ? RW : 8;             // rows in flight per wave
       constexpr int CPR = BM / 4;                     // 8-byte chunks per row
       constexpr int CL = (CPR + 63) / 64;             // chunks per lane and row
-      const bool fast = (Oi & 3) == 0 && eo0 + BM <= Oi;
-#pragma unroll 1
-      for (int m0 = 0; m0 < RW; m0 += RC) {
-        uint2 v[RC][CL];
+      constexpr int LPR = CPR < 64 ? CPR : 64;        // lanes per row (full-tile path)
+      constexpr int RPI = 64 / LPR;                   // rows per wave instruction
+      constexpr int RWF = BN / (NW * RPI);            // row groups per wave
+      constexpr int RF = RWF < 8 ? (RWF > 0 ? RWF : 1) : 8;   // row groups in flight
+      constexpr bool FULL_OK = CPR % LPR == 0 && BN % (NW * RPI) == 0 && RWF % RF == 0 && RWF > 0;
+      if (FULL_OK && (Oi & 3) == 0 && eo0 + BM <= Oi && et0 + BN <= Ti) {
+        // whole tile inside y: straight-line reads and 8-byte stores
+        constexpr int CF = CPR / LPR;
+        const int lr = lane / LPR, lc = lane % LPR;
 #pragma unroll
-        for (int m = 0; m < RC; ++m)
+        for (int m0 = 0; m0 < RWF; m0 += RF) {
+          uint2 v[RF][CF];
 #pragma unroll
-          for (int c = 0; c < CL; ++c) {
-            const int tl = min(wave + NW * (m0 + m), BN - 1), ch = min(lane + 64 * c, CPR - 1);
-            v[m][c] = *(const uint2*)(ot + tl * C::PO + 8 * ch);
+          for (int m = 0; m < RF; ++m)
+#pragma unroll
+            for (int c = 0; c < CF; ++c)
+              v[m][c] = *(const uint2*)(ot + ((wave + NW * (m0 + m)) * RPI + lr) * C::PO +
+                                        8 * (lc + LPR * c));
+#pragma unroll
+          for (int m = 0; m < RF; ++m) {
+            uint16_t* yr = (uint16_t*)y +
+                           (int64_t)(et0 + (wave + NW * (m0 + m)) * RPI + lr) * Oi + eo0;
+#pragma unroll
+            for (int c = 0; c < CF; ++c) *(uint2*)(yr + 4 * (lc + LPR * c)) = v[m][c];
           }
+        }
+      } else {
+        const bool fast = (Oi & 3) == 0 && eo0 + BM <= Oi;
+#pragma unroll 1
+        for (int m0 = 0; m0 < RW; m0 += RC) {
+          uint2 v[RC][CL];
 #pragma unroll
-        for (int m = 0; m < RC; ++m) {
-          const int tl = wave + NW * (m0 + m), t = et0 + tl;
-          if (m0 + m >= RW || tl >= BN || t >= Ti) continue;
-          uint16_t* yr = (uint16_t*)y + (int64_t)t * Oi + eo0;
+          for (int m = 0; m < RC; ++m)
 #pragma unroll
-          for (int c = 0; c < CL; ++c) {
-            const int ch = lane + 64 * c;
-            if (ch >= CPR) continue;
-            if (fast) {
-              *(uint2*)(yr + 4 * ch) = v[m][c];
-            } else {
-              const uint16_t h[4] = {(uint16_t)(v[m][c].x & 0xFFFF), (uint16_t)(v[m][c].x >> 16),
-                                     (uint16_t)(v[m][c].y & 0xFFFF), (uint16_t)(v[m][c].y >> 16)};
+            for (int c = 0; c < CL; ++c) {
+              const int tl = min(wave + NW * (m0 + m), BN - 1), ch = min(lane + 64 * c, CPR - 1);
+              v[m][c] = *(const uint2*)(ot + tl * C::PO + 8 * ch);
+            }
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                if (eo0 + 4 * ch + r < Oi) yr[4 * ch + r] = h[r];
+          for (int m = 0; m < RC; ++m) {
+            const int tl = wave + NW * (m0 + m), t = et0 + tl;
+            if (m0 + m >= RW || tl >= BN || t >= Ti) continue;
+            uint16_t* yr = (uint16_t*)y + (int64_t)t * Oi + eo0;
+#pragma unroll
+            for (int c = 0; c < CL; ++c) {
+              const int ch = lane + 64 * c;
+              if (ch >= CPR) continue;
+              if (fast) {
+                *(uint2*)(yr + 4 * ch) = v[m][c];
+              } else {
+                const uint16_t h[4] = {(uint16_t)(v[m][c].x & 0xFFFF), (uint16_t)(v[m][c].x >> 16),
+                                       (uint16_t)(v[m][c].y & 0xFFFF), (uint16_t)(v[m][c].y >> 16)};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (eo0 + 4 * ch + r < Oi) yr[4 * ch + r] = h[r];
+              }
             }
           }
         }
