@@ -10,8 +10,9 @@ A step is one pass of the whole forward hot path over one batch:
     dequant epilogue (gate and up fused into one GEMM over concatenated rows);
     all projections' weights are prepared by one batched call;
   decode workload (BitNet-2B4T-shaped layer, prepacked 2:4 weights): for each
-    of L distinct layer copies, int8 quantization of the layer inputs and the
-    q|k|v, o, gate|up and down GEMMs.
+    of L distinct layer copies, the q|k|v, o, gate|up and down projections of
+    T bf16 tokens, each one sbl_linear_fwd call (per-token int8 quantization
+    inside the GEMV).
 The step is captured once into a HIP graph and replayed (the library launches
 stay the same kernels; the graph only removes Python/ctypes launch cost).
 Prints ONE JSON line.
@@ -190,34 +191,34 @@ class DecodeStep:
             self.packed.append(pk)
             self.swr.append(sr)
         torch.cuda.synchronize()
-        self.xq = {k: torch.empty((T, K), dtype=torch.int8, device=dev)
-                   for k, K in self.K_of.items()}
-        self.sx = {k: torch.empty(T, dtype=torch.float32, device=dev) for k in self.K_of}
         self.y = {xn: torch.empty((T, sum(l.O for l in ls)), dtype=torch.bfloat16, device=dev)
                   for xn, ls in self.groups.items()}
+        self.ws = {xn: torch.empty(max(1, sbl.sbl_linear_fwd_workspace(
+            T, sum(l.O for l in ls), self.K_of[xn], 2, 4, True)), dtype=torch.uint8, device=dev)
+            for xn, ls in self.groups.items()}
         self.weights = sum(l.O * l.K for l in wl.linears)
-        self.bytes_layer = sum(self.call_bytes(xn) for xn in self.groups) + \
-            sum(3.0 * T * K + 4 * T for K in self.K_of.values())
+        self.bytes_layer = sum(self.call_bytes(xn) for xn in self.groups)
         self.ops = 2.0 * T * self.weights * L
 
     def call_bytes(self, xn):
+        """Algorithmic HBM bytes of one projection group: packed W, bf16 x,
+        per-row weight scales and the bf16 output."""
         T = self.T
         K = self.K_of[xn]
         O = sum(l.O for l in self.groups[xn])
-        return sbl.sbl_packed_bytes(O, K, 2, 4) + T * K + 4 * T + 4 * O + 2 * T * O
+        return sbl.sbl_packed_bytes(O, K, 2, 4) + 2 * T * K + 4 * O + 2 * T * O
 
     def calls(self):
+        """Per layer and projection group one sbl_linear_fwd on the prepacked
+        weights (the activation quantization runs inside the GEMV)."""
         out = []
         for li in range(self.L):
             for xn in self.groups:
                 O = sum(l.O for l in self.groups[xn])
-                out.append((f"quant_act[{xn}]",
-                            lambda xn=xn: sbl.sbl_quant_act(self.x[xn], xq=self.xq[xn],
-                                                            sx=self.sx[xn])))
-                out.append((f"gemm[{'+'.join(l.name for l in self.groups[xn])}]",
-                            lambda xn=xn, O=O, li=li: sbl.sbl_gemm(
-                                self.xq[xn], self.sx[xn], self.packed[li][xn], self.swr[li][xn],
-                                O, 2, 4, y=self.y[xn])))
+                out.append((f"linear[{'+'.join(l.name for l in self.groups[xn])}]",
+                            lambda xn=xn, O=O, li=li: sbl.sbl_linear_fwd(
+                                self.x[xn], 2, 4, prepacked=self.packed[li][xn],
+                                sw=self.swr[li][xn], O=O, y=self.y[xn], ws=self.ws[xn])))
         return out
 
     cold_weights = True    # 30 layers of packed weights exceed the last-level cache
@@ -228,12 +229,9 @@ class DecodeStep:
         run_all(self.calls())
 
     def call_info(self, name):
-        if name.startswith("gemm["):
-            xn = [k for k, ls in self.groups.items()
-                  if name == f"gemm[{'+'.join(l.name for l in ls)}]"][0]
-            return "hbm", float(self.call_bytes(xn)), "bytes"
-        K = self.K_of[name[10:-1]]
-        return "hbm", 3.0 * self.T * K + 4.0 * self.T, "bytes"
+        xn = [k for k, ls in self.groups.items()
+              if name == f"linear[{'+'.join(l.name for l in ls)}]"][0]
+        return "hbm", float(self.call_bytes(xn)), "bytes"
 
 
 # ------------------------------------------------------------------ timing --
@@ -389,6 +387,22 @@ def calibrate_copy():
                       "bytes_written_per_copy": n, "copies": 3}))
 
 
+def per_call_rates(step, per_call):
+    """Device time of one launch of each call and its rate against the call's
+    own roofline (HBM GB/s or effective TOPS)."""
+    out = {}
+    for k, ms in per_call.items():
+        bound, units, _ = step.call_info(k)
+        rate = units / (ms * 1e-3)
+        if bound == "hbm":
+            out[k] = {"us": round(ms * 1e3, 2), "GB/s": round(rate / 1e9, 1),
+                      "frac": round(rate / 1e9 / PEAK_HBM_GBS, 4)}
+        else:
+            out[k] = {"us": round(ms * 1e3, 2), "TOPS": round(rate / 1e12, 1),
+                      "frac": round(rate / 1e12 / PEAK_INT8_DENSE_TOPS, 4)}
+    return out
+
+
 def main():
     a = parse()
     if a.calibrate_copy:
@@ -445,6 +459,7 @@ def main():
         "dtype": "int8xternary->int32 (bf16 in/out)", "data": "synthetic",
         "config": config, "roofline": roof,
         "breakdown_ms": {k: round(share[k], 5) for k in share},
+        "per_call": per_call_rates(step, per_call),
         "breakdown_note": "per-step device ms of each call, from graph replays of that call alone",
         "timing": "eager launches" if a.eager else "HIP graph replay",
     }

@@ -88,39 +88,6 @@ __device__ __forceinline__ void store_out(void* __restrict__ y, int32_t* __restr
   }
 }
 
-// Epilogue of one 16x16 tile slice held by a lane: outputs o..o+3 of token t.
-// y = fp32(fp32(acc * sx[t]) * sw[o]), rounded to bf16 (RNE) or kept fp32.
-template <bool YBF16>
-__device__ __forceinline__ void store_tile(void* __restrict__ y, int32_t* __restrict__ acc_out,
-                                           const v4i& c, int t, int o, int O, float s_t,
-                                           const float* __restrict__ sw, int sw_inc) {
-  float v[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float a = (float)c[r] * s_t;
-    v[r] = a * sw[min(o + r, O - 1) * sw_inc];
-  }
-  const int64_t base = (int64_t)t * O + o;
-  if (o + 3 < O && (O & 3) == 0) {
-    if constexpr (YBF16) {
-      const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-      const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-      *(uint2*)((uint16_t*)y + base) = make_uint2(lo, hi);
-    } else {
-      *(float4*)((float*)y + base) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-    if (acc_out) *(int4*)(acc_out + base) = make_int4(c[0], c[1], c[2], c[3]);
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (o + r >= O) break;
-      if constexpr (YBF16) ((uint16_t*)y)[base + r] = (uint16_t)f32_to_bf16_bits(v[r]);
-      else ((float*)y)[base + r] = v[r];
-      if (acc_out) acc_out[base + r] = c[r];
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Tile order: workgroups are dispatched round-robin over the 8 XCDs, each with
 // its own L2. Block b runs on XCD b % 8; renumber so every XCD owns one
@@ -608,18 +575,6 @@ struct RaCfg {
   static constexpr size_t LDS = SCALES + (size_t)(BM + BN) * 4;
 };
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource over [base, base + 4 GiB): loads take a per-lane 32-bit
-// offset plus a wave-uniform scalar offset, so address arithmetic costs no
-// VALU. Offsets are always in bounds by construction (no reliance on the
-// hardware range check).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF,
-                                           0x00020000);
-}
-
 template <int WO, int KS, int FI, int FJ, int NA, bool SP, bool YBF16>
 __global__ __launch_bounds__(64 * WO * KS) __attribute__((amdgpu_waves_per_eu(2)))
 void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
@@ -992,92 +947,6 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
 }
 
 // ---------------------------------------------------------------------------
-// Decode (T <= 16): bandwidth-oriented variant. One workgroup per 16-row tile
-// of W; its 4 wavefronts split the K-steps into contiguous ranges and each
-// issues the loads of kGemvUnroll steps before consuming them, so a wave keeps
-// several KB of packed weights in flight. Tokens occupy the 16 columns of the
-// MFMA (columns >= T read zeros). The 4 partial accumulators are summed in LDS.
-// ---------------------------------------------------------------------------
-constexpr int kGemvUnroll = 8;
-
-template <bool SP, bool KA16, bool YBF16>
-__global__ __launch_bounds__(256) void k_gemv(const int8_t* __restrict__ xq,
-                                              const float* __restrict__ sx,
-                                              const uint8_t* __restrict__ packed, int64_t pitch,
-                                              const float* __restrict__ sw, int64_t sw_inc,
-                                              int64_t T, int64_t O, int64_t K,
-                                              void* __restrict__ y, int32_t* __restrict__ acc_out) {
-  constexpr int BK = SP ? 128 : 64;
-  constexpr int U = kGemvUnroll;
-  __shared__ v4i red[4][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int64_t o0 = (int64_t)blockIdx.x * 16;
-  const int64_t nk = cdiv(K, BK);
-  const int64_t per = cdiv(nk, 4);
-  const int64_t ks0 = wave * per, ks1 = (ks0 + per < nk) ? ks0 + per : nk;
-  const bool rowv = o0 + r16 < O;
-  const uint8_t* arow = packed + (o0 + r16) * pitch + (SP ? 8 * g : 4 * g);
-  const bool tv = r16 < T;
-  const int8_t* xrow = xq + r16 * K;
-
-  v4i acc = {0, 0, 0, 0};
-  for (int64_t ks = ks0; ks < ks1; ks += U) {
-    uint2 a[U];
-    uint4 b0[U], b1[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = ks + u;
-      a[u] = make_uint2(0, SP ? 0x44444444u : 0u);
-      b0[u] = b1[u] = make_uint4(0, 0, 0, 0);
-      if (k < ks1) {
-        if (rowv) {
-          if constexpr (SP) a[u] = *(const uint2*)(arow + k * 32);
-          else a[u].x = *(const uint32_t*)(arow + k * 16);
-        }
-        if (tv) {
-          if constexpr (SP) {
-            b0[u] = load_x16<KA16>(xrow, k * BK + 16 * g, K);
-            b1[u] = load_x16<KA16>(xrow, k * BK + 64 + 16 * g, K);
-          } else {
-            b0[u] = load_x16<KA16>(xrow, k * BK + 16 * g, K);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (ks + u < ks1) {
-        const v4i af = {(int)expand_codes(a[u].x, 0), (int)expand_codes(a[u].x, 1),
-                        (int)expand_codes(a[u].x, 2), (int)expand_codes(a[u].x, 3)};
-        const v4i lo = {(int)b0[u].x, (int)b0[u].y, (int)b0[u].z, (int)b0[u].w};
-        if constexpr (SP) {
-          const v8i bf = {lo[0], lo[1], lo[2], lo[3], (int)b1[u].x, (int)b1[u].y, (int)b1[u].z,
-                          (int)b1[u].w};
-          acc = __builtin_amdgcn_smfmac_i32_16x16x128_i8(af, bf, acc, (int)a[u].y, 0, 0);
-        } else {
-          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(af, lo, acc, 0, 0, 0);
-        }
-      }
-    }
-  }
-  red[wave][lane] = acc;
-  __syncthreads();
-  if (wave != 0) return;
-  const v4i c = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
-  store_out<YBF16>(y, acc_out, c, (int64_t)r16, o0 + 4 * g, T, O, sx, sw, sw_inc);
-}
-
-template <bool SP, bool KA16, bool YBF16>
-static hipError_t launch_gemv(const int8_t* xq, const float* sx, const uint8_t* packed,
-                              int64_t pitch, const float* sw, int64_t sw_inc, int64_t T,
-                              int64_t O, int64_t K, void* y, int32_t* acc, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemv<SP, KA16, YBF16>), dim3((unsigned)cdiv(O, 16)), dim3(256), 0, s, xq,
-                     sx, packed, pitch, sw, sw_inc, T, O, K, y, acc);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // Tile configurations and the per-shape choice.
 // ---------------------------------------------------------------------------
 enum TileCfg { kT256x256 = 0, kT256x128 = 1, kT128x256 = 2, kT128x128 = 3, kT256x32 = 4,
@@ -1230,18 +1099,8 @@ hipError_t launch_gemm(const int8_t* xq, const float* sx, const void* packed, co
   const Args a{xq, sx, (const uint8_t*)packed, row_pitch(K, N, M), sw, sw_inc, T, O, K, y, acc};
   const bool ka16 = (K % 16) == 0;
   const char* ev = std::getenv("SBL_GEMM_TILE");
-  if (T <= 16 && !(ev && std::atoi(ev) >= 0)) {
-#define SBL_GEMV(SPV, KAV, YV) \
-    return launch_gemv<SPV, KAV, YV>(xq, sx, a.packed, a.pitch, sw, sw_inc, T, O, K, y, acc, s)
-    if (sp) {
-      if (ka16) { if (y_bf16) SBL_GEMV(true, true, true); else SBL_GEMV(true, true, false); }
-      else { if (y_bf16) SBL_GEMV(true, false, true); else SBL_GEMV(true, false, false); }
-    } else {
-      if (ka16) { if (y_bf16) SBL_GEMV(false, true, true); else SBL_GEMV(false, true, false); }
-      else { if (y_bf16) SBL_GEMV(false, false, true); else SBL_GEMV(false, false, false); }
-    }
-#undef SBL_GEMV
-  }
+  if (T <= 16 && !(ev && std::atoi(ev) >= 0) && decode_fits(T, O, K, N, M, 0))
+    return launch_decode(xq, 0, sx, 0.0f, packed, sw, sw_inc, T, O, K, N, M, y, y_bf16, acc, s);
   int cfg = choose_cfg(T, O, K, sp);
   if (cfg >= kDma128x256 && K % (sp ? 128 : 64) != 0) cfg = kT128x128;  // DMA path needs whole K-steps
 #define SBL_DISPATCH(SPV, KAV, YV) return launch_sel<SPV, KAV, YV>(cfg, a, s)

@@ -1,0 +1,305 @@
+// a5 + a6 (and a1, fused) for decode-sized batches of at most 16 tokens: a
+// streaming GEMV on the matrix cores.
+//
+// Sparse-BitNet summary, section 3.4 "Activation quantization" and "The Full
+// Sparse-BitLinear Layer" (Eq. 4): per token x~ = Clip(x * 127 / (max|x| +
+// eps), -128, 127), and y = (W_eff x~) scaled by the token's and the weight's
+// scale. BitNet b1.58 2B4T summary, section 3.4 (per-token absmax, nearest
+// rounding).
+//
+// With T <= 16 each packed weight byte meets at most 16 tokens: the work is
+// bound by the HBM reads of the packed W, and with so little arithmetic per
+// workgroup the instructions a wavefront executes once (not in a loop) are
+// what the latency is made of. So every phase is either a handful of
+// instructions or a short loop:
+//  - the 16-row tiles of W are split evenly over at most one workgroup of 8
+//    wavefronts per compute unit; a workgroup copies all of its packed W
+//    straight into LDS with 16-byte LDS-DMA loads (one instruction moves 1 KB:
+//    16 rows x two K-steps), issued at the start so the whole weight stream is
+//    in flight at once;
+//  - the T activation rows are quantized by all 512 threads together (a token
+//    is shared by 512 / T' threads, T' = T rounded up to a power of two), into
+//    int8 rows in LDS -- the same arithmetic as the stand-alone quantizer, so
+//    the codes are identical -- or, when xq is given, copied by LDS-DMA;
+//  - the waves then split the K-steps of each tile (MFMA A operand = 8 bytes of
+//    packed W per lane and K-step, the operand layout of the prefill kernel;
+//    B = the int8 rows, columns t >= T read row T-1 and are never stored),
+//    add their int32 partial sums into LDS (ds_add, exact), and the
+//    workgroup dequantizes y = fp32(fp32(acc * s_x) * s_w).
+#include "sbl_internal.h"
+#include "device_util.cuh"
+
+#include <cstdlib>
+
+namespace sbl {
+namespace {
+
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kDecMaxVec = 16;               // 16-byte activation vectors per thread
+constexpr int kDecMaxLds = 150 * 1024;       // dynamic LDS limit of the decode kernel
+
+struct DecodeArgs {
+  const void* x;          // XM 0: xq int8 [T, K]; XM 1 / 2: x bf16 / fp32 [T, K]
+  const float* sx;        // XM 0: per-token scales
+  float eps;              // XM 1 / 2: activation epsilon
+  const uint8_t* packed;  // packed rows, pitch bytes each
+  int pitch;
+  const float* sw;        // weight scale(s), element o at o * sw_inc
+  int sw_inc;
+  int T, O, K, R;         // R: most tiles of one workgroup
+  void* y;                // [T, O] bf16 or fp32
+  int32_t* acc;           // optional [T, O] int32
+};
+
+// LDS: W [R][np][1 KB] | xs [T][xpitch] int8 | sxs [16] f32 | pmax [16] u32 (per half-wave) |
+//      red [R][64][4] i32     (np = pairs of K-steps)
+__host__ __device__ inline int dec_np(int K) { return ((K + 127) / 128 + 1) / 2; }
+__host__ __device__ inline int dec_xpitch(int K) { return 128 * ((K + 127) / 128) + 16; }
+__host__ __device__ inline int dec_off_x(int K, int R) { return R * dec_np(K) * 1024; }
+__host__ __device__ inline int dec_off_sx(int T, int K, int R) {
+  return dec_off_x(K, R) + ((T * dec_xpitch(K) + 15) & ~15);
+}
+__host__ __device__ inline int dec_lds(int T, int K, int R) {
+  return dec_off_sx(T, K, R) + 64 + 64 + R * 1024;
+}
+// threads per token: 512 / (T rounded up to a power of two)
+__host__ __device__ inline int dec_group(int T) {
+  int tp = 1;
+  while (tp < T) tp <<= 1;
+  return kDecThreads / tp;
+}
+
+// max over each row of 16 lanes, left in the row's lane 15 (row_shr 1, 2, 4, 8;
+// lanes without a source keep 0, the identity of an unsigned max)
+__device__ __forceinline__ uint32_t row_max_dpp(uint32_t m) {
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x111, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x112, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x114, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x118, 0xF, 0xF, false));
+  return m;
+}
+
+__device__ __forceinline__ v4i expand4(uint32_t w) {
+  return v4i{(int)expand_codes(w, 0), (int)expand_codes(w, 1), (int)expand_codes(w, 2),
+             (int)expand_codes(w, 3)};
+}
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// XM: 0 = xq given, 1 = bf16 x, 2 = fp32 x.
+template <bool SP, int XM, bool YBF16>
+__global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int T = a.T, O = a.O, K = a.K;
+  const int ns = (K + 127) >> 7, np = (ns + 1) >> 1;   // K-steps, pairs of K-steps
+  const int XP = dec_xpitch(K);
+  uint8_t* const wsm = smem;
+  int8_t* const xs = (int8_t*)(smem + dec_off_x(K, a.R));
+  float* const sxs = (float*)(smem + dec_off_sx(T, K, a.R));
+  uint32_t* const pmax = (uint32_t*)(sxs + 16);
+  int* const red = (int*)(pmax + 16);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
+  // this workgroup's tiles [tb, tb + ntb) of the (O + 15) / 16 (even split)
+  const int ntiles = (O + 15) >> 4;
+  const int tb = (int)((int64_t)blockIdx.x * ntiles / gridDim.x);
+  const int ntb = (int)((int64_t)(blockIdx.x + 1) * ntiles / gridDim.x) - tb;
+
+  // activations of the thread's token (XM 1 / 2), loaded first: waiting for
+  // them then does not wait for the W copies issued after them
+  constexpr bool BF = XM == 1;
+  constexpr int EV = XM == 0 ? 16 : BF ? 8 : 4;         // elements per 16-byte vector
+  const int nvr = K / EV;                                // vectors per row
+  const int G = dec_group(T);                            // threads per token
+  const int tt = min(tid / G, T - 1), col = tid % G;     // token and first vector
+  const bool tok = tid / G < T;                          // thread has a token
+  const int nvt = (nvr + G - 1) / G;                     // vectors per thread (uniform)
+  uint4 v[kDecMaxVec];
+  if constexpr (XM != 0) {
+    const uint4* const row = (const uint4*)a.x + (int64_t)tt * nvr;
+#pragma unroll
+    for (int i = 0; i < kDecMaxVec; ++i)
+      if (i < nvt) v[i] = row[min(col + G * i, nvr - 1)];   // clamped duplicates are harmless
+  }
+
+  // packed W -> LDS: job j = (tile j / np, pair j % np), one DMA per wave and
+  // job. Lane l moves 16 bytes of row l % 16 at byte 64 p + 16 (l / 16); the
+  // second step of a last odd pair re-reads the first (it is never computed).
+  for (int j = wave; j < ntb * np; j += kDecWaves) {
+    const int r = j / np, p = j - r * np;
+    const int ch = lane >> 4;
+    const int chs = (2 * p + (ch >> 1) < ns) ? ch : ch - 2;
+    const int o = min((tb + r) * 16 + r16, O - 1);
+    dma16(a.packed + (int64_t)o * a.pitch + 64 * p + 16 * chs, wsm + j * 1024);
+  }
+  for (int i = tid; i < ntb * 256; i += kDecThreads) red[i] = 0;
+
+  if constexpr (XM == 0) {
+    // xq rows -> LDS by DMA (K % 16 == 0): job (token t, 1 KB piece q)
+    const int nq = (K + 1023) >> 10;
+    const int8_t* const xq = (const int8_t*)a.x;
+    for (int j = wave; j < T * nq; j += kDecWaves) {
+      const int t = j / nq, q = j - t * nq;
+      if (1024 * q + 16 * lane < K)
+        dma16(xq + (int64_t)t * K + 1024 * q + 16 * lane, (uint8_t*)xs + t * XP + 1024 * q);
+    }
+    if (tid < T) sxs[tid] = a.sx[tid];
+  } else {
+    // per-token max over the token's G threads: within each wave by DPP (lane
+    // 31 holds the max of lanes 0-31, lane 63 that of 32-63 or of the whole
+    // wave), then over the token's waves through LDS
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < kDecMaxVec; ++i)
+      if (i < nvt) m = max(m, absmax_vec<BF>(v[i]));
+    m = row_max_dpp(m);
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x142, 0xA, 0xF, false));
+    if (G >= 64) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x143, 0xC, 0xF, false));
+    const uint32_t m_lo = __builtin_amdgcn_readlane(m, 31), m_hi = __builtin_amdgcn_readlane(m, 63);
+    if (lane == 0) {
+      pmax[2 * wave] = G >= 64 ? m_hi : m_lo;
+      pmax[2 * wave + 1] = m_hi;
+    }
+    __syncthreads();
+    uint32_t mt = 0;
+    if (G >= 64) {
+      const int wpt = G >> 6;                            // waves per token
+      for (int k = 0; k < wpt; ++k) mt = max(mt, pmax[2 * (tt * wpt + k)]);
+    } else {
+      mt = pmax[tt];
+    }
+    const ActScale sc = act_scale(mt, a.eps);
+    if (col == 0 && tok) sxs[tt] = sc.s;
+    int8_t* const xrow = xs + tt * XP;
+#pragma unroll
+    for (int i = 0; i < kDecMaxVec; ++i) {
+      const int c = col + G * i;
+      if (i < nvt && c < nvr && tok) {
+        const uint2 q = act_codes_vec<BF>(v[i], sc.q);
+        if constexpr (BF) *(uint2*)(xrow + c * EV) = q;
+        else *(uint32_t*)(xrow + c * EV) = q.x;
+      }
+    }
+  }
+  // columns K .. 128 * ns of every row are zero (they meet the padding of the
+  // last K-step's codes)
+  const int tail = 128 * ns - K;
+  if (tail > 0)
+    for (int i = tid; i < T * tail; i += kDecThreads) xs[(i / tail) * XP + K + i % tail] = 0;
+  __builtin_amdgcn_s_waitcnt(0);    // this wave's LDS-DMA copies have landed ...
+  __syncthreads();                   // ... and every wave's
+
+  // K-steps s = wave, wave + 8, ... of every tile, two accumulators
+  const int8_t* const xr = xs + min(r16, T - 1) * XP;
+  const int aoff = 16 * r16 + 8 * (g & 1) + 256 * (g >> 1);
+  auto unit = [&](int r, int s, v4i& acc) {
+    const uint2 w = *(const uint2*)(wsm + (r * np + (s >> 1)) * 1024 + 512 * (s & 1) + aoff);
+    const int kb = 128 * s;
+    if constexpr (SP) {
+      const v4i lo = *(const v4i*)(xr + kb + 16 * g);
+      const v4i hi = *(const v4i*)(xr + kb + 64 + 16 * g);
+      acc = __builtin_amdgcn_smfmac_i32_16x16x128_i8(
+          expand4(w.x), v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, acc, (int)w.y,
+          0, 0);
+    } else {
+      const v4i b0 = *(const v4i*)(xr + kb + 32 * g);
+      const v4i b1 = *(const v4i*)(xr + kb + 32 * g + 16);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand4(w.x), b0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand4(w.y), b1, acc, 0, 0, 0);
+    }
+  };
+  for (int r = 0; r < ntb; ++r) {
+    v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    int s = wave;
+    for (; s + kDecWaves < ns; s += 2 * kDecWaves) {
+      unit(r, s, acc0);
+      unit(r, s + kDecWaves, acc1);
+    }
+    if (s < ns) unit(r, s, acc0);
+    acc0 += acc1;
+    if (wave < ns) {
+      int* const rp = red + r * 256 + lane * 4;
+      atomicAdd(rp + 0, acc0[0]);
+      atomicAdd(rp + 1, acc0[1]);
+      atomicAdd(rp + 2, acc0[2]);
+      atomicAdd(rp + 3, acc0[3]);
+    }
+  }
+  __syncthreads();
+
+  // lane l of tile r: outputs o = 16 (tb + r) + 4 (l / 16) + 0..3 of token l % 16
+  for (int i = tid; i < ntb * 64; i += kDecThreads) {
+    const int t = i & 15, o = (tb + (i >> 6)) * 16 + 4 * ((i >> 4) & 3);
+    if (t < T && o < O)
+      store_tile<YBF16>(a.y, a.acc, *(const v4i*)(red + 4 * i), t, o, O, sxs[t], a.sw, a.sw_inc);
+  }
+}
+
+// workgroups: at most one per compute unit and one per tile
+int dec_blocks(int64_t O) {
+  const char* ev = std::getenv("SBL_DECODE_BLOCKS");   // tuning override
+  const int64_t ntiles = cdiv(O, 16);
+  int64_t nb = ev ? std::atoi(ev) : 0;
+  if (nb < 1) nb = device_info().cus;
+  return (int)(nb < ntiles ? nb : ntiles);
+}
+
+template <bool SP, int XM, bool YBF16>
+hipError_t run_decode(const DecodeArgs& a, int blocks, hipStream_t s) {
+  auto kern = k_decode<SP, XM, YBF16>;
+  const int lds = dec_lds(a.T, a.K, a.R);
+  if (lds > 65536) {
+    static int set = 0;   // the attribute is per kernel; raised as needed
+    if (lds > set) {
+      const hipError_t e =
+          hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+      set = lds;
+    }
+  }
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kDecThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <bool SP, bool YBF16>
+hipError_t dispatch_x(int xmode, const DecodeArgs& a, int blocks, hipStream_t s) {
+  if (xmode == 0) return run_decode<SP, 0, YBF16>(a, blocks, s);
+  if (xmode == 1) return run_decode<SP, 1, YBF16>(a, blocks, s);
+  return run_decode<SP, 2, YBF16>(a, blocks, s);
+}
+
+}  // namespace
+
+bool decode_fits(int64_t T, int64_t O, int64_t K, int N, int M, int xmode) {
+  if (T < 1 || T > 16 || O < 1 || K < 1 || K % 16 != 0) return false;
+  if (O * row_pitch(K, N, M) >= (int64_t(1) << 31)) return false;
+  // activation vectors per thread
+  const int64_t nvr = K / (xmode == 0 ? 16 : xmode == 1 ? 8 : 4);
+  if (xmode != 0 && cdiv(nvr, dec_group((int)T)) > kDecMaxVec) return false;
+  const int64_t R = cdiv(cdiv(O, 16), dec_blocks(O));
+  return dec_lds((int)T, (int)K, (int)R) <= kDecMaxLds;
+}
+
+hipError_t launch_decode(const void* x, int xmode, const float* sx, float eps, const void* packed,
+                         const float* sw, int64_t sw_inc, int64_t T, int64_t O, int64_t K, int N,
+                         int M, void* y, bool y_bf16, int32_t* acc, hipStream_t s) {
+  if (!decode_fits(T, O, K, N, M, xmode)) return hipErrorInvalidValue;
+  const int blocks = dec_blocks(O);
+  const int R = (int)cdiv(cdiv(O, 16), blocks);
+  const DecodeArgs a{x, sx, eps, (const uint8_t*)packed, (int)row_pitch(K, N, M), sw,
+                     (int)sw_inc, (int)T, (int)O, (int)K, R, y, acc};
+  if (index_form(N, M))
+    return y_bf16 ? dispatch_x<true, true>(xmode, a, blocks, s)
+                  : dispatch_x<true, false>(xmode, a, blocks, s);
+  return y_bf16 ? dispatch_x<false, true>(xmode, a, blocks, s)
+                : dispatch_x<false, false>(xmode, a, blocks, s);
+}
+
+}  // namespace sbl

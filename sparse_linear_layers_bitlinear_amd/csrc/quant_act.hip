@@ -18,47 +18,11 @@ namespace sbl {
 
 constexpr int kActRowsPerBlock = 4;  // 4 wavefronts, one row each
 
-// Quantize V values with scale s and store them as V int8 at q.
-template <int V>
-__device__ __forceinline__ void quant_store(const float* f, float s, int8_t* q) {
-  uint32_t packed[V / 4];
-#pragma unroll
-  for (int e = 0; e < V; ++e) {
-    float v = rintf(f[e] * s);
-    v = fminf(fmaxf(v, -128.0f), 127.0f);
-    const uint32_t b = (uint32_t)((int)v) & 0xFFu;
-    if (e % 4 == 0) packed[e / 4] = b; else packed[e / 4] |= b << (8 * (e % 4));
-  }
-  if constexpr (V == 8) *(uint2*)q = make_uint2(packed[0], packed[1]);
-  else *(uint32_t*)q = packed[0];
-}
-
+// codes of one 16-byte input vector: 8 bytes (bf16) or 4 bytes (fp32)
 template <bool BF16>
-__device__ __forceinline__ void unpack_vec(const uint4& d, float* f) {
-  if constexpr (BF16) {
-    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      f[2 * h] = bf16_bits_to_f32(w[h] & 0xFFFFu);
-      f[2 * h + 1] = bf16_bits_to_f32(w[h] >> 16);
-    }
-  } else {
-    f[0] = __uint_as_float(d.x); f[1] = __uint_as_float(d.y);
-    f[2] = __uint_as_float(d.z); f[3] = __uint_as_float(d.w);
-  }
-}
-
-template <bool BF16>
-__device__ __forceinline__ uint32_t absmax_vec(const uint4& d) {
-  if constexpr (BF16) {
-    const uint32_t m = 0x7FFF7FFFu;
-    const uint32_t a = d.x & m, b = d.y & m, c = d.z & m, e = d.w & m;
-    const uint32_t lo = max(max(a & 0xFFFFu, b & 0xFFFFu), max(c & 0xFFFFu, e & 0xFFFFu));
-    const uint32_t hi = max(max(a >> 16, b >> 16), max(c >> 16, e >> 16));
-    return max(lo, hi) << 16;
-  } else {
-    return max(max(d.x & 0x7FFFFFFFu, d.y & 0x7FFFFFFFu), max(d.z & 0x7FFFFFFFu, d.w & 0x7FFFFFFFu));
-  }
+__device__ __forceinline__ void store_codes(const uint2& c, int8_t* q) {
+  if constexpr (BF16) *(uint2*)q = c;
+  else *(uint32_t*)q = c.x;
 }
 
 // Vector path. Rows of up to 64 * kActCache vectors stay in registers: all
@@ -91,24 +55,16 @@ __global__ __launch_bounds__(256) void k_quant_act_vec(const void* __restrict__ 
   for (int64_t i = lane + 64 * kActCache; i < nvec; i += 64) mx = max(mx, absmax_vec<BF16>(row[i]));
   mx = wave_max_u32(mx);
 
-  // scale in IEEE fp32: d = m + eps, s = 127 / d
-  const float dd = __uint_as_float(mx) + eps;
-  const float s = 127.0f / dd;
-  if (lane == 0) sx[t] = dd / 127.0f;
+  const ActScale sc = act_scale(mx, eps);
+  if (lane == 0) sx[t] = sc.s;
 
-  float f[V];
 #pragma unroll
   for (int u = 0; u < kActCache; ++u) {
     const int64_t i = lane + 64 * u;
-    if (i < nvec) {
-      unpack_vec<BF16>(d[u], f);
-      quant_store<V>(f, s, qrow + i * V);
-    }
+    if (i < nvec) store_codes<BF16>(act_codes_vec<BF16>(d[u], sc.q), qrow + i * V);
   }
-  for (int64_t i = lane + 64 * kActCache; i < nvec; i += 64) {
-    unpack_vec<BF16>(row[i], f);
-    quant_store<V>(f, s, qrow + i * V);
-  }
+  for (int64_t i = lane + 64 * kActCache; i < nvec; i += 64)
+    store_codes<BF16>(act_codes_vec<BF16>(row[i], sc.q), qrow + i * V);
 }
 
 // Scalar path for rows that are not 16-byte aligned or not whole vectors.
@@ -129,14 +85,11 @@ __global__ __launch_bounds__(256) void k_quant_act_scalar(const void* __restrict
     mx = max(mx, u & 0x7FFFFFFFu);
   }
   mx = wave_max_u32(mx);
-  const float dd = __uint_as_float(mx) + eps;
-  const float s = 127.0f / dd;
-  if (lane == 0) sx[t] = dd / 127.0f;
+  const ActScale sc = act_scale(mx, eps);
+  if (lane == 0) sx[t] = sc.s;
   for (int64_t i = lane; i < K; i += 64) {
     const float f = BF16 ? bf16_bits_to_f32(xb[i]) : xf[i];
-    float v = rintf(f * s);
-    v = fminf(fmaxf(v, -128.0f), 127.0f);
-    qrow[i] = (int8_t)(int)v;
+    qrow[i] = (int8_t)act_code(f, sc.q);
   }
 }
 

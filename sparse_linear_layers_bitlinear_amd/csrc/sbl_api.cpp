@@ -252,11 +252,10 @@ sbl_status sbl_linear_fwd(const void* x, sbl_dtype xdt, const void* w_master, sb
   int8_t* xq = (int8_t*)(base + L.xq);
   float* sx = (float*)(base + L.sx);
   float* gsw = (float*)(base + L.gsw);
-  hipError_t e = launch_quant_act(x, xdt == SBL_BF16, T, K, K, eps_a, xq, sx, stream);
-  if (e != hipSuccess) return hip_status(e, "linear_fwd/quant_act");
   const void* packed = prepacked;
   const float* sw = sw_prepacked;
   int64_t inc = sw_inc;
+  hipError_t e;
   if (!pre) {
     void* pk = base + L.packed;
     const PrepTensor t{w_master, O, K, nullptr, nullptr, pk, gsw, nullptr};
@@ -266,6 +265,15 @@ sbl_status sbl_linear_fwd(const void* x, sbl_dtype xdt, const void* w_master, sb
     sw = gsw + 1;
     inc = 0;
   }
+  // decode-sized batches: activation quantization fused into the GEMV
+  const int xmode = xdt == SBL_BF16 ? 1 : 2;
+  const char* ev = std::getenv("SBL_GEMM_TILE");   // a forced tile configuration takes the GEMM
+  if (T <= 16 && !(ev && std::atoi(ev) >= 0) && decode_fits(T, O, K, N, M, xmode))
+    return hip_status(launch_decode(x, xmode, nullptr, eps_a, packed, sw, inc, T, O, K, N, M, y,
+                                    ydt == SBL_BF16, nullptr, stream),
+                      "linear_fwd/decode");
+  e = launch_quant_act(x, xdt == SBL_BF16, T, K, K, eps_a, xq, sx, stream);
+  if (e != hipSuccess) return hip_status(e, "linear_fwd/quant_act");
   return hip_status(launch_gemm(xq, sx, packed, sw, inc, T, O, K, N, M, y, ydt == SBL_BF16,
                                 nullptr, stream),
                     "linear_fwd/gemm");

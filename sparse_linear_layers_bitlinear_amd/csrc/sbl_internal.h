@@ -65,6 +65,14 @@ hipError_t launch_pack(const int8_t* w_eff, const uint8_t* mask, int64_t O, int6
 hipError_t launch_unpack(const void* packed, int64_t O, int64_t K, int N, int M, int8_t* w_eff,
                          uint8_t* mask, hipStream_t s);
 
+// Decode path (1 <= T <= 16). xmode 0: xq int8 [T,K] and sx given; 1 / 2:
+// x bf16 / fp32 [T,K], quantized per token inside the kernel with eps.
+// decode_fits() tells whether a shape takes it (else the tiled GEMM runs).
+bool decode_fits(int64_t T, int64_t O, int64_t K, int N, int M, int xmode);
+hipError_t launch_decode(const void* x, int xmode, const float* sx, float eps, const void* packed,
+                         const float* sw, int64_t sw_inc, int64_t T, int64_t O, int64_t K, int N,
+                         int M, void* y, bool y_bf16, int32_t* acc, hipStream_t s);
+
 hipError_t launch_gemm(const int8_t* xq, const float* sx, const void* packed, const float* sw,
                        int64_t sw_inc, int64_t T, int64_t O, int64_t K, int N, int M, void* y,
                        bool y_bf16, int32_t* acc, hipStream_t s);

@@ -409,6 +409,74 @@ def test_decode_bitnet_layer(S, T):
         assert_f32_close(host(y), ref["y"])
 
 
+# ---------------------------------------------- decode path (T <= 16 tokens) --
+def _x_tensor(x, xdt):
+    return bf16_tensor(x) if xdt == "bf16" else to_dev(x)
+
+
+def _x_host(x, xdt):
+    """The activations the library sees (bf16 inputs round to bf16 first)."""
+    return bf16_round(x) if xdt == "bf16" else x
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 16])
+@pytest.mark.parametrize("xdt", ["bf16", "fp32"])
+@pytest.mark.parametrize("N,M,O,K", [(2, 4, 200, 2560), (6, 8, 37, 1000), (2, 4, 64, 6912),
+                                     (6, 8, 130, 8192), (2, 4, 48, 264), (1, 4, 16, 128)])
+def test_decode_fused_linear(S, T, xdt, N, M, O, K):
+    """Decode-sized batches: sbl_linear_fwd quantizes the activations inside
+    the GEMV. Against the oracle, and bit-identical to the separate
+    activation-quantization and GEMM calls."""
+    log_case("decode fused", T, xdt, N, M, O, K)
+    W, x = make_linear_inputs(T, O, K, seed=T * 31 + O + K + N)
+    if xdt == "fp32":   # full fp32 values, not bf16-exact ones
+        x = np.random.default_rng(T + K).standard_normal((T, K), dtype=np.float32)
+    xt = _x_tensor(x, xdt)
+    r = S.sbl_quant_mask_weight(to_dev(W), N, M)
+    y = S.sbl_linear_fwd(xt, N, M, prepacked=r["packed"], sw=r["gamma_sw"][1:], O=O,
+                         out_dtype=torch.float32)
+    yb = S.sbl_linear_fwd(xt, N, M, prepacked=r["packed"], sw=r["gamma_sw"][1:], O=O,
+                          out_dtype=torch.bfloat16)
+    ref = o.linear_fwd(_x_host(x, xdt), W, N, M)
+    assert_f32_close(host(y), ref["y"])
+    assert_bf16_close(host(yb), ref["y"])
+    xq, sx = S.sbl_quant_act(xt)
+    assert np.array_equal(host(xq), ref["xq"])
+    y2, acc = S.sbl_gemm(xq, sx, r["packed"], r["gamma_sw"][1:], O, N, M,
+                         out_dtype=torch.float32, want_acc=True)
+    assert np.array_equal(host(acc), ref["acc"])
+    assert np.array_equal(f32_bits(host(y)), f32_bits(host(y2)))
+    # from master weights (weight preparation, then the fused decode)
+    y3 = S.sbl_linear_fwd(xt, N, M, w_master=to_dev(W), out_dtype=torch.float32)
+    assert np.array_equal(f32_bits(host(y3)), f32_bits(host(y)))
+
+
+@pytest.mark.parametrize("R", [2, 3, 8])
+def test_decode_tiles_per_workgroup(S, R, monkeypatch):
+    """Several 16-row tiles per decode workgroup (forced), ragged O."""
+    monkeypatch.setenv("SBL_DECODE_R", str(R))
+    for (T, O, K, N, M) in [(4, 1000, 512, 2, 4), (16, 333, 1024, 6, 8), (1, 17, 128, 2, 4),
+                            (7, 130, 2688, 4, 8)]:
+        log_case("decode R", R, T, O, K, N, M)
+        _gemm_case(S, T, O, K, N, M, torch.bfloat16, seed=R * 13 + T + O, sw_per_row=True)
+        W, x = make_linear_inputs(T, O, K, seed=R + O)
+        r = S.sbl_quant_mask_weight(to_dev(W), N, M)
+        y = S.sbl_linear_fwd(bf16_tensor(x), N, M, prepacked=r["packed"],
+                             sw=r["gamma_sw"][1:], O=O, out_dtype=torch.float32)
+        assert_f32_close(host(y), o.linear_fwd(bf16_round(x), W, N, M)["y"])
+
+
+def test_decode_large_k_falls_back(S):
+    """16 tokens with K too long to stage in LDS take the tiled path."""
+    T, O, K, N, M = 16, 40, 12288, 2, 4
+    log_case("decode fallback", T, O, K)
+    W, x = make_linear_inputs(T, O, K, seed=5)
+    r = S.sbl_quant_mask_weight(to_dev(W), N, M)
+    y = S.sbl_linear_fwd(bf16_tensor(x), N, M, prepacked=r["packed"], sw=r["gamma_sw"][1:],
+                         O=O, out_dtype=torch.float32)
+    assert_f32_close(host(y), o.linear_fwd(bf16_round(x), W, N, M)["y"])
+
+
 @pytest.mark.parametrize("cfg", list(range(24)))
 def test_gemm_every_tile_config(S, cfg, monkeypatch):
     """Each workgroup-tile configuration of the GEMM, forced, on ragged shapes."""
