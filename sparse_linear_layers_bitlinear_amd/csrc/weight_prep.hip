@@ -332,26 +332,37 @@ __device__ PrepScalars scalars_from_bins(const unsigned long long* bins, int64_t
 
 // Sum of the per-block partial vectors into the 16 bins (one workgroup; the
 // serial part that turns the bins into gamma and the threshold runs in the
-// mask/pack kernel, overlapped with its W staging).
-__global__ __launch_bounds__(256) void k_absmean_reduce(const PrepBatchK batch,
+// mask/pack kernel, overlapped with its W staging). The partials were written
+// by workgroups all over the chip and come from beyond this XCD's L2, so every
+// thread issues the loads of all its (at most 4) partial vectors at once.
+constexpr int kReduceThreads = 256;
+constexpr int kReducePer = kAbsmeanMaxBlocks / kReduceThreads;
+static_assert(kAbsmeanMaxBlocks % kReduceThreads == 0, "partials per reduce thread");
+__global__ __launch_bounds__(kReduceThreads) void k_absmean_reduce(const PrepBatchK batch,
                                                         const unsigned long long* __restrict__ partials_all,
                                                         unsigned long long* __restrict__ bins_all) {
   const PrepItemK pi = prep_item(batch, blockIdx.x);     // one block per tensor
   const unsigned long long* __restrict__ partials = partials_all + (int64_t)pi.part0 * 16;
   const int nparts = pi.nparts;
   unsigned long long* __restrict__ bins_out = bins_all + (int64_t)blockIdx.x * 16;
+  uint4 v[kReducePer][8];
+#pragma unroll
+  for (int u = 0; u < kReducePer; ++u) {
+    const int b = min((int)threadIdx.x + kReduceThreads * u, nparts - 1);   // in bounds
+    const uint4* p = (const uint4*)(partials + (int64_t)b * 16);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[u][q] = p[q];
+  }
   unsigned long long acc[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) acc[j] = 0;
-  for (int b = threadIdx.x; b < nparts; b += 256) {
-    const uint4* p = (const uint4*)(partials + (int64_t)b * 16);
-    uint4 v[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = p[q];
+  for (int u = 0; u < kReducePer; ++u) {
+    const unsigned long long keep = (int)threadIdx.x + kReduceThreads * u < nparts ? ~0ull : 0ull;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      acc[2 * q] += (unsigned long long)v[q].x | ((unsigned long long)v[q].y << 32);
-      acc[2 * q + 1] += (unsigned long long)v[q].z | ((unsigned long long)v[q].w << 32);
+      acc[2 * q] += ((unsigned long long)v[u][q].x | ((unsigned long long)v[u][q].y << 32)) & keep;
+      acc[2 * q + 1] += ((unsigned long long)v[u][q].z | ((unsigned long long)v[u][q].w << 32)) & keep;
     }
   }
   // 256 x 16 -> 16 x 16 -> 16 through LDS (independent accesses)
@@ -517,6 +528,17 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
   constexpr int PIECES = 32 / V;               // pieces per chunk = pieces per thread
   const bool rows16 = ((K32 * (BF16 ? 2u : 4u)) % 16u) == 0;
   uint4 d[PIECES];
+  if (K32 % 128u == 0 && rows16) {
+    // every chunk lies inside its row and the rows are 32 * C elements long:
+    // the block's chunks are one contiguous run of W. All loads unconditional
+    // (clamped to the tensor's last piece; those chunks are inactive), so they
+    // are all in flight together.
+    const uint4* const src = (const uint4*)wv;
+    const uint32_t last = total * PIECES - 1u;
+#pragma unroll
+    for (int q = 0; q < PIECES; ++q)
+      d[q] = src[min(base * PIECES + threadIdx.x + (uint32_t)kChunksPerBlock * q, last)];
+  } else {
 #pragma unroll
   for (int q = 0; q < PIECES; ++q) {
     const uint32_t p = threadIdx.x + (uint32_t)kChunksPerBlock * q;
@@ -539,6 +561,7 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
         d[q] = make_uint4(t[0], t[1], t[2], t[3]);
       }
     }
+  }
   }
 #pragma unroll
   for (int q = 0; q < PIECES; ++q) {
@@ -671,7 +694,7 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
     hipLaunchKernelGGL((k_absmean_partial<false>), dim3(parts), dim3(kAbsThreads), 0, s, b, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_absmean_reduce, dim3(count), dim3(256), 0, s, b, partials, bins);
+  hipLaunchKernelGGL(k_absmean_reduce, dim3(count), dim3(kReduceThreads), 0, s, b, partials, bins);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)blk3), block(kQmpThreads);
