@@ -354,25 +354,33 @@ def _cpu_model():
     return "unknown"
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_qwen05b_ffn.txt")
-GEMM_SRC = os.path.join(ROOT, "sparse_linear_layers_bitlinear_amd", "csrc", "gemm.hip")
-
-
-def measured_traffic(kernel_call):
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary, scaled by the same counters on a plain
-    copy of known size. None if absent, for another kernel, or taken on a
-    different version of the kernel source."""
+TRAFFIC_FILES = [os.path.join(ROOT, "profiles", f)
+                 for f in ("traffic_qwen05b_ffn.txt", "traffic_bitnet_decode_t8.txt")]
+def measured_traffic(workload, kernel_call):
+    """HBM bytes per launch of the dominant call from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (scaled by the same counters on a plain
+    copy of known size). None if the call has no entry or its kernels' source
+    has changed since the counters were taken."""
     import hashlib
-    try:
-        kv = dict(line.split("=", 1) for line in open(TRAFFIC_FILE).read().split("\n")
+    text = ""
+    for path in TRAFFIC_FILES:
+        try:
+            text += open(path).read() + "\n\n"
+        except OSError:
+            pass
+    for block in text.split("\n\n"):
+        kv = dict(line.split("=", 1) for line in block.split("\n")
                   if "=" in line and not line.startswith("#"))
-        src = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
-        if kv.get("call", "").strip() != kernel_call or kv.get("gemm_src_sha256", "").strip() != src:
+        if kv.get("call", "").strip() != kernel_call or kv.get("workload", "").strip() != workload:
+            continue
+        try:
+            src = os.path.join(ROOT, kv["src"].strip())
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["src_sha256"].strip():
+                return None
+            return float(kv["hbm_bytes_per_launch"])
+        except (OSError, KeyError, ValueError):
             return None
-        return float(kv["hbm_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
-        return None
+    return None
 
 
 def calibrate_copy():
@@ -385,6 +393,13 @@ def calibrate_copy():
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n,
                       "bytes_written_per_copy": n, "copies": 3}))
+
+
+def traffic_tag(a, N, M):
+    """Workload key of the committed counter summaries."""
+    if a.workload == "bitnet_decode":
+        return f"bitnet_decode T={a.decode_T} L={a.layers}"
+    return f"{a.workload} T={WORKLOADS[a.workload].T} {N}:{M}"
 
 
 def per_call_rates(step, per_call):
@@ -434,7 +449,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(dom) if a.workload == "qwen05b_ffn" else None
+    roof["traffic"] = measured_traffic(traffic_tag(a, N, M), dom)
     roof["kernel"] = dom
     roof["avg_ms"] = round(per_call[dom], 5)
 
