@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    p.add_argument("--diagnostics", action="store_true",
+                   help="prefill: the weight preparation also emits the mask diagnostics (keep bits, "
+                        "flips against the previous step's mask, per-group pruning threshold)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -61,9 +64,9 @@ def parse():
 
 # ---------------------------------------------------------------- prefill --
 class PrefillStep:
-    def __init__(self, wl_name, N, M):
+    def __init__(self, wl_name, N, M, diagnostics=False):
         wl = WORKLOADS[wl_name]
-        self.wl, self.N, self.M = wl, N, M
+        self.wl, self.N, self.M, self.diag = wl, N, M, diagnostics
         W, X = make_workload(wl_name)
         dev = torch.device("cuda:0")
         self.T = wl.T
@@ -99,6 +102,18 @@ class PrefillStep:
                     "gamma_sw": torch.empty(2, dtype=torch.float32, device=dev)})
                 off_p += nb
                 off_o += l.O
+        if diagnostics:
+            # the previous step's mask: the same preparation on slightly moved weights
+            prev = [dict(it, w=(it["w"] * 1.001 + 1e-4).contiguous(), want_mask_bits=True)
+                    for it in self.prep_items]
+            prev = sbl.sbl_quant_mask_weight_batch(prev, N, M, ws=self.ws)
+            for it, pv in zip(self.prep_items, prev):
+                O, K = it["w"].shape
+                it["prev_mask_bits"] = pv["mask_bits"]
+                it["mask_bits"] = torch.empty_like(pv["mask_bits"])
+                it["flips"] = torch.empty(1, dtype=torch.int64, device=dev)
+                it["group_thr"] = torch.empty((O, K // M), dtype=torch.float32, device=dev)
+            torch.cuda.synchronize()
         self.ops = sum(2.0 * self.T * l.O * l.K for l in wl.linears)
 
     def calls(self):
@@ -144,10 +159,13 @@ class PrefillStep:
         if name.startswith("quant_act["):
             K = self.K_of[name[10:-1]]
             return "hbm", 2.0 * T * K + T * K + 4.0 * T, "bytes"
-        # weight preparation: W read twice (absmean pass, mask/code pass), packed written
-        return "hbm", sum(2.0 * l.O * l.K * self.W[l.name].element_size() +
-                          sbl.sbl_packed_bytes(l.O, l.K, self.N, self.M)
-                          for l in self.wl.linears), "bytes"
+        # weight preparation: W read twice (absmean pass, mask/code pass), packed written;
+        # with diagnostics also the keep bits written, the previous ones read, the thresholds
+        diag = sum(2.0 * 4 * l.O * (-(-l.K // 128) * 4) + 4.0 * l.O * l.K / self.M
+                   for l in self.wl.linears) if self.diag else 0.0
+        return "hbm", diag + sum(2.0 * l.O * l.K * self.W[l.name].element_size() +
+                                 sbl.sbl_packed_bytes(l.O, l.K, self.N, self.M)
+                                 for l in self.wl.linears), "bytes"
 
 
 # ----------------------------------------------------------------- decode --
@@ -399,7 +417,7 @@ def traffic_tag(a, N, M):
     """Workload key of the committed counter summaries."""
     if a.workload == "bitnet_decode":
         return f"bitnet_decode T={a.decode_T} L={a.layers}"
-    return f"{a.workload} T={WORKLOADS[a.workload].T} {N}:{M}"
+    return f"{a.workload} T={WORKLOADS[a.workload].T} {N}:{M}" + (" diag" if a.diagnostics else "")
 
 
 def per_call_rates(step, per_call):
@@ -435,7 +453,7 @@ def main():
     if a.workload == "bitnet_decode":
         step = DecodeStep(a.decode_T, a.layers)
     else:
-        step = PrefillStep(a.workload, N, M)
+        step = PrefillStep(a.workload, N, M, a.diagnostics)
     ms = time_steps(step, a.steps, a.warmup, a.eager)
     per_call, calls_per_step = per_call_times(step, max(5, min(a.steps, 20)))
     share = {k: per_call[k] * calls_per_step[k] for k in per_call}
@@ -465,6 +483,7 @@ def main():
         metric = "Sparse-BitLinear effective TOPS (prefill)"
         unit = "TOPS"
         config = {"workload": a.workload, "tokens": step.T, "nm": f"{N}:{M}",
+                  "mask_diagnostics": bool(a.diagnostics),
                   "projections": [f"{l.name} {l.O}x{l.K}" for l in wl.linears],
                   "mask": "recomputed every step", "dense_equiv_ops_per_step": step.ops}
     out = {

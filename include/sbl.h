@@ -134,6 +134,25 @@ typedef struct sbl_weight_prep {
   void* packed;
   float* gamma_sw;
   float* sw_rows;
+  /* Mask diagnostics, all optional (NULL = not computed). Sparse-BitNet
+   * summary, section 3.4 / 5: the mask flip rate r_t (Eq. 6: the mask
+   * positions that change between consecutive steps) and the per-block
+   * pruning threshold of the magnitude-stratification analysis (Fig. 6: the
+   * magnitude of the (N+1)-th largest weight of each group).
+   * mask_bits: device uint32 [O][C], C = ceil(K/128)*4 words per row; bit e of
+   *   word (o, c) is the keep bit of k = 32c + e (0 for k >= K) -- the layout
+   *   of the dense-form mask area.
+   * prev_mask_bits: device, same layout (e.g. the previous step's mask_bits);
+   *   given together with flips and mask_bits.
+   * flips: device uint64, set to the number of positions whose keep bit differs
+   *   from prev_mask_bits (r_t = flips / (O*K)); counted by one more small
+   *   kernel after the mask pass.
+   * group_thr: device float [O][K/M]: (N+1)-th largest |w| of each group of M
+   *   along K (the largest dropped magnitude; 0 when N == M). */
+  uint32_t* mask_bits;
+  const uint32_t* prev_mask_bits;
+  unsigned long long* flips;
+  float* group_thr;
 } sbl_weight_prep;
 
 #define SBL_MAX_PREP_BATCH 8
@@ -154,7 +173,8 @@ sbl_status sbl_quant_mask_weight_batch_workspace(int count, size_t* bytes);
  * ws: device workspace of at least sbl_quant_mask_weight_batch_workspace
  *   bytes; no initialisation needed, scratch after the call.
  * Errors: as sbl_quant_mask_weight, checked for every item before anything
- * is enqueued; count out of range -> SBL_ERR_SHAPE.
+ * is enqueued; count out of range -> SBL_ERR_SHAPE; prev_mask_bits, flips
+ * and mask_bits not all given when either of the first two is -> SBL_ERR_NULL.
  */
 sbl_status sbl_quant_mask_weight_batch(const sbl_weight_prep* items, int count, sbl_dtype wdt,
                                        int N, int M, float eps_w, void* ws, size_t ws_bytes,

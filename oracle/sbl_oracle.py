@@ -40,7 +40,7 @@ __all__ = [
     "quant_act", "absmean", "nm_mask", "ternary_codes", "apply_mask",
     "quant_mask_weight", "gemm_int", "gemm_int_bruteforce", "dequant",
     "to_bf16", "linear_fwd", "packed_row_bytes", "packed_bytes", "pack",
-    "unpack", "INDEX_FORM",
+    "unpack", "INDEX_FORM", "mask_words", "mask_flips", "group_threshold",
 ]
 
 F32 = np.float32
@@ -356,3 +356,50 @@ def unpack(packed: np.ndarray, O: int, K: int, N: int, M: int):
     w = _sext2(cw[:, :, None] >> _field_shift(np.arange(16))).reshape(O, -1)
     mk = ((mw[:, :, None] >> np.arange(32, dtype=np.uint32)) & 1).astype(np.uint8)
     return w[:, :K].copy(), mk.reshape(O, -1)[:, :K].copy()
+
+
+# ---------------------------------------------------------------------------
+# Mask diagnostics: flip count (for the flip rate r_t) and per-group threshold
+# ---------------------------------------------------------------------------
+def mask_words(mask: np.ndarray) -> np.ndarray:
+    """The library's bit layout of a keep-mask: uint32 [O, C] with
+    C = ceil(K/128)*4 words per row; bit e of word c is the mask of column
+    k = 32c + e (0 for k >= K). (A storage layout of this build, not a
+    definition of the pages.)"""
+    mask = np.asarray(mask, dtype=np.uint8)
+    O, K = mask.shape
+    C = _ceil(K, 128) * 4
+    full = np.zeros((O, 32 * C), np.uint64)
+    full[:, :K] = mask
+    bits = full.reshape(O, C, 32) << np.arange(32, dtype=np.uint64)
+    return bits.sum(axis=2).astype(np.uint32)
+
+
+def mask_flips(mask_prev: np.ndarray, mask_cur: np.ndarray) -> int:
+    """Number of mask positions that changed between two steps.
+
+    [SB] section 3.4 (Dual STE discussion) and the analysis of Figure 3b: the
+    mask flip rate r_t (Eq. 6) measures how many mask positions change
+    between consecutive steps. Reading: r_t = mask_flips / (O*K) (the
+    equation itself is not printed on the pages)."""
+    a = np.asarray(mask_prev, dtype=np.uint8)
+    b = np.asarray(mask_cur, dtype=np.uint8)
+    assert a.shape == b.shape
+    return int(np.count_nonzero(a != b))
+
+
+def group_threshold(w: np.ndarray, N: int, M: int) -> np.ndarray:
+    """Per-block pruning threshold of the magnitude-stratification analysis.
+
+    [SB] Figure 6 discussion: for each block (group of M along the input
+    dimension) the threshold t is the magnitude of the (N+1)-th largest
+    weight. With N == M nothing is pruned; reading: t = 0 then.
+    Returns float32 [O, K/M] (the master magnitude itself, not normalized)."""
+    w = np.asarray(w, dtype=F32)
+    O, K = w.shape
+    assert K % M == 0 and 1 <= N <= M
+    a = np.abs(w).reshape(O, K // M, M)
+    if N == M:
+        return np.zeros((O, K // M), F32)
+    desc = -np.sort(-a, axis=2)                         # magnitudes, largest first
+    return desc[:, :, N].astype(F32)

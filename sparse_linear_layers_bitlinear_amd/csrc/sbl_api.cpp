@@ -159,11 +159,19 @@ sbl_status sbl_quant_mask_weight_batch(const sbl_weight_prep* items, int count, 
     if (st != SBL_OK) return st;
     if (it.O < 1 || it.O * it.K >= (int64_t(1) << 31)) return SBL_ERR_SHAPE;
     if (!it.w || !it.gamma_sw) return SBL_ERR_NULL;
+    if ((it.prev_mask_bits == nullptr) != (it.flips == nullptr)) return SBL_ERR_NULL;
+    if (it.flips && !it.mask_bits) return SBL_ERR_NULL;   // flips compare the new mask bits
     for (const void* p : {it.w, (const void*)it.w_eff, (const void*)it.mask,
                           (const void*)it.packed, (const void*)it.gamma_sw,
-                          (const void*)it.sw_rows})
+                          (const void*)it.sw_rows, (const void*)it.mask_bits,
+                          (const void*)it.prev_mask_bits, (const void*)it.flips,
+                          (const void*)it.group_thr})
       if (p && !aligned16(p)) return SBL_ERR_ALIGN;
     t[i] = PrepTensor{it.w, it.O, it.K, it.w_eff, it.mask, it.packed, it.gamma_sw, it.sw_rows};
+    t[i].mask_bits = it.mask_bits;
+    t[i].prev_mask_bits = it.prev_mask_bits;
+    t[i].flips = it.flips;
+    t[i].group_thr = it.group_thr;
   }
   if (!ws) return SBL_ERR_WORKSPACE;
   if (ws_bytes < prep_workspace_bytes(count)) return SBL_ERR_WORKSPACE;

@@ -45,6 +45,10 @@ struct PrepTensor {
   void* packed;       // optional
   float* gamma_sw;    // required, device float[2]
   float* sw_rows;     // optional
+  uint32_t* mask_bits = nullptr;             // optional diagnostics (see sbl.h)
+  const uint32_t* prev_mask_bits = nullptr;
+  unsigned long long* flips = nullptr;
+  float* group_thr = nullptr;
 };
 
 struct DeviceInfo {

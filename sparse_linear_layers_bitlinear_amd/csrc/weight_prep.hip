@@ -87,6 +87,10 @@ struct PrepItemK {
   uint8_t* packed;
   float* gamma_sw;
   float* sw_rows;
+  uint32_t* mask_bits;                       // optional mask diagnostics
+  const uint32_t* prev_mask_bits;
+  unsigned long long* flips;
+  float* group_thr;
   int64_t O, K;
   int32_t C, pitch, code_chunks, mask_off;   // packed-record geometry
   int32_t part0, nparts;                     // its partial vectors (= its partial-pass blocks)
@@ -345,6 +349,7 @@ __global__ __launch_bounds__(kReduceThreads) void k_absmean_reduce(const PrepBat
   const unsigned long long* __restrict__ partials = partials_all + (int64_t)pi.part0 * 16;
   const int nparts = pi.nparts;
   unsigned long long* __restrict__ bins_out = bins_all + (int64_t)blockIdx.x * 16;
+  if (threadIdx.x == 0 && pi.flips) *pi.flips = 0;     // accumulated by the mask pass
   uint4 v[kReducePer][8];
 #pragma unroll
   for (int u = 0; u < kReducePer; ++u) {
@@ -608,6 +613,24 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
       keep |= kb << (g * M);
     }
   }
+  // mask diagnostics (need no scalar either)
+  {
+    const uint32_t vbits = k0 >= K32 ? 0u : (K32 - k0 >= 32u ? 0xFFFFFFFFu : ((1u << (K32 - k0)) - 1u));
+    if (pi.mask_bits && active) pi.mask_bits[(int64_t)o * C + c] = keep & vbits;
+    if (pi.group_thr && active) {
+      // (N+1)-th largest |w| of each group = the largest dropped magnitude
+      constexpr int G = 32 / M;
+      float* const thr = pi.group_thr + (int64_t)o * (K / M) + (int64_t)c * G;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int e = 0; e < M; ++e)
+          if (!((keep >> (g * M + e)) & 1u)) t = max(t, a[g * M + e]);
+        if (k0 + (uint32_t)(g * M) < K32) thr[g] = __uint_as_float(t);
+      }
+    }
+  }
   __syncthreads();                                    // (2) scalars from the fifth wave
   if (!active) return;
   const PrepScalars sc = scal;
@@ -653,6 +676,30 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
   }
 }
 
+// Mask flips against the previous step's keep bits (both in the word layout
+// of mask_bits), for the tensors that ask for them: a grid-stride popcount
+// of (cur ^ prev), summed in LDS, one atomic per workgroup (the counter was
+// zeroed by the reduce kernel). Same-address atomics from every workgroup of
+// the mask pass would serialize; kFlipBlocks per tensor keeps them few.
+constexpr int kFlipBlocks = 64;
+__global__ __launch_bounds__(256) void k_mask_flips(const PrepBatchK batch) {
+  const int item = blockIdx.x / kFlipBlocks, lb = blockIdx.x % kFlipBlocks;
+  const PrepItemK pi = prep_item(batch, item);
+  if (!pi.flips) return;                               // uniform per workgroup
+  const int64_t n = pi.O * (int64_t)pi.C;
+  uint32_t cnt = 0;
+  for (int64_t i = (int64_t)lb * 256 + threadIdx.x; i < n; i += (int64_t)kFlipBlocks * 256)
+    cnt += (uint32_t)__popc(pi.mask_bits[i] ^ pi.prev_mask_bits[i]);
+  __shared__ uint32_t part[4];
+  const uint32_t w = wave_sum_u32(cnt);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = w;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t t = part[0] + part[1] + part[2] + part[3];
+    if (t) atomicAdd(pi.flips, (unsigned long long)t);
+  }
+}
+
 hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf16, int N, int M,
                                     float eps, void* ws, hipStream_t s) {
   PrepBatchK b{};
@@ -669,6 +716,10 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
     k.packed = (uint8_t*)t.packed;
     k.gamma_sw = t.gamma_sw;
     k.sw_rows = t.sw_rows;
+    k.mask_bits = t.mask_bits;
+    k.prev_mask_bits = t.prev_mask_bits;
+    k.flips = t.flips;
+    k.group_thr = t.group_thr;
     k.O = t.O;
     k.K = t.K;
     k.C = (int32_t)row_chunks(t.K);
@@ -716,6 +767,11 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
   }
 #undef SBL_QMP8
 #undef SBL_QMP
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bool any_flips = false;
+  for (int i = 0; i < count; ++i) any_flips |= items[i].flips != nullptr;
+  if (any_flips) hipLaunchKernelGGL(k_mask_flips, dim3(count * kFlipBlocks), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 

@@ -33,7 +33,9 @@ class WeightPrep(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("O", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("w_eff", ctypes.c_void_p), ("mask", ctypes.c_void_p),
                 ("packed", ctypes.c_void_p), ("gamma_sw", ctypes.c_void_p),
-                ("sw_rows", ctypes.c_void_p)]
+                ("sw_rows", ctypes.c_void_p), ("mask_bits", ctypes.c_void_p),
+                ("prev_mask_bits", ctypes.c_void_p), ("flips", ctypes.c_void_p),
+                ("group_thr", ctypes.c_void_p)]
 
 
 SBL_MAX_PREP_BATCH = 8
@@ -155,8 +157,10 @@ def sbl_quant_mask_weight_batch_workspace(count: int) -> int:
 def sbl_quant_mask_weight_batch(items, N: int, M: int, eps_w: float = 1e-5, ws=None):
     """items: list of dicts with w [O, K] (one dtype for all, contiguous) and
     optional output tensors packed, sw_rows, w_eff, mask, gamma_sw (allocated
-    here when absent: gamma_sw always, packed unless want_packed=False).
-    Returns the list of dicts with every output filled in."""
+    here when absent: gamma_sw always, packed unless want_packed=False), and
+    the optional mask diagnostics mask_bits, prev_mask_bits + flips, group_thr
+    (want_mask_bits / want_group_thr allocate them; flips is allocated when
+    prev_mask_bits is given). Returns the list of dicts with every output."""
     assert 1 <= len(items) <= SBL_MAX_PREP_BATCH
     dev = items[0]["w"].device
     dt = items[0]["w"].dtype
@@ -172,10 +176,22 @@ def sbl_quant_mask_weight_batch(items, N: int, M: int, eps_w: float = 1e-5, ws=N
         if o.get("packed") is None and o.get("want_packed", True):
             o["packed"] = torch.empty(sbl_packed_bytes(O, K, N, M), dtype=torch.uint8,
                                       device=dev)
-        for k in ("packed", "sw_rows", "w_eff", "mask"):
+        C = -(-K // 128) * 4
+        if o.get("mask_bits") is None and o.get("want_mask_bits"):
+            o["mask_bits"] = torch.empty((O, C), dtype=torch.int32, device=dev)
+        if o.get("group_thr") is None and o.get("want_group_thr"):
+            o["group_thr"] = torch.empty((O, K // M), dtype=torch.float32, device=dev)
+        if o.get("prev_mask_bits") is not None:
+            if o.get("flips") is None:
+                o["flips"] = torch.empty(1, dtype=torch.int64, device=dev)
+            if o.get("mask_bits") is None:
+                o["mask_bits"] = torch.empty((O, C), dtype=torch.int32, device=dev)
+        for k in ("packed", "sw_rows", "w_eff", "mask", "mask_bits", "prev_mask_bits", "flips",
+                  "group_thr"):
             o.setdefault(k, None)
         arr[i] = WeightPrep(_ptr(w), O, K, _ptr(o["w_eff"]), _ptr(o["mask"]), _ptr(o["packed"]),
-                            _ptr(o["gamma_sw"]), _ptr(o["sw_rows"]))
+                            _ptr(o["gamma_sw"]), _ptr(o["sw_rows"]), _ptr(o["mask_bits"]),
+                            _ptr(o["prev_mask_bits"]), _ptr(o["flips"]), _ptr(o["group_thr"]))
         outs.append(o)
     nws = sbl_quant_mask_weight_batch_workspace(len(items))
     if ws is None:

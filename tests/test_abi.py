@@ -154,6 +154,19 @@ def test_weight_batch_validation(S):
     assert call(items(ok), 1, N=9) == 3                           # N:M
     assert call(items(ok, ok, ok), 3, wsb=16) == 6                # workspace size
     assert call(items(ok), 1, wsp=None) == 6
+    diag = items(ok)
+    diag[0].prev_mask_bits = FAKE                                 # previous mask without flips
+    assert call(diag, 1) == 1
+    diag = items(ok)
+    diag[0].flips = FAKE                                          # flips without previous mask
+    assert call(diag, 1) == 1
+    diag = items(ok)
+    diag[0].prev_mask_bits = FAKE                                 # flips without the new mask bits
+    diag[0].flips = FAKE
+    assert call(diag, 1) == 1
+    diag = items(ok)
+    diag[0].group_thr = MIS                                       # misaligned diagnostics output
+    assert call(diag, 1) == 5
     n = ctypes.c_size_t()
     for cnt in range(1, 9):
         assert L.sbl_quant_mask_weight_batch_workspace(cnt, ctypes.byref(n)) == 0

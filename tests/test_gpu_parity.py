@@ -154,6 +154,42 @@ def test_quant_mask_weight_batch_parity(S, N, M, dt):
         assert np.array_equal(host(one["gamma_sw"]), gs)
 
 
+@pytest.mark.parametrize("N,M", [(6, 8), (2, 4), (3, 8), (7, 8), (8, 8), (1, 4)])
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+def test_mask_diagnostics_parity(S, N, M, dt):
+    """Mask diagnostics computed with the mask: the keep bits, the number of
+    positions that flipped against a previous step's mask, and the (N+1)-th
+    largest magnitude of every group -- bit for bit against the oracle."""
+    shapes = [(37, 264), (64, 1024), (19, 136), (5, 8)]
+    shapes = [(O, K) for O, K in shapes if K % M == 0]
+    log_case("mask diagnostics", N, M, dt, shapes)
+    rng = np.random.default_rng(N * 8 + M)
+    cases, items = [], []
+    for i, (O, K) in enumerate(shapes):
+        W0, _ = make_linear_inputs(1, O, K, seed=2000 + i)
+        W1 = (W0 + np.float32(0.01) * rng.standard_normal((O, K), dtype=np.float32)).astype(F32)
+        if i == 0:
+            W1[0, :M] = W1[0, 0]                 # a tied group
+        if dt == "bf16":
+            W0, W1 = bf16_round(W0), bf16_round(W1)
+        prev = o.mask_words(o.nm_mask(W0, N, M))
+        cases.append((W0, W1, prev))
+        items.append({"w": bf16_tensor(W1) if dt == "bf16" else to_dev(W1),
+                      "prev_mask_bits": to_dev(prev.view(np.int32)),
+                      "want_mask_bits": True, "want_group_thr": True})
+    outs = S.sbl_quant_mask_weight_batch(items, N, M)
+    for (W0, W1, prev), r in zip(cases, outs):
+        m0, m1 = o.nm_mask(W0, N, M), o.nm_mask(W1, N, M)
+        assert np.array_equal(host(r["mask_bits"]).view(np.uint32), o.mask_words(m1))
+        assert int(host(r["flips"])[0]) == o.mask_flips(m0, m1)
+        assert np.array_equal(f32_bits(host(r["group_thr"])), f32_bits(o.group_threshold(W1, N, M)))
+    # the flip counter starts from zero on every call
+    outs2 = S.sbl_quant_mask_weight_batch(
+        [dict(it, flips=r["flips"]) for it, r in zip(items, outs)], N, M)
+    for (W0, W1, prev), r in zip(cases, outs2):
+        assert int(host(r["flips"])[0]) == o.mask_flips(o.nm_mask(W0, N, M), o.nm_mask(W1, N, M))
+
+
 def test_quant_mask_weight_batch_full_size(S):
     """The three projections of the Qwen2.5-0.5B FFN prepared in one batch
     (K differs between them), as the benchmark step does."""

@@ -369,3 +369,52 @@ def test_workload_shapes():
     assert [l.K for l in wl.linears] == [2048, 2048, 11008]
     assert all(l.O % 128 == 0 and l.K % 128 == 0
                for w in WORKLOADS.values() for l in w.linears if w.name != "tiny")
+
+
+# ------------------------------------------------------ mask diagnostics ---
+@pytest.mark.parametrize("N,M", [(6, 8), (2, 4), (1, 8), (7, 8), (8, 8), (4, 4)])
+def test_group_threshold_bruteforce_and_mask_relation(N, M):
+    """The (N+1)-th largest |w| per group, by a plain sort of Python floats,
+    and its relation to the mask: every kept magnitude >= t = the largest
+    dropped magnitude (whatever the tie rule)."""
+    rng = np.random.default_rng(N * 10 + M)
+    w = rng.standard_normal((5, 8 * M)).astype(np.float32)
+    w[0, :M] = 0.25                       # a group of ties
+    w[1, M:2 * M] = np.float32(-0.0)      # signed zeros
+    t = o.group_threshold(w, N, M)
+    mask = o.nm_mask(w, N, M)
+    for r in range(w.shape[0]):
+        for g in range(w.shape[1] // M):
+            mags = [abs(float(v)) for v in w[r, g * M:(g + 1) * M]]
+            want = 0.0 if N == M else sorted(mags, reverse=True)[N]
+            assert float(t[r, g]) == want
+            kept = [m for m, k in zip(mags, mask[r, g * M:(g + 1) * M]) if k]
+            dropped = [m for m, k in zip(mags, mask[r, g * M:(g + 1) * M]) if not k]
+            if dropped:
+                assert min(kept) >= float(t[r, g]) == max(dropped)
+
+
+def test_mask_flips_hamming_and_pairs():
+    a = np.array([[1, 1, 0, 0, 1, 0, 1, 0]], np.uint8)
+    b = np.array([[0, 1, 1, 0, 1, 0, 1, 0]], np.uint8)
+    assert o.mask_flips(a, b) == 2 == o.mask_flips(b, a)
+    assert o.mask_flips(a, a) == 0
+    rng = np.random.default_rng(3)
+    w1 = rng.standard_normal((6, 64)).astype(np.float32)
+    w2 = w1 + np.float32(0.3) * rng.standard_normal((6, 64)).astype(np.float32)
+    m1, m2 = o.nm_mask(w1, 6, 8), o.nm_mask(w2, 6, 8)
+    brute = sum(int(x != y) for x, y in zip(m1.ravel().tolist(), m2.ravel().tolist()))
+    assert o.mask_flips(m1, m2) == brute
+    # both masks keep exactly N per group: flips come in pairs within a group
+    d = (m1 != m2).reshape(6, 8, 8).sum(axis=2)
+    assert np.all(d % 2 == 0) and brute > 0
+
+
+def test_mask_words_hand_layout():
+    m = np.zeros((2, 40), np.uint8)
+    m[0, [0, 31, 32, 39]] = 1
+    m[1, 5] = 1
+    words = o.mask_words(m)
+    assert words.shape == (2, 4) and words.dtype == np.uint32
+    assert words[0].tolist() == [0x80000001, 0x81, 0, 0]
+    assert words[1].tolist() == [0x20, 0, 0, 0]
