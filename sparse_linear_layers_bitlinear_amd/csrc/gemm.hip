@@ -575,6 +575,12 @@ struct RaCfg {
   static constexpr size_t LDS = SCALES + (size_t)(BM + BN) * 4;
 };
 
+// largest divisor of n that is at most 8 (1 for n <= 0)
+__host__ __device__ constexpr int largest_divisor_upto8(int n) {
+  return n <= 0 ? 1 : n % 8 == 0 ? 8 : n % 7 == 0 ? 7 : n % 6 == 0 ? 6 : n % 5 == 0 ? 5 :
+         n % 4 == 0 ? 4 : n % 3 == 0 ? 3 : n % 2 == 0 ? 2 : 1;
+}
+
 template <int WO, int KS, int FI, int FJ, int NA, bool SP, bool YBF16>
 __global__ __launch_bounds__(64 * WO * KS) __attribute__((amdgpu_waves_per_eu(2)))
 void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
@@ -865,7 +871,7 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
       constexpr int LPR = CPR < 64 ? CPR : 64;        // lanes per row (full-tile path)
       constexpr int RPI = 64 / LPR;                   // rows per wave instruction
       constexpr int RWF = BN / (NW * RPI);            // row groups per wave
-      constexpr int RF = RWF < 8 ? (RWF > 0 ? RWF : 1) : 8;   // row groups in flight
+      constexpr int RF = largest_divisor_upto8(RWF);          // row groups in flight
       constexpr bool FULL_OK = CPR % LPR == 0 && BN % (NW * RPI) == 0 && RWF % RF == 0 && RWF > 0;
       if (FULL_OK && (Oi & 3) == 0 && eo0 + BM <= Oi && et0 + BN <= Ti) {
         // whole tile inside y: straight-line reads and 8-byte stores
@@ -963,7 +969,9 @@ enum TileCfg { kT256x256 = 0, kT256x128 = 1, kT128x256 = 2, kT128x128 = 3, kT256
                kR128x64k4 = 21,    // WO 2, KS 4, FI 4, FJ 4
                kR128x128k2 = 22,   // WO 2, KS 2, FI 4, FJ 8 (NA 2)
                kR512x64w8 = 23,    // WO 8, KS 1, FI 4, FJ 4
-               kNumCfg = 24 };
+               kR256x80 = 24,      // WO 4, KS 1, FI 4, FJ 5
+               kR256x96 = 25,      // WO 4, KS 1, FI 4, FJ 6 (NA 2)
+               kNumCfg = 26 };
 
 struct Args {
   const int8_t* xq; const float* sx; const uint8_t* packed; int64_t pitch; const float* sw;
@@ -1045,6 +1053,8 @@ static hipError_t launch_sel(int cfg, const Args& a, hipStream_t s) {
     case kR128x64k4: return launch_ra<2, 4, 4, 4, 4, SP, KA16, YBF16>(a, s);
     case kR128x128k2: return launch_ra<2, 2, 4, 8, 2, SP, KA16, YBF16>(a, s);
     case kR512x64w8: return launch_ra<8, 1, 4, 4, 4, SP, KA16, YBF16>(a, s);
+    case kR256x80: return launch_ra<4, 1, 4, 5, 4, SP, KA16, YBF16>(a, s);
+    case kR256x96: return launch_ra<4, 1, 4, 6, 2, SP, KA16, YBF16>(a, s);
     case kT64x128: return launch_cfg<64, 128, 2, 2, SP, KA16, YBF16>(a, s);
     case kDma128x256: return launch_dma<128, 256, 2, 4, SP, YBF16, SP ? 3 : 4>(a, s);
     case kDma256x128: return launch_dma<256, 128, 4, 2, SP, YBF16, SP ? 4 : 5>(a, s);
@@ -1070,8 +1080,7 @@ static hipError_t launch_sel(int cfg, const Args& a, hipStream_t s) {
 //  - dense N:M, K >= 2048 and at least two 256x128 tiles per CU: 256x128
 //    (wave tile 64x128, half the code-expansion work per MFMA);
 //  - dense N:M otherwise: 256x64;
-//  - 2:4: 256x64 for short K, the LDS-staged 256x128 (8 waves) for medium K,
-//    512x64 (8 waves) for long K.
+//  - 2:4: 256x96 (wave tile 64x96) below K = 4096, 512x64 (8 waves) above.
 static int choose_cfg(int64_t T, int64_t O, int64_t K, bool sp) {
   // tuning override (read on every call so tests can force each configuration)
   const char* ev = std::getenv("SBL_GEMM_TILE");
@@ -1082,11 +1091,7 @@ static int choose_cfg(int64_t T, int64_t O, int64_t K, bool sp) {
   const int64_t t64 = cdiv(O, 256) * cdiv(T, 64);
   const int64_t t128 = cdiv(O, 256) * cdiv(T, 128);
   if (t64 < cus) return kR128x64k2;
-  if (sp) {
-    if (K >= 4096) return kR512x64w8;
-    if (K >= 1536) return kT256x128w8;
-    return kR256x64;
-  }
+  if (sp) return K >= 4096 ? kR512x64w8 : kR256x96;
   if (K >= 2048 && t128 >= 2 * cus) return kR256x128;
   return kR256x64;
 }
