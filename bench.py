@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    p.add_argument("--fused-norm", action="store_true",
+                   help="prefill: quantize each FFN input as Q_a(RMSNorm(x) * g) in one pass "
+                        "(sbl_rmsnorm_quant_act) instead of Q_a(x)")
     p.add_argument("--diagnostics", action="store_true",
                    help="prefill: the weight preparation also emits the mask diagnostics (keep bits, "
                         "flips against the previous step's mask, per-group pruning threshold)")
@@ -64,9 +67,9 @@ def parse():
 
 # ---------------------------------------------------------------- prefill --
 class PrefillStep:
-    def __init__(self, wl_name, N, M, diagnostics=False):
+    def __init__(self, wl_name, N, M, diagnostics=False, fused_norm=False):
         wl = WORKLOADS[wl_name]
-        self.wl, self.N, self.M, self.diag = wl, N, M, diagnostics
+        self.wl, self.N, self.M, self.diag, self.norm = wl, N, M, diagnostics, fused_norm
         W, X = make_workload(wl_name)
         dev = torch.device("cuda:0")
         self.T = wl.T
@@ -76,6 +79,11 @@ class PrefillStep:
         self.xq = {k: torch.empty((self.T, K), dtype=torch.int8, device=dev)
                    for k, K in self.K_of.items()}
         self.sx = {k: torch.empty(self.T, dtype=torch.float32, device=dev) for k in self.K_of}
+        # RMSNorm gains for the fused-norm variant (seeded, 1 + 0.1 N(0,1))
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        self.gain = {k: 1 + 0.1 * torch.randn(K, generator=gen, device=dev)
+                     for k, K in self.K_of.items()}
         # group projections that share an input into one GEMM over concatenated rows
         self.groups = {}
         for lin in wl.linears:
@@ -121,8 +129,12 @@ class PrefillStep:
         N, M = self.N, self.M
         out = []
         for xn in self.groups:
-            out.append((f"quant_act[{xn}]",
-                        lambda xn=xn: sbl.sbl_quant_act(self.x[xn], xq=self.xq[xn], sx=self.sx[xn])))
+            if self.norm:
+                out.append((f"quant_act[{xn}]", lambda xn=xn: sbl.sbl_rmsnorm_quant_act(
+                    self.x[xn], self.gain[xn], xq=self.xq[xn], sx=self.sx[xn])))
+            else:
+                out.append((f"quant_act[{xn}]", lambda xn=xn: sbl.sbl_quant_act(
+                    self.x[xn], xq=self.xq[xn], sx=self.sx[xn])))
         out.append((f"quant_mask_weight[{'+'.join(l.name for l in self.wl.linears)}]",
                     lambda: sbl.sbl_quant_mask_weight_batch(self.prep_items, N, M, ws=self.ws)))
         for xn, lins in self.groups.items():
@@ -158,7 +170,7 @@ class PrefillStep:
             return "mfma", ops, "ops"
         if name.startswith("quant_act["):
             K = self.K_of[name[10:-1]]
-            return "hbm", 2.0 * T * K + T * K + 4.0 * T, "bytes"
+            return "hbm", 2.0 * T * K + T * K + 4.0 * T + (4.0 * K if self.norm else 0.0), "bytes"
         # weight preparation: W read twice (absmean pass, mask/code pass), packed written;
         # with diagnostics also the keep bits written, the previous ones read, the thresholds
         diag = sum(2.0 * 4 * l.O * (-(-l.K // 128) * 4) + 4.0 * l.O * l.K / self.M
@@ -417,7 +429,8 @@ def traffic_tag(a, N, M):
     """Workload key of the committed counter summaries."""
     if a.workload == "bitnet_decode":
         return f"bitnet_decode T={a.decode_T} L={a.layers}"
-    return f"{a.workload} T={WORKLOADS[a.workload].T} {N}:{M}" + (" diag" if a.diagnostics else "")
+    return (f"{a.workload} T={WORKLOADS[a.workload].T} {N}:{M}" + (" diag" if a.diagnostics else "")
+            + (" norm" if a.fused_norm else ""))
 
 
 def per_call_rates(step, per_call):
@@ -453,7 +466,7 @@ def main():
     if a.workload == "bitnet_decode":
         step = DecodeStep(a.decode_T, a.layers)
     else:
-        step = PrefillStep(a.workload, N, M, a.diagnostics)
+        step = PrefillStep(a.workload, N, M, a.diagnostics, a.fused_norm)
     ms = time_steps(step, a.steps, a.warmup, a.eager)
     per_call, calls_per_step = per_call_times(step, max(5, min(a.steps, 20)))
     share = {k: per_call[k] * calls_per_step[k] for k in per_call}
@@ -483,7 +496,7 @@ def main():
         metric = "Sparse-BitLinear effective TOPS (prefill)"
         unit = "TOPS"
         config = {"workload": a.workload, "tokens": step.T, "nm": f"{N}:{M}",
-                  "mask_diagnostics": bool(a.diagnostics),
+                  "mask_diagnostics": bool(a.diagnostics), "fused_rmsnorm": bool(a.fused_norm),
                   "projections": [f"{l.name} {l.O}x{l.K}" for l in wl.linears],
                   "mask": "recomputed every step", "dense_equiv_ops_per_step": step.ops}
     out = {

@@ -93,6 +93,26 @@ const char* sbl_version(void);
 sbl_status sbl_quant_act(const void* x, sbl_dtype xdt, int64_t T, int64_t K, int64_t ldx,
                          float eps_a, int8_t* xq, float* sx, hipStream_t stream);
 
+/*
+ * a1 with the normalization before it fused in: x~ = Q_a(RMSNorm(x)).
+ * Sparse-BitNet summary, section 3.4 (Algorithm 1 walk-through: the
+ * activations are normalized -- RMSNorm in BitNet -- then quantized); BitNet
+ * b1.58 2B4T summary, section 3.2 (subln normalization, no bias terms).
+ * The pages fix no arithmetic for the norm; per row t this call computes
+ *   sq_k = fp32(x_k * x_k), S = their fp64 sum in a fixed order (lane l of a
+ *     64-lane group sums the 16-byte vectors l, l+64, ... in element order;
+ *     the 64 partial sums are combined by an xor butterfly, offsets 32..1),
+ *   r = fp32(1 / sqrt(S / K + eps_n)) in fp64,
+ *   z_k = fp32(fp32(x_k * r) * gain[k])  (gain NULL: z_k = fp32(x_k * r)),
+ * and then exactly sbl_quant_act on z (xq and sx as there; sx refers to z).
+ * gain: optional device float [K] (16-byte aligned). eps_n > 0, normal.
+ * Rows must be 16-byte aligned (ldx * element size % 16 == 0) and K a
+ * multiple of 8 (bf16) or 4 (fp32), else SBL_ERR_SHAPE.
+ */
+sbl_status sbl_rmsnorm_quant_act(const void* x, sbl_dtype xdt, const float* gain, int64_t T,
+                                 int64_t K, int64_t ldx, float eps_n, float eps_a, int8_t* xq,
+                                 float* sx, hipStream_t stream);
+
 /* Workspace bytes sbl_quant_mask_weight needs for an [O, K] tensor. */
 sbl_status sbl_quant_mask_weight_workspace(int64_t O, int64_t K, size_t* bytes);
 

@@ -41,6 +41,7 @@ __all__ = [
     "quant_mask_weight", "gemm_int", "gemm_int_bruteforce", "dequant",
     "to_bf16", "linear_fwd", "packed_row_bytes", "packed_bytes", "pack",
     "unpack", "INDEX_FORM", "mask_words", "mask_flips", "group_threshold",
+    "rms_scale", "rmsnorm_quant_act",
 ]
 
 F32 = np.float32
@@ -403,3 +404,46 @@ def group_threshold(w: np.ndarray, N: int, M: int) -> np.ndarray:
         return np.zeros((O, K // M), F32)
     desc = -np.sort(-a, axis=2)                         # magnitudes, largest first
     return desc[:, :, N].astype(F32)
+
+
+# ---------------------------------------------------------------------------
+# Q_a(Norm(x)): RMS normalization before the activation quantizer
+# ---------------------------------------------------------------------------
+def rms_scale(x: np.ndarray, eps_n: float, vec: int) -> np.ndarray:
+    """Per-row r = fp32(1 / sqrt(S / K + eps_n)).
+
+    [SB] Algorithm 1 walk-through: x~ = Q_a(Norm(x)), Norm likely RMSNorm;
+    [B2T] section 3.2: subln normalization without bias terms. The pages fix
+    no arithmetic; reading (the kernel's): sq_k = fp32(x_k * x_k); S is their
+    fp64 sum in this order -- lane l of 64 sums the vectors l, l+64, ... of
+    `vec` consecutive elements, element by element; the 64 lane sums are
+    combined by an xor butterfly (offsets 32, 16, ..., 1); then fp64 division,
+    square root and reciprocal, rounded once to fp32.
+    x: [T, K] float32 with K % vec == 0. Returns float32 [T]."""
+    x = np.asarray(x, dtype=F32)
+    T, K = x.shape
+    assert K % vec == 0
+    sq = (x * x).astype(F32).astype(np.float64)         # fp32 products, exact in fp64
+    nvec = K // vec
+    U = -(-nvec // 64)
+    padded = np.zeros((T, U * 64, vec), np.float64)     # +0.0 padding adds nothing
+    padded[:, :nvec] = sq.reshape(T, nvec, vec)
+    per_lane = padded.reshape(T, U, 64, vec).transpose(0, 2, 1, 3).reshape(T, 64, U * vec)
+    S = np.cumsum(per_lane, axis=2)[:, :, -1]           # sequential per lane
+    lanes = np.arange(64)
+    for off in (32, 16, 8, 4, 2, 1):
+        S = S + S[:, lanes ^ off]
+    S = S[:, 0]
+    r = 1.0 / np.sqrt(S / float(K) + float(np.float32(eps_n)))
+    return r.astype(F32)
+
+
+def rmsnorm_quant_act(x: np.ndarray, gain, eps_n: float, eps_a: float, vec: int):
+    """z = fp32(fp32(x * r) * gain) per element (gain None: fp32(x * r)),
+    then quant_act(z). Returns (xq int8 [T, K], sx float32 [T])."""
+    x = np.asarray(x, dtype=F32)
+    r = rms_scale(x, eps_n, vec)
+    z = (x * r[:, None]).astype(F32)
+    if gain is not None:
+        z = (z * np.asarray(gain, dtype=F32)[None, :]).astype(F32)
+    return quant_act(z, eps_a)

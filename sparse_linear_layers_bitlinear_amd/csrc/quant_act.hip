@@ -93,6 +93,148 @@ __global__ __launch_bounds__(256) void k_quant_act_scalar(const void* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// RMS normalization fused into the quantizer: x~ = Q_a(Norm(x)).
+// Sparse-BitNet summary, section 3.4 (Algorithm 1 walk-through: the input is
+// normalized, RMSNorm in the BitNet architecture, then quantized); BitNet
+// b1.58 2B4T summary, section 3.2 (subln normalization, no bias terms).
+// The pages fix no arithmetic; this kernel defines it, per row:
+//   sq_k = fp32(x_k * x_k); lane l of the row's wavefront owns the 16-byte
+//   vectors l, l + 64, ... and adds their sq_k in fp64, vector by vector in
+//   element order; the 64 lane sums are combined by an xor butterfly
+//   (offsets 32, 16, ..., 1), so every lane holds the same S;
+//   r = fp32(1 / sqrt(S / K + eps_n))   (fp64 division, square root, division)
+//   z_k = fp32(fp32(x_k * r) * g_k)     (without g: z_k = fp32(x_k * r))
+// and then exactly the quantizer above on z. x is read once (plus g, which
+// stays in L2) and only the int8 codes are written: the HBM round trip of a
+// separate normalized tensor is gone.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ __forceinline__ void unpack_f32(const uint4& d, float* f) {
+  const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+  if constexpr (BF16) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      f[2 * h] = __uint_as_float(w[h] << 16);
+      f[2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) f[h] = __uint_as_float(w[h]);
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_rmsnorm_quant_act(const void* __restrict__ xv,
+                                                           const float* __restrict__ gain,
+                                                           int64_t T, int64_t K, int64_t ldx,
+                                                           float eps_n, float eps,
+                                                           int8_t* __restrict__ xq,
+                                                           float* __restrict__ sx) {
+  constexpr int V = BF16 ? 8 : 4;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * kActRowsPerBlock + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int64_t nvec = K / V;
+  const uint4* row = (const uint4*)((const char*)xv + t * ldx * (BF16 ? 2 : 4));
+  int8_t* qrow = xq + t * K;
+
+  uint4 d[kActCache];
+#pragma unroll
+  for (int u = 0; u < kActCache; ++u) {
+    const int64_t i = lane + 64 * u;
+    d[u] = i < nvec ? row[i] : make_uint4(0, 0, 0, 0);   // zeros add +0 to S
+  }
+  double S = 0.0;
+  auto add_sq = [&](const uint4& v) {
+    float f[V];
+    unpack_f32<BF16>(v, f);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const float p = f[e] * f[e];
+      S += (double)p;
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kActCache; ++u) add_sq(d[u]);
+  for (int64_t i = lane + 64 * kActCache; i < nvec; i += 64) add_sq(row[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) S = S + __shfl_xor(S, off, 64);
+  const float r = (float)(1.0 / sqrt(S / (double)K + (double)eps_n));
+
+  // z of vector i (V values)
+  auto norm = [&](const uint4& v, int64_t i, float* z) {
+    unpack_f32<BF16>(v, z);
+#pragma unroll
+    for (int e = 0; e < V; ++e) z[e] = z[e] * r;
+    if (gain) {
+#pragma unroll
+      for (int e4 = 0; e4 < V; e4 += 4) {
+        const float4 g4 = *(const float4*)(gain + i * V + e4);
+        z[e4] = z[e4] * g4.x;
+        z[e4 + 1] = z[e4 + 1] * g4.y;
+        z[e4 + 2] = z[e4 + 2] * g4.z;
+        z[e4 + 3] = z[e4 + 3] * g4.w;
+      }
+    }
+  };
+  uint32_t mx = 0;
+  float z[V];
+#pragma unroll
+  for (int u = 0; u < kActCache; ++u) {
+    const int64_t i = lane + 64 * u;
+    if (i < nvec) {
+      norm(d[u], i, z);
+#pragma unroll
+      for (int e = 0; e < V; ++e) mx = max(mx, __float_as_uint(z[e]) & 0x7FFFFFFFu);
+    }
+  }
+  for (int64_t i = lane + 64 * kActCache; i < nvec; i += 64) {
+    norm(row[i], i, z);
+#pragma unroll
+    for (int e = 0; e < V; ++e) mx = max(mx, __float_as_uint(z[e]) & 0x7FFFFFFFu);
+  }
+  mx = wave_max_u32(mx);
+  const ActScale sc = act_scale(mx, eps);
+  if (lane == 0) sx[t] = sc.s;
+  auto put = [&](int64_t i, const float* zz) {
+    uint32_t c[8];
+#pragma unroll
+    for (int e = 0; e < V; ++e) c[e] = act_code_bits(zz[e], sc.q);
+    if constexpr (BF16)
+      *(uint2*)(qrow + i * V) = make_uint2(pack_low_bytes(c[0], c[1], c[2], c[3]),
+                                           pack_low_bytes(c[4], c[5], c[6], c[7]));
+    else
+      *(uint32_t*)(qrow + i * V) = pack_low_bytes(c[0], c[1], c[2], c[3]);
+  };
+#pragma unroll
+  for (int u = 0; u < kActCache; ++u) {
+    const int64_t i = lane + 64 * u;
+    if (i < nvec) {
+      norm(d[u], i, z);
+      put(i, z);
+    }
+  }
+  for (int64_t i = lane + 64 * kActCache; i < nvec; i += 64) {
+    norm(row[i], i, z);
+    put(i, z);
+  }
+}
+
+hipError_t launch_rmsnorm_quant_act(const void* x, bool bf16, const float* gain, int64_t T,
+                                    int64_t K, int64_t ldx, float eps_n, float eps, int8_t* xq,
+                                    float* sx, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((unsigned)cdiv(T, kActRowsPerBlock)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(k_rmsnorm_quant_act<true>, grid, block, 0, s, x, gain, T, K, ldx, eps_n,
+                       eps, xq, sx);
+  else
+    hipLaunchKernelGGL(k_rmsnorm_quant_act<false>, grid, block, 0, s, x, gain, T, K, ldx, eps_n,
+                       eps, xq, sx);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t T, int64_t K, int64_t ldx,
                             float eps, int8_t* xq, float* sx, hipStream_t s) {
   if (T == 0) return hipSuccess;

@@ -111,6 +111,23 @@ sbl_status sbl_quant_act(const void* x, sbl_dtype xdt, int64_t T, int64_t K, int
                     "quant_act");
 }
 
+sbl_status sbl_rmsnorm_quant_act(const void* x, sbl_dtype xdt, const float* gain, int64_t T,
+                                 int64_t K, int64_t ldx, float eps_n, float eps_a, int8_t* xq,
+                                 float* sx, hipStream_t stream) {
+  if (!dtype_ok(xdt)) return SBL_ERR_DTYPE;
+  if (T < 0 || K < 1 || K > kMaxK || ldx < K) return SBL_ERR_SHAPE;
+  const int64_t es = xdt == SBL_BF16 ? 2 : 4, V = 16 / es;
+  if (K % V != 0 || (ldx * es) % 16 != 0) return SBL_ERR_SHAPE;
+  if (!eps_ok(eps_a) || !eps_ok(eps_n)) return SBL_ERR_VALUE;
+  if (T == 0) return SBL_OK;
+  if (!x || !xq || !sx) return SBL_ERR_NULL;
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(sx) || (gain && !aligned16(gain)))
+    return SBL_ERR_ALIGN;
+  return hip_status(launch_rmsnorm_quant_act(x, xdt == SBL_BF16, gain, T, K, ldx, eps_n, eps_a,
+                                             xq, sx, stream),
+                    "rmsnorm_quant_act");
+}
+
 sbl_status sbl_quant_mask_weight_workspace(int64_t O, int64_t K, size_t* bytes) {
   if (!bytes) return SBL_ERR_NULL;
   if (O < 1 || K < 1 || O * K >= (int64_t(1) << 31)) return SBL_ERR_SHAPE;

@@ -60,6 +60,11 @@ const DeviceInfo& device_info();  // cached per device
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t T, int64_t K, int64_t ldx,
                             float eps, int8_t* xq, float* sx, hipStream_t s);
 
+// x [T,K] with 16-byte aligned rows and K a multiple of the vector width
+hipError_t launch_rmsnorm_quant_act(const void* x, bool bf16, const float* gain, int64_t T,
+                                    int64_t K, int64_t ldx, float eps_n, float eps, int8_t* xq,
+                                    float* sx, hipStream_t s);
+
 // count in [1, kMaxPrepBatch]; every tensor of the batch shares dtype and N:M
 hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf16, int N, int M,
                                     float eps, void* ws, hipStream_t s);

@@ -52,6 +52,7 @@ def _load():
         "sbl_status_string": ([I], ctypes.c_char_p),
         "sbl_version": ([], ctypes.c_char_p),
         "sbl_quant_act": ([P, I, I64, I64, I64, F, P, P, P], I),
+        "sbl_rmsnorm_quant_act": ([P, I, P, I64, I64, I64, F, F, P, P, P], I),
         "sbl_quant_mask_weight_workspace": ([I64, I64, ctypes.POINTER(S)], I),
         "sbl_quant_mask_weight": ([P, I, I64, I64, I, I, F, P, P, P, P, P, P, S, P], I),
         "sbl_quant_mask_weight_batch_workspace": ([I, ctypes.POINTER(S)], I),
@@ -121,6 +122,20 @@ def sbl_quant_act(x: torch.Tensor, eps_a: float = 1e-5, xq=None, sx=None):
     sx = torch.empty((T,), dtype=torch.float32, device=x.device) if sx is None else sx
     _check("sbl_quant_act", _lib.sbl_quant_act(
         _ptr(x), _dt(x.dtype), T, K, x.stride(0), eps_a, _ptr(xq), _ptr(sx), _stream(x.device)))
+    return xq, sx
+
+
+def sbl_rmsnorm_quant_act(x: torch.Tensor, gain=None, eps_n: float = 1e-6, eps_a: float = 1e-5,
+                          xq=None, sx=None):
+    """x [T, K] bf16/fp32 (row stride x.stride(0)), gain [K] fp32 or None ->
+    (xq int8 [T, K], sx f32 [T]) of Q_a(RMSNorm(x) * gain)."""
+    assert x.dim() == 2 and x.stride(1) == 1
+    T, K = x.shape
+    xq = torch.empty((T, K), dtype=torch.int8, device=x.device) if xq is None else xq
+    sx = torch.empty((T,), dtype=torch.float32, device=x.device) if sx is None else sx
+    _check("sbl_rmsnorm_quant_act", _lib.sbl_rmsnorm_quant_act(
+        _ptr(x), _dt(x.dtype), _ptr(gain), T, K, x.stride(0), eps_n, eps_a, _ptr(xq), _ptr(sx),
+        _stream(x.device)))
     return xq, sx
 
 

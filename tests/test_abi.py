@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     for n in ["sbl_quant_act", "sbl_quant_mask_weight", "sbl_pack", "sbl_unpack", "sbl_gemm",
               "sbl_linear_fwd", "sbl_packed_bytes", "sbl_quant_mask_weight_workspace",
               "sbl_linear_fwd_workspace", "sbl_status_string", "sbl_version",
-              "sbl_quant_mask_weight_batch", "sbl_quant_mask_weight_batch_workspace"]:
+              "sbl_quant_mask_weight_batch", "sbl_quant_mask_weight_batch_workspace",
+              "sbl_rmsnorm_quant_act"]:
         assert n in names
 
 

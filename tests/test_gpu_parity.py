@@ -93,6 +93,39 @@ def test_quant_act_empty_and_errors(S):
         S.sbl_quant_act(torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda:0"), eps_a=0.0)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("T,K,gain", [(1, 896, True), (7, 4864, True), (64, 2048, False),
+                                      (3, 8200, True), (5, 16, False), (33, 20000, True)])
+def test_rmsnorm_quant_act_parity(S, dt, T, K, gain):
+    """Q_a(RMSNorm(x) * g) in one pass: codes and scales bit for bit against
+    the oracle (same fixed fp64 summation order), rows longer than the
+    register cache included."""
+    if dt == "fp32" and K % 4:
+        pytest.skip("K % 4")
+    log_case("rmsnorm_quant_act", dt, T, K, gain)
+    rng = np.random.default_rng(T * 7 + K)
+    x = (rng.standard_normal((T, K), dtype=np.float32) * np.float32(2.0)).astype(F32)
+    if dt == "bf16":
+        x = bf16_round(x)
+    g = (1 + 0.1 * rng.standard_normal(K)).astype(F32) if gain else None
+    xt = bf16_tensor(x) if dt == "bf16" else to_dev(x)
+    xq, sx = S.sbl_rmsnorm_quant_act(xt, to_dev(g) if gain else None, eps_n=1e-6)
+    rq, rs = o.rmsnorm_quant_act(x, g, 1e-6, 1e-5, 8 if dt == "bf16" else 4)
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(f32_bits(host(sx)), f32_bits(rs))
+
+
+def test_rmsnorm_quant_act_errors(S):
+    x = torch.zeros((4, 12), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(S.SblError):
+        S.sbl_rmsnorm_quant_act(x)                    # K % 8 != 0
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda:0")
+    with pytest.raises(S.SblError):
+        S.sbl_rmsnorm_quant_act(x, eps_n=0.0)
+    xq, sx = S.sbl_rmsnorm_quant_act(x[:0])
+    assert xq.shape == (0, 64)
+
+
 # ------------------------------------------------------ a2-a4: weight side --
 NM_ALL = [(n, 4) for n in range(1, 5)] + [(n, 8) for n in range(1, 9)]
 

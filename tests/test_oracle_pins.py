@@ -418,3 +418,47 @@ def test_mask_words_hand_layout():
     assert words.shape == (2, 4) and words.dtype == np.uint32
     assert words[0].tolist() == [0x80000001, 0x81, 0, 0]
     assert words[1].tolist() == [0x20, 0, 0, 0]
+
+
+# ------------------------------------------------------- Q_a(Norm(x)) ------
+def test_rms_scale_against_exact_sum():
+    """r against the exactly rounded sum of squares (math.fsum): the fixed
+    summation order costs at most a few fp64 ulps, invisible after the fp32
+    rounding except at rare ties; every term, K and eps placement pinned."""
+    rng = np.random.default_rng(11)
+    for (T, K, vec) in [(3, 64, 8), (5, 1000, 4), (2, 9000, 8)]:
+        x = rng.standard_normal((T, K)).astype(np.float32) * np.float32(3.0)
+        eps = 1e-6
+        r = o.rms_scale(x, eps, vec)
+        for t in range(T):
+            S = math.fsum(float(np.float32(v) * np.float32(v)) for v in x[t])
+            exact = 1.0 / math.sqrt(S / K + float(np.float32(eps)))
+            assert abs(float(r[t]) - exact) <= 1e-6 * exact
+
+
+def test_rmsnorm_quant_act_hand_example_and_unit_rms():
+    x = np.zeros((1, 8), np.float32)
+    x[0, :2] = [3.0, 4.0]                     # S = 25, mean 25/8
+    xq, sx = o.rmsnorm_quant_act(x, None, 1e-6, 1e-5, 8)
+    r = np.float32(1.0 / math.sqrt(25.0 / 8 + float(np.float32(1e-6))))
+    z = (x * r).astype(np.float32)
+    xq2, sx2 = o.quant_act(z)
+    assert np.array_equal(xq, xq2) and np.array_equal(sx, sx2)
+    assert xq[0, 1] == 127 and xq[0, 0] == round(127 * 3 / 4)
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((4, 512)).astype(np.float32)
+    r = o.rms_scale(x, 1e-12, 8)
+    z = x * r[:, None]
+    assert np.allclose(np.mean(z.astype(np.float64) ** 2, axis=1), 1.0, rtol=1e-5)
+
+
+def test_rmsnorm_quant_act_power_of_two_invariance():
+    """Scaling x by 2 and eps_n by 4 scales S and S/K + eps exactly: r halves
+    exactly, z and the codes are unchanged (with and without a gain)."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((6, 256)).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(256)).astype(np.float32)
+    for gain in (None, g):
+        a = o.rmsnorm_quant_act(x, gain, float(np.float32(1e-5)), 1e-5, 8)
+        b = o.rmsnorm_quant_act(2 * x, gain, 4 * float(np.float32(1e-5)), 1e-5, 8)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
