@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--fused-norm", action="store_true",
                    help="prefill: quantize each FFN input as Q_a(RMSNorm(x) * g) in one pass "
                         "(sbl_rmsnorm_quant_act) instead of Q_a(x)")
+    p.add_argument("--mask-from-ternary", action="store_true",
+                   help="prefill: the ablated recipe, mask ranked on the ternary codes")
     p.add_argument("--diagnostics", action="store_true",
                    help="prefill: the weight preparation also emits the mask diagnostics (keep bits, "
                         "flips against the previous step's mask, per-group pruning threshold)")
@@ -67,7 +69,7 @@ def parse():
 
 # ---------------------------------------------------------------- prefill --
 class PrefillStep:
-    def __init__(self, wl_name, N, M, diagnostics=False, fused_norm=False):
+    def __init__(self, wl_name, N, M, diagnostics=False, fused_norm=False, variant=0):
         wl = WORKLOADS[wl_name]
         self.wl, self.N, self.M, self.diag, self.norm = wl, N, M, diagnostics, fused_norm
         W, X = make_workload(wl_name)
@@ -107,7 +109,8 @@ class PrefillStep:
                 self.prep_items.append({
                     "w": self.W[l.name], "packed": self.packed[xn][off_p:off_p + nb],
                     "sw_rows": self.swr[xn][off_o:off_o + l.O],
-                    "gamma_sw": torch.empty(2, dtype=torch.float32, device=dev)})
+                    "gamma_sw": torch.empty(2, dtype=torch.float32, device=dev),
+                    "variant": variant})
                 off_p += nb
                 off_o += l.O
         if diagnostics:
@@ -430,7 +433,7 @@ def traffic_tag(a, N, M):
     if a.workload == "bitnet_decode":
         return f"bitnet_decode T={a.decode_T} L={a.layers}"
     return (f"{a.workload} T={WORKLOADS[a.workload].T} {N}:{M}" + (" diag" if a.diagnostics else "")
-            + (" norm" if a.fused_norm else ""))
+            + (" norm" if a.fused_norm else "") + (" ternary-mask" if a.mask_from_ternary else ""))
 
 
 def per_call_rates(step, per_call):
@@ -466,7 +469,8 @@ def main():
     if a.workload == "bitnet_decode":
         step = DecodeStep(a.decode_T, a.layers)
     else:
-        step = PrefillStep(a.workload, N, M, a.diagnostics, a.fused_norm)
+        step = PrefillStep(a.workload, N, M, a.diagnostics, a.fused_norm,
+                           1 if a.mask_from_ternary else 0)
     ms = time_steps(step, a.steps, a.warmup, a.eager)
     per_call, calls_per_step = per_call_times(step, max(5, min(a.steps, 20)))
     share = {k: per_call[k] * calls_per_step[k] for k in per_call}
@@ -497,6 +501,7 @@ def main():
         unit = "TOPS"
         config = {"workload": a.workload, "tokens": step.T, "nm": f"{N}:{M}",
                   "mask_diagnostics": bool(a.diagnostics), "fused_rmsnorm": bool(a.fused_norm),
+                  "mask_from": "ternary codes (ablation)" if a.mask_from_ternary else "master |W|",
                   "projections": [f"{l.name} {l.O}x{l.K}" for l in wl.linears],
                   "mask": "recomputed every step", "dense_equiv_ops_per_step": step.ops}
     out = {

@@ -41,7 +41,7 @@ __all__ = [
     "quant_mask_weight", "gemm_int", "gemm_int_bruteforce", "dequant",
     "to_bf16", "linear_fwd", "packed_row_bytes", "packed_bytes", "pack",
     "unpack", "INDEX_FORM", "mask_words", "mask_flips", "group_threshold",
-    "rms_scale", "rmsnorm_quant_act",
+    "rms_scale", "rmsnorm_quant_act", "dropped_max",
 ]
 
 F32 = np.float32
@@ -138,14 +138,24 @@ def apply_mask(codes: np.ndarray, mask: np.ndarray) -> np.ndarray:
     return (codes.astype(np.int8) * mask.astype(np.int8)).astype(np.int8)
 
 
-def quant_mask_weight(w: np.ndarray, N: int, M: int, eps_w: float = 1e-5):
+def quant_mask_weight(w: np.ndarray, N: int, M: int, eps_w: float = 1e-5,
+                      variant: str = "method"):
     """The whole weight side of the forward, in the order [SB] gives in
     "The Full Sparse-BitLinear Layer": mask from master |W|, gamma from the
     full unmasked W, RoundClip, then the mask applied to the ternary codes.
+
+    variant="ternary" is the ablation of [SB] "Where the mask is computed" /
+    Figure 3a: the mask is ranked on the ternary magnitudes |W_q| instead
+    (ties, which are the rule here, go to the lower index).
     Returns (w_eff int8, mask uint8, gamma f32, sw f32)."""
-    mask = nm_mask(w, N, M)
     gamma, sw = absmean(w, eps_w)
     codes = ternary_codes(w, sw)
+    if variant == "method":
+        mask = nm_mask(w, N, M)
+    elif variant == "ternary":
+        mask = nm_mask(np.abs(codes).astype(F32), N, M)
+    else:
+        raise ValueError(variant)
     return apply_mask(codes, mask), mask, gamma, sw
 
 
@@ -387,6 +397,17 @@ def mask_flips(mask_prev: np.ndarray, mask_cur: np.ndarray) -> int:
     b = np.asarray(mask_cur, dtype=np.uint8)
     assert a.shape == b.shape
     return int(np.count_nonzero(a != b))
+
+
+def dropped_max(w: np.ndarray, mask: np.ndarray, M: int) -> np.ndarray:
+    """Largest |w| among the dropped slots of each group of M under a given
+    mask (0 when nothing is dropped); equals group_threshold for the mask
+    ranked on |w|. float32 [O, K/M]."""
+    w = np.asarray(w, dtype=F32)
+    O, K = w.shape
+    a = np.where(np.asarray(mask).reshape(O, K // M, M) == 0, np.abs(w).reshape(O, K // M, M),
+                 F32(0))
+    return a.max(axis=2).astype(F32)
 
 
 def group_threshold(w: np.ndarray, N: int, M: int) -> np.ndarray:

@@ -189,6 +189,9 @@ sbl_status sbl_quant_mask_weight_batch(const sbl_weight_prep* items, int count, 
     t[i].prev_mask_bits = it.prev_mask_bits;
     t[i].flips = it.flips;
     t[i].group_thr = it.group_thr;
+    if (it.variant != SBL_PREP_METHOD && it.variant != SBL_PREP_MASK_FROM_TERNARY)
+      return SBL_ERR_VALUE;
+    t[i].variant = it.variant;
   }
   if (!ws) return SBL_ERR_WORKSPACE;
   if (ws_bytes < prep_workspace_bytes(count)) return SBL_ERR_WORKSPACE;

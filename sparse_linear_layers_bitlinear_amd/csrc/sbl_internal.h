@@ -49,6 +49,7 @@ struct PrepTensor {
   const uint32_t* prev_mask_bits = nullptr;
   unsigned long long* flips = nullptr;
   float* group_thr = nullptr;
+  int variant = 0;                           // 0: method; 1: mask ranked on |W_q|
 };
 
 struct DeviceInfo {

@@ -91,6 +91,7 @@ struct PrepItemK {
   const uint32_t* prev_mask_bits;
   unsigned long long* flips;
   float* group_thr;
+  int32_t variant, pad_v;
   int64_t O, K;
   int32_t C, pitch, code_chunks, mask_off;   // packed-record geometry
   int32_t part0, nparts;                     // its partial vectors (= its partial-pass blocks)
@@ -400,6 +401,20 @@ __global__ __launch_bounds__(kReduceThreads) void k_absmean_reduce(const PrepBat
 constexpr int kChunksPerBlock = 128;
 constexpr int kLdsStride = 36;   // words per staged chunk: 16-byte aligned, conflict-free
 
+// The n lowest set bits of v (n <= 8).
+__device__ __forceinline__ uint32_t lowest_bits(uint32_t v, int n) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i < n) {
+      const uint32_t b = v & (0u - v);
+      r |= b;
+      v ^= b;
+    }
+  }
+  return r;
+}
+
 // Keep bits of one group of M magnitudes (bit i = slot i kept):
 // rank_i = #{j : |w_j| > |w_i|} + #{j < i : |w_j| == |w_i|}; keep iff rank_i < N.
 // With c = [a_j > a_i] for a pair i < j: rank_i gains c and rank_j gains 1 - c,
@@ -613,12 +628,34 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
       keep |= kb << (g * M);
     }
   }
-  // mask diagnostics (need no scalar either)
+  __syncthreads();                                    // (2) scalars from the fifth wave
+  if (!active) return;
+  const PrepScalars sc = scal;
+  const uint32_t tb = sc.t_bits;
+  uint32_t nz = 0;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) nz |= ((tb - 1u - a[e]) >> 31) << e;   // a >= tb (both < 2^31, tb >= 1)
+  const uint32_t valid = k0 >= K32 ? 0u : (K32 - k0 >= 32u ? 0xFFFFFFFFu : ((1u << (K32 - k0)) - 1u));
+  if (pi.variant == 1) {
+    // ablation: rank the ternary magnitudes |W_q| -- the nonzero codes first,
+    // then the zero codes, each in index order
+    constexpr uint32_t MM = (1u << M) - 1u;
+    keep = 0;
+#pragma unroll
+    for (int g = 0; g < 32 / M; ++g) {
+      const uint32_t z = (nz >> (g * M)) & MM;
+      const int cnt = __popc(z);
+      const uint32_t kg = cnt >= N ? lowest_bits(z, N) : (z | lowest_bits(~z & MM, N - cnt));
+      keep |= kg << (g * M);
+    }
+  }
+  // mask diagnostics
   {
     const uint32_t vbits = k0 >= K32 ? 0u : (K32 - k0 >= 32u ? 0xFFFFFFFFu : ((1u << (K32 - k0)) - 1u));
-    if (pi.mask_bits && active) pi.mask_bits[(int64_t)o * C + c] = keep & vbits;
-    if (pi.group_thr && active) {
-      // (N+1)-th largest |w| of each group = the largest dropped magnitude
+    if (pi.mask_bits) pi.mask_bits[(int64_t)o * C + c] = keep & vbits;
+    if (pi.group_thr) {
+      // largest dropped magnitude of each group (the (N+1)-th largest |w|
+      // when the mask is ranked on |w|)
       constexpr int G = 32 / M;
       float* const thr = pi.group_thr + (int64_t)o * (K / M) + (int64_t)c * G;
 #pragma unroll
@@ -631,14 +668,6 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
       }
     }
   }
-  __syncthreads();                                    // (2) scalars from the fifth wave
-  if (!active) return;
-  const PrepScalars sc = scal;
-  const uint32_t tb = sc.t_bits;
-  uint32_t nz = 0;
-#pragma unroll
-  for (int e = 0; e < 32; ++e) nz |= ((tb - 1u - a[e]) >> 31) << e;   // a >= tb (both < 2^31, tb >= 1)
-  const uint32_t valid = k0 >= K32 ? 0u : (K32 - k0 >= 32u ? 0xFFFFFFFFu : ((1u << (K32 - k0)) - 1u));
   const uint32_t kn = nz & keep & valid;          // nonzero code, kept
   const uint32_t kneg = kn & sgn;                 // ... and negative
 
@@ -720,6 +749,8 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
     k.prev_mask_bits = t.prev_mask_bits;
     k.flips = t.flips;
     k.group_thr = t.group_thr;
+    k.variant = t.variant;
+    k.pad_v = 0;
     k.O = t.O;
     k.K = t.K;
     k.C = (int32_t)row_chunks(t.K);

@@ -35,10 +35,11 @@ class WeightPrep(ctypes.Structure):
                 ("packed", ctypes.c_void_p), ("gamma_sw", ctypes.c_void_p),
                 ("sw_rows", ctypes.c_void_p), ("mask_bits", ctypes.c_void_p),
                 ("prev_mask_bits", ctypes.c_void_p), ("flips", ctypes.c_void_p),
-                ("group_thr", ctypes.c_void_p)]
+                ("group_thr", ctypes.c_void_p), ("variant", ctypes.c_int32)]
 
 
 SBL_MAX_PREP_BATCH = 8
+SBL_PREP_METHOD, SBL_PREP_MASK_FROM_TERNARY = 0, 1
 
 
 def _load():
@@ -175,7 +176,8 @@ def sbl_quant_mask_weight_batch(items, N: int, M: int, eps_w: float = 1e-5, ws=N
     here when absent: gamma_sw always, packed unless want_packed=False), and
     the optional mask diagnostics mask_bits, prev_mask_bits + flips, group_thr
     (want_mask_bits / want_group_thr allocate them; flips is allocated when
-    prev_mask_bits is given). Returns the list of dicts with every output."""
+    prev_mask_bits is given), and variant (SBL_PREP_METHOD or
+    SBL_PREP_MASK_FROM_TERNARY). Returns the list of dicts with every output."""
     assert 1 <= len(items) <= SBL_MAX_PREP_BATCH
     dev = items[0]["w"].device
     dt = items[0]["w"].dtype
@@ -206,7 +208,8 @@ def sbl_quant_mask_weight_batch(items, N: int, M: int, eps_w: float = 1e-5, ws=N
             o.setdefault(k, None)
         arr[i] = WeightPrep(_ptr(w), O, K, _ptr(o["w_eff"]), _ptr(o["mask"]), _ptr(o["packed"]),
                             _ptr(o["gamma_sw"]), _ptr(o["sw_rows"]), _ptr(o["mask_bits"]),
-                            _ptr(o["prev_mask_bits"]), _ptr(o["flips"]), _ptr(o["group_thr"]))
+                            _ptr(o["prev_mask_bits"]), _ptr(o["flips"]), _ptr(o["group_thr"]),
+                            int(o.get("variant", SBL_PREP_METHOD)))
         outs.append(o)
     nws = sbl_quant_mask_weight_batch_workspace(len(items))
     if ws is None:

@@ -166,6 +166,9 @@ def test_weight_batch_validation(S):
     diag[0].flips = FAKE
     assert call(diag, 1) == 1
     diag = items(ok)
+    diag[0].variant = 7                                           # unknown recipe
+    assert call(diag, 1) == 8
+    diag = items(ok)
     diag[0].group_thr = MIS                                       # misaligned diagnostics output
     assert call(diag, 1) == 5
     n = ctypes.c_size_t()

@@ -223,6 +223,37 @@ def test_mask_diagnostics_parity(S, N, M, dt):
         assert int(host(r["flips"])[0]) == o.mask_flips(o.nm_mask(W0, N, M), o.nm_mask(W1, N, M))
 
 
+@pytest.mark.parametrize("N,M", [(6, 8), (2, 4), (3, 8), (5, 8), (1, 4)])
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+def test_mask_from_ternary_variant_parity(S, N, M, dt):
+    """The ablated recipe (mask ranked on |W_q|): mask, codes, packing and the
+    diagnostics against the oracle; the method's prep of the same W differs."""
+    shapes = [(37, 264), (64, 1024), (5, 8)]
+    shapes = [(O, K) for O, K in shapes if K % M == 0]
+    log_case("mask from ternary", N, M, dt, shapes)
+    Ws, items = [], []
+    for i, (O, K) in enumerate(shapes):
+        W, _ = make_linear_inputs(1, O, K, seed=3000 + i + N)
+        if dt == "bf16":
+            W = bf16_round(W)
+        Ws.append(W)
+        items.append({"w": bf16_tensor(W) if dt == "bf16" else to_dev(W), "variant": 1,
+                      "w_eff": torch.empty((O, K), dtype=torch.int8, device="cuda:0"),
+                      "mask": torch.empty((O, K), dtype=torch.uint8, device="cuda:0"),
+                      "want_mask_bits": True, "want_group_thr": True})
+    outs = S.sbl_quant_mask_weight_batch(items, N, M)
+    differs = False
+    for W, r in zip(Ws, outs):
+        w_eff, mask, gamma, sw = o.quant_mask_weight(W, N, M, variant="ternary")
+        assert np.array_equal(host(r["mask"]), mask)
+        assert np.array_equal(host(r["w_eff"]), w_eff)
+        assert np.array_equal(host(r["packed"]).reshape(W.shape[0], -1), o.pack(w_eff, mask, N, M))
+        assert np.array_equal(host(r["mask_bits"]).view(np.uint32), o.mask_words(mask))
+        assert np.array_equal(f32_bits(host(r["group_thr"])), f32_bits(o.dropped_max(W, mask, M)))
+        differs |= not np.array_equal(mask, o.nm_mask(W, N, M))
+    assert differs
+
+
 def test_quant_mask_weight_batch_full_size(S):
     """The three projections of the Qwen2.5-0.5B FFN prepared in one batch
     (K differs between them), as the benchmark step does."""

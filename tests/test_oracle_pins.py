@@ -143,6 +143,15 @@ def test_master_vs_ternary_worked_example(golden_dir):
     assert not np.array_equal(m_t, mask)
     # quant-then-mask: W_eff keeps the zero code at the kept slot 5
     assert w_eff[0].tolist() == [1, -1, 1, 0, 1, 0, -1, 0]
+    # the ablated recipe of the weight side gives exactly that ternary-ranked mask
+    w2, m2, g2, sw2 = o.quant_mask_weight(w, N, M, 1e-5, variant="ternary")
+    assert m2[0].tolist() == ex["expected_mask_from_ternary_lower_index_ties"]
+    assert g2 == gamma and sw2 == sw
+    assert w2[0].tolist() == (codes * m2)[0].tolist()
+    # largest dropped magnitude: 0.2 (slot 7) under the master mask, 0.3 under the ternary one
+    assert o.dropped_max(w, mask, M)[0].tolist() == [np.float32(0.2)]
+    assert o.dropped_max(w, m2, M)[0].tolist() == [np.float32(0.3)]
+    assert np.array_equal(o.dropped_max(w, mask, M), o.group_threshold(w, N, M))
 
 
 # ------------------------------------------------------------ absmean (a2) --
