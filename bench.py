@@ -59,6 +59,8 @@ def parse():
                         "(sbl_rmsnorm_quant_act) instead of Q_a(x)")
     p.add_argument("--mask-from-ternary", action="store_true",
                    help="prefill: the ablated recipe, mask ranked on the ternary codes")
+    p.add_argument("--mask-then-quant", action="store_true",
+                   help="prefill: the composition-order ablation, gamma over the kept weights only")
     p.add_argument("--diagnostics", action="store_true",
                    help="prefill: the weight preparation also emits the mask diagnostics (keep bits, "
                         "flips against the previous step's mask, per-group pruning threshold)")
@@ -433,7 +435,8 @@ def traffic_tag(a, N, M):
     if a.workload == "bitnet_decode":
         return f"bitnet_decode T={a.decode_T} L={a.layers}"
     return (f"{a.workload} T={WORKLOADS[a.workload].T} {N}:{M}" + (" diag" if a.diagnostics else "")
-            + (" norm" if a.fused_norm else "") + (" ternary-mask" if a.mask_from_ternary else ""))
+            + (" norm" if a.fused_norm else "") + (" ternary-mask" if a.mask_from_ternary else "")
+            + (" mask-then-quant" if a.mask_then_quant else ""))
 
 
 def per_call_rates(step, per_call):
@@ -466,11 +469,13 @@ def main():
     N, M = wl.N, wl.M
     if a.nm:
         N, M = (int(v) for v in a.nm.split(":"))
+    if a.mask_from_ternary and a.mask_then_quant:
+        sys.exit("bench.py: --mask-from-ternary and --mask-then-quant are two separate ablations")
     if a.workload == "bitnet_decode":
         step = DecodeStep(a.decode_T, a.layers)
     else:
         step = PrefillStep(a.workload, N, M, a.diagnostics, a.fused_norm,
-                           1 if a.mask_from_ternary else 0)
+                           1 if a.mask_from_ternary else 2 if a.mask_then_quant else 0)
     ms = time_steps(step, a.steps, a.warmup, a.eager)
     per_call, calls_per_step = per_call_times(step, max(5, min(a.steps, 20)))
     share = {k: per_call[k] * calls_per_step[k] for k in per_call}
@@ -502,6 +507,7 @@ def main():
         config = {"workload": a.workload, "tokens": step.T, "nm": f"{N}:{M}",
                   "mask_diagnostics": bool(a.diagnostics), "fused_rmsnorm": bool(a.fused_norm),
                   "mask_from": "ternary codes (ablation)" if a.mask_from_ternary else "master |W|",
+                  "composition": "mask-then-quant (ablation)" if a.mask_then_quant else "quant-then-mask",
                   "projections": [f"{l.name} {l.O}x{l.K}" for l in wl.linears],
                   "mask": "recomputed every step", "dense_equiv_ops_per_step": step.ops}
     out = {

@@ -177,13 +177,18 @@ typedef struct sbl_weight_prep {
    * computed" and the Figure 3a ablations): SBL_PREP_METHOD (0) ranks the mask
    * on the master magnitudes |W| -- the method; SBL_PREP_MASK_FROM_TERNARY (1)
    * ranks it on the ternary magnitudes |W_q| (ties: lower index first), the
-   * ablated variant. gamma covers all of W in both. group_thr is then the
-   * largest dropped |w| of each group under the mask actually used. */
+   * ablated variant; gamma covers all of W in both. SBL_PREP_MASK_THEN_QUANT
+   * (2), the composition-order ablation (section 3.4 "Composition Order"),
+   * keeps the master-ranked mask but takes gamma over the kept weights only:
+   * gamma = fp32(RN_fp64(sum of kept |w|) / (O * K/M * N)); a batch is either
+   * all of variant 2 or has none. group_thr is the largest dropped |w| of each
+   * group under the mask actually used. */
   int32_t variant;
 } sbl_weight_prep;
 
 #define SBL_PREP_METHOD 0
 #define SBL_PREP_MASK_FROM_TERNARY 1
+#define SBL_PREP_MASK_THEN_QUANT 2
 
 #define SBL_MAX_PREP_BATCH 8
 
@@ -205,7 +210,8 @@ sbl_status sbl_quant_mask_weight_batch_workspace(int count, size_t* bytes);
  * Errors: as sbl_quant_mask_weight, checked for every item before anything
  * is enqueued; count out of range -> SBL_ERR_SHAPE; prev_mask_bits, flips
  * and mask_bits not all given when either of the first two is -> SBL_ERR_NULL;
- * an unknown variant -> SBL_ERR_VALUE.
+ * an unknown variant, or variant 2 mixed with others in one batch ->
+ * SBL_ERR_VALUE.
  */
 sbl_status sbl_quant_mask_weight_batch(const sbl_weight_prep* items, int count, sbl_dtype wdt,
                                        int N, int M, float eps_w, void* ws, size_t ws_bytes,

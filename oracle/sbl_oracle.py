@@ -147,7 +147,18 @@ def quant_mask_weight(w: np.ndarray, N: int, M: int, eps_w: float = 1e-5,
     variant="ternary" is the ablation of [SB] "Where the mask is computed" /
     Figure 3a: the mask is ranked on the ternary magnitudes |W_q| instead
     (ties, which are the rule here, go to the lower index).
+
+    variant="mask_then_quant" is the ablation of [SB] "Composition Order":
+    W_eff = Q_t(W (.) M) -- the same master-ranked mask, but gamma is the mean
+    |w| over the kept (Top-N) weights only, n = O * K/M * N, then RoundClip
+    of the masked weight (pruned entries are 0 and stay 0).
     Returns (w_eff int8, mask uint8, gamma f32, sw f32)."""
+    if variant == "mask_then_quant":
+        mask = nm_mask(w, N, M)
+        w = np.asarray(w, dtype=F32)
+        gamma, sw = absmean(w[mask == 1], eps_w)
+        w_masked = np.where(mask == 1, w, F32(0.0)).astype(F32)
+        return ternary_codes(w_masked, sw), mask, gamma, sw
     gamma, sw = absmean(w, eps_w)
     codes = ternary_codes(w, sw)
     if variant == "method":

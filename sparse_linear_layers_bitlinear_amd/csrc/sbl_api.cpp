@@ -189,7 +189,11 @@ sbl_status sbl_quant_mask_weight_batch(const sbl_weight_prep* items, int count, 
     t[i].prev_mask_bits = it.prev_mask_bits;
     t[i].flips = it.flips;
     t[i].group_thr = it.group_thr;
-    if (it.variant != SBL_PREP_METHOD && it.variant != SBL_PREP_MASK_FROM_TERNARY)
+    if (it.variant != SBL_PREP_METHOD && it.variant != SBL_PREP_MASK_FROM_TERNARY &&
+        it.variant != SBL_PREP_MASK_THEN_QUANT)
+      return SBL_ERR_VALUE;
+    // mask-then-quant changes the partial pass for the whole batch
+    if ((it.variant == SBL_PREP_MASK_THEN_QUANT) != (items[0].variant == SBL_PREP_MASK_THEN_QUANT))
       return SBL_ERR_VALUE;
     t[i].variant = it.variant;
   }

@@ -493,6 +493,96 @@ __device__ __forceinline__ uint32_t byte_slice16(uint32_t lo, uint32_t hi) {
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// Mask-then-quant (ablation, variant 2): gamma over the kept weights only.
+// Sparse-BitNet summary, section 3.4 "Composition Order": W_eff =
+// Q_t(W (.) M), whose scale comes from the Top-N active weights alone. The
+// partial pass then needs the mask: one thread per 32-wide chunk (as in the
+// mask pass) forms the keep bits with the same rank rule and adds exactly the
+// kept |w| -- the same 96-bit window accumulator and LDS bins as
+// k_absmean_partial, the same 16 partials per block. `vec`: every row starts
+// 16-byte aligned, so whole chunks are read with 16-byte loads.
+// ---------------------------------------------------------------------------
+template <bool BF16, int M, int SEL>
+__global__ __launch_bounds__(kAbsThreads) void k_absmean_partial_kept(
+    const PrepBatchK batch, int N, bool vec, unsigned long long* __restrict__ partials_all) {
+  const int item = prep_index(batch, blockIdx.x, false);
+  const PrepItemK pi = prep_item(batch, item);
+  const void* __restrict__ wv = pi.w;
+  const uint32_t lb = blockIdx.x - pi.blk1, nblk = pi.nparts;
+  unsigned long long* __restrict__ partials = partials_all + (int64_t)pi.part0 * 16;
+  __shared__ unsigned long long bins[16];
+  if (threadIdx.x < 16) bins[threadIdx.x] = 0;
+  __syncthreads();
+  const uint32_t C32 = (uint32_t)pi.C, K32 = (uint32_t)pi.K;
+  const uint32_t total = (uint32_t)(pi.O * pi.C);
+  uint32_t a0 = 0, a1 = 0, a2 = 0;
+  for (uint32_t ch = lb * kAbsThreads + threadIdx.x; ch < total; ch += nblk * kAbsThreads) {
+    const uint32_t o = ch / C32, c = ch - o * C32, k0 = 32u * c;
+    uint32_t a[32];
+    const int64_t row = (int64_t)o * pi.K + k0;
+    if (vec && k0 + 32u <= K32) {
+      constexpr int NV = BF16 ? 4 : 8;             // 16-byte vectors per chunk
+      const uint4* src = (const uint4*)((const char*)wv + row * (BF16 ? 2 : 4));
+      uint4 d[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) d[v] = src[v];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const uint32_t w4[4] = {d[v].x, d[v].y, d[v].z, d[v].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          if constexpr (BF16) {
+            a[8 * v + 2 * h] = (w4[h] << 16) & 0x7FFFFFFFu;
+            a[8 * v + 2 * h + 1] = w4[h] & 0x7FFF0000u;
+          } else {
+            a[4 * v + h] = w4[h] & 0x7FFFFFFFu;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const uint32_t k = k0 + (uint32_t)e;
+        uint32_t u = 0;
+        if (k < K32)
+          u = BF16 ? ((uint32_t)((const uint16_t*)wv)[row + e] << 16) : ((const uint32_t*)wv)[row + e];
+        a[e] = u & 0x7FFFFFFFu;
+      }
+    }
+    uint32_t keep = 0;
+#pragma unroll
+    for (int g = 0; g < 32 / M; ++g) {
+      uint32_t kb;
+      if constexpr (SEL == 1) kb = drop_low_keep_bits8<1>(a + g * M);
+      else if constexpr (SEL == 2) kb = drop_low_keep_bits8<2>(a + g * M);
+      else if constexpr (SEL == 3) kb = 0xFFu;
+      else kb = topn_keep_bits<M>(a + g * M, N);
+      keep |= kb << (g * M);
+    }
+    bool other = false;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const uint32_t u = ((keep >> e) & 1u) ? a[e] : 0u;    // dropped slots add nothing
+      add96(a0, a1, a2, abs_term3(u, other));
+    }
+    if (other) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e)
+        if ((keep >> e) & 1u) abs_accumulate_other(bins, a[e]);
+    }
+  }
+  const unsigned long long lo = a0;
+  const unsigned long long hi = (unsigned long long)a1 | ((unsigned long long)a2 << 32);
+  const unsigned long long slo = wave_sum_u64(lo), shi = wave_sum_u64(hi);
+  if ((threadIdx.x & 63) == 0) {
+    atomicAdd(&bins[2 * kAbsWindow], slo);
+    atomicAdd(&bins[2 * kAbsWindow + 1], shi);
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) partials[(int64_t)lb * 16 + threadIdx.x] = bins[threadIdx.x];
+}
+
 // Workgroup: one thread per chunk and one more wave that turns the summed
 // absmean bins into gamma, sw and the threshold (a serial computation) while
 // the others stage W and rank the groups; the threshold is needed only for
@@ -529,7 +619,8 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
     __builtin_amdgcn_wave_barrier();
     __syncthreads();                                    // (1) W staged by the other waves
     if (lane == 0) {
-      const PrepScalars sc = scalars_from_bins(red, O * K, eps);
+      const int64_t n = pi.variant == 2 ? O * (K / M) * N : O * K;   // kept weights only
+      const PrepScalars sc = scalars_from_bins(red, n, eps);
       scal = sc;
       if (lb == 0) {
         gamma_sw[0] = sc.gamma;
@@ -759,7 +850,9 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
     k.mask_off = (int32_t)dense_code_bytes(t.K);
     // about one batch of loads per thread (the exact accumulation is VALU
     // work: spread it over many waves)
-    const int64_t want = cdiv(cdiv(t.O * t.K, V), (int64_t)kAbsThreads * kAbsBatch);
+    // (variant 2: one chunk of 32 per thread and step)
+    const int64_t want = t.variant == 2 ? cdiv(t.O * (int64_t)row_chunks(t.K), (int64_t)kAbsThreads)
+                                        : cdiv(cdiv(t.O * t.K, V), (int64_t)kAbsThreads * kAbsBatch);
     const int nb = (int)(want < 1 ? 1 : (want > cap ? cap : want));
     k.part0 = parts;
     k.nparts = nb;
@@ -770,10 +863,25 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
   }
   auto* partials = (unsigned long long*)ws;
   auto* bins = partials + (size_t)kAbsmeanMaxBlocks * 16;
-  if (bf16)
+  if (items[0].variant == 2) {   // a batch is all of variant 2 or none (checked by the caller)
+    bool vec = true;               // (w itself is 16-byte aligned)
+    for (int i = 0; i < count; ++i) vec = vec && (items[i].K * (bf16 ? 2 : 4)) % 16 == 0;
+#define SBL_KEPT(BV, MV, SV) \
+    hipLaunchKernelGGL((k_absmean_partial_kept<BV, MV, SV>), dim3(parts), dim3(kAbsThreads), 0, s, b, N, vec, partials)
+#define SBL_KEPT_NM(BV)                                             \
+    if (M == 4) SBL_KEPT(BV, 4, 0);                                   \
+    else if (N == 8) SBL_KEPT(BV, 8, 3);                              \
+    else if (N == 7) SBL_KEPT(BV, 8, 1);                              \
+    else if (N == 6) SBL_KEPT(BV, 8, 2);                              \
+    else SBL_KEPT(BV, 8, 0)
+    if (bf16) { SBL_KEPT_NM(true); } else { SBL_KEPT_NM(false); }
+#undef SBL_KEPT_NM
+#undef SBL_KEPT
+  } else if (bf16) {
     hipLaunchKernelGGL((k_absmean_partial<true>), dim3(parts), dim3(kAbsThreads), 0, s, b, partials);
-  else
+  } else {
     hipLaunchKernelGGL((k_absmean_partial<false>), dim3(parts), dim3(kAbsThreads), 0, s, b, partials);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_absmean_reduce, dim3(count), dim3(kReduceThreads), 0, s, b, partials, bins);

@@ -39,7 +39,7 @@ class WeightPrep(ctypes.Structure):
 
 
 SBL_MAX_PREP_BATCH = 8
-SBL_PREP_METHOD, SBL_PREP_MASK_FROM_TERNARY = 0, 1
+SBL_PREP_METHOD, SBL_PREP_MASK_FROM_TERNARY, SBL_PREP_MASK_THEN_QUANT = 0, 1, 2
 
 
 def _load():
@@ -176,8 +176,9 @@ def sbl_quant_mask_weight_batch(items, N: int, M: int, eps_w: float = 1e-5, ws=N
     here when absent: gamma_sw always, packed unless want_packed=False), and
     the optional mask diagnostics mask_bits, prev_mask_bits + flips, group_thr
     (want_mask_bits / want_group_thr allocate them; flips is allocated when
-    prev_mask_bits is given), and variant (SBL_PREP_METHOD or
-    SBL_PREP_MASK_FROM_TERNARY). Returns the list of dicts with every output."""
+    prev_mask_bits is given), and variant (SBL_PREP_METHOD,
+    SBL_PREP_MASK_FROM_TERNARY, or SBL_PREP_MASK_THEN_QUANT for every item of
+    the batch). Returns the list of dicts with every output."""
     assert 1 <= len(items) <= SBL_MAX_PREP_BATCH
     dev = items[0]["w"].device
     dt = items[0]["w"].dtype

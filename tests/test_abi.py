@@ -168,6 +168,9 @@ def test_weight_batch_validation(S):
     diag = items(ok)
     diag[0].variant = 7                                           # unknown recipe
     assert call(diag, 1) == 8
+    diag = items(ok, ok)
+    diag[1].variant = 2                                           # mask-then-quant mixed in
+    assert call(diag, 2) == 8
     diag = items(ok)
     diag[0].group_thr = MIS                                       # misaligned diagnostics output
     assert call(diag, 1) == 5

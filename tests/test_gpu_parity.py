@@ -254,6 +254,56 @@ def test_mask_from_ternary_variant_parity(S, N, M, dt):
     assert differs
 
 
+@pytest.mark.parametrize("N,M", [(6, 8), (2, 4), (7, 8), (8, 8), (3, 8), (1, 4)])
+@pytest.mark.parametrize("dt", ["fp32", "bf16"])
+def test_mask_then_quant_variant_parity(S, N, M, dt):
+    """The composition-order ablation (gamma over the kept weights): gamma and
+    sw bit for bit, codes, mask, packing and the dropped maximum against the
+    oracle, in one batch of ragged shapes; the last item spans a wide exponent
+    range so the exact sum leaves its main window. K = 100 (M = 4 only) leaves
+    bf16 rows unaligned, so that batch takes the element-wise loads."""
+    shapes = [(37, 264), (64, 1024), (5, 8), (11, 100), (19, 72)]
+    shapes = [(O, K) for O, K in shapes if K % M == 0]
+    log_case("mask then quant", N, M, dt, shapes)
+    rng = np.random.default_rng(77 + N)
+    Ws, items = [], []
+    for i, (O, K) in enumerate(shapes):
+        W, _ = make_linear_inputs(1, O, K, seed=4000 + i + N)
+        if i == len(shapes) - 1:
+            W = (W * np.exp2(rng.integers(-60, 60, W.shape))).astype(np.float32)
+        if dt == "bf16":
+            W = bf16_round(W)
+        Ws.append(W)
+        items.append({"w": bf16_tensor(W) if dt == "bf16" else to_dev(W), "variant": 2,
+                      "w_eff": torch.empty((O, K), dtype=torch.int8, device="cuda:0"),
+                      "mask": torch.empty((O, K), dtype=torch.uint8, device="cuda:0"),
+                      "want_group_thr": True})
+    outs = S.sbl_quant_mask_weight_batch(items, N, M)
+    for W, r in zip(Ws, outs):
+        w_eff, mask, gamma, sw = o.quant_mask_weight(W, N, M, variant="mask_then_quant")
+        gs = host(r["gamma_sw"])
+        assert f32_bits(gs[0]) == f32_bits(gamma) and f32_bits(gs[1]) == f32_bits(sw)
+        assert np.array_equal(host(r["mask"]), mask)
+        assert np.array_equal(host(r["w_eff"]), w_eff)
+        assert np.array_equal(host(r["packed"]).reshape(W.shape[0], -1), o.pack(w_eff, mask, N, M))
+        assert np.array_equal(f32_bits(host(r["group_thr"])), f32_bits(o.dropped_max(W, mask, M)))
+
+
+def test_mask_then_quant_full_size(S):
+    """The Qwen2.5-0.5B FFN projections under mask-then-quant, one batch."""
+    from sparse_linear_layers_bitlinear_amd.workloads import WORKLOADS, make_workload
+    log_case("mask then quant full", "qwen05b_ffn")
+    wl = WORKLOADS["qwen05b_ffn"]
+    W, _ = make_workload("qwen05b_ffn")
+    items = [{"w": to_dev(W[l.name]), "variant": 2} for l in wl.linears]
+    outs = S.sbl_quant_mask_weight_batch(items, wl.N, wl.M)
+    for l, r in zip(wl.linears, outs):
+        w_eff, mask, gamma, sw = o.quant_mask_weight(W[l.name], wl.N, wl.M, variant="mask_then_quant")
+        gs = host(r["gamma_sw"])
+        assert f32_bits(gs[0]) == f32_bits(gamma) and f32_bits(gs[1]) == f32_bits(sw)
+        assert np.array_equal(host(r["packed"]).reshape(l.O, -1), o.pack(w_eff, mask, wl.N, wl.M))
+
+
 def test_quant_mask_weight_batch_full_size(S):
     """The three projections of the Qwen2.5-0.5B FFN prepared in one batch
     (K differs between them), as the benchmark step does."""

@@ -154,6 +154,42 @@ def test_master_vs_ternary_worked_example(golden_dir):
     assert np.array_equal(o.dropped_max(w, mask, M), o.group_threshold(w, N, M))
 
 
+def test_mask_then_quant_worked_example(golden_dir):
+    ex = json.load(open(os.path.join(golden_dir, "composition_order.json")))
+    w = np.array([ex["w_master"]], np.float32)
+    N, M = ex["N"], ex["M"]
+    q_eff, q_mask, q_gamma, _ = o.quant_mask_weight(w, N, M, 1e-5)
+    m_eff, m_mask, m_gamma, m_sw = o.quant_mask_weight(w, N, M, 1e-5, variant="mask_then_quant")
+    assert q_mask[0].tolist() == ex["expected_mask"] and np.array_equal(m_mask, q_mask)
+    assert q_gamma == F32(0.4609375) and m_gamma == F32(0.875)
+    assert m_sw == F32(F32(0.875) + F32(1e-5))
+    assert q_eff[0].tolist() == ex["expected_w_eff_quant_then_mask"]
+    assert m_eff[0].tolist() == ex["expected_w_eff_mask_then_quant"]
+
+
+def test_mask_then_quant_properties():
+    """gamma over the Top-N of each group is at least the full mean (each
+    group's Top-N mean is at least its mean); the exact rational mean of the
+    kept |w|; RoundClip is monotone in 1/sw, so the nonzero codes are a subset
+    of quant-then-mask's; N = M keeps all and reduces to the method."""
+    rng = np.random.default_rng(31)
+    for N, M, K in [(2, 4, 64), (6, 8, 96), (5, 8, 40), (1, 4, 32)]:
+        w = (rng.standard_normal((9, K)) * 0.02).astype(np.float32)
+        q_eff, q_mask, q_gamma, _ = o.quant_mask_weight(w, N, M)
+        m_eff, m_mask, m_gamma, m_sw = o.quant_mask_weight(w, N, M, variant="mask_then_quant")
+        assert np.array_equal(m_mask, q_mask)
+        assert m_gamma >= q_gamma
+        g, sw = _gamma_exact(w[q_mask == 1], 1e-5)
+        assert m_gamma == g and m_sw == sw
+        assert np.all(m_eff[q_mask == 0] == 0)
+        assert np.all((m_eff != 0) <= (q_eff != 0))
+        assert np.all(m_eff[m_eff != 0] == q_eff[m_eff != 0])
+        assert (m_eff != 0).sum() < (q_eff != 0).sum()       # strictly sparser here
+    w = (rng.standard_normal((5, 64)) * 0.02).astype(np.float32)
+    for a, b in zip(o.quant_mask_weight(w, 8, 8), o.quant_mask_weight(w, 8, 8, variant="mask_then_quant")):
+        assert np.array_equal(a, b)
+
+
 # ------------------------------------------------------------ absmean (a2) --
 def _gamma_exact(w, eps):
     S = sum((Fraction(float(v)) for v in np.abs(w.astype(np.float64)).ravel()),
