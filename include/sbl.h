@@ -268,6 +268,60 @@ sbl_status sbl_linear_fwd(const void* x, sbl_dtype xdt, const void* w_master, sb
                           int64_t T, int64_t O, int64_t K, int N, int M, float eps_a, float eps_w,
                           void* y, sbl_dtype ydt, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Backward of the layer under the Dual straight-through estimator
+ * (Sparse-BitNet summary, section 3.4 "Gradient Estimation: The Dual
+ * Straight-Through Estimator" and the backward steps of the Algorithm 1
+ * walk-through; Algorithm 2's WeightQuantMasked hands its output gradient
+ * back unchanged). The forward is y = x~ W~^T with x~ = sx * xq (the
+ * dequantized activation) and W~ = sw * W_eff, so
+ *   dX = dY W~      -- the gradient at x~, which the STE of Q_a passes to x;
+ *   dW = dY^T x~    -- the gradient at W~, which the Dual STE passes to every
+ *                      master weight, kept or pruned, with no clip window.
+ * Both contractions run on the bf16 matrix cores with fp32 accumulation; dY
+ * is bf16 (the training dtype of the pages) and x~ enters dW as bf16 (see
+ * sbl_act_dequant). Shapes: O % 8 == 0 and K % 8 == 0 (16-byte vectors along
+ * both), plus the conventions above; ldy >= O with ldy % 8 == 0.
+ */
+
+/*
+ * x~ as the weight gradient consumes it: xt[t,k] = bf16 of fp32(xq[t,k]) *
+ * sx[t], rounded to nearest even. xq: device int8 [T,K] and sx: device
+ * float[T] from sbl_quant_act; xt: device bf16 [T,K]. K % 8 == 0 or
+ * SBL_ERR_SHAPE; T = 0 enqueues nothing.
+ */
+sbl_status sbl_act_dequant(const int8_t* xq, const float* sx, int64_t T, int64_t K, void* xt,
+                           hipStream_t stream);
+
+/*
+ * dX[t,k] (+)= sum_o dY[t,o] * sw_o * W_eff[o,k].
+ * dy: device bf16 [T, ldy], columns 0..O-1 used. packed, sw_rows: the
+ * forward's packed weights ([O] concatenated rows, N:M as packed) and their
+ * per-row sw (sbl_gemm's sw with sw_inc = 1). The O rows form nseg (1..4)
+ * segments of seg_rows[i] rows each (seg_rows may be NULL when nseg = 1:
+ * one segment of O rows); sw must be constant within a segment (one weight
+ * tensor each) and is read from its first row. Each segment's sum is scaled
+ * by its sw in fp32 and the segments added in order.
+ * dx: device [T, lddx] of dxdt (lddx >= K); accumulate != 0 adds to what dx
+ * holds (for bf16: one rounding of fp32(dx) + result), else overwrites.
+ * Errors: seg_rows not summing to O, a segment empty or not a multiple of 8,
+ * nseg out of range -> SBL_ERR_SHAPE. T = 0 enqueues nothing.
+ */
+sbl_status sbl_linear_bwd_dx(const void* dy, int64_t ldy, const void* packed, const float* sw_rows,
+                             int64_t T, int64_t O, int64_t K, int N, int M, const int64_t* seg_rows,
+                             int nseg, void* dx, sbl_dtype dxdt, int64_t lddx, int accumulate,
+                             hipStream_t stream);
+
+/*
+ * dW[o,k] = sum_t dY[t,o] * xt[t,k]: the master-weight gradient of every
+ * weight, pruned ones included (the Dual STE).
+ * dy: device bf16 [T, ldy]; xt: device bf16 [T,K] from sbl_act_dequant;
+ * dw: device [O,K] of dwdt, overwritten (T = 0 writes zeros; dy and xt may
+ * then be NULL).
+ */
+sbl_status sbl_linear_bwd_dw(const void* dy, int64_t ldy, const void* xt, int64_t T, int64_t O,
+                             int64_t K, void* dw, sbl_dtype dwdt, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

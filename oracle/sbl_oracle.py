@@ -1,4 +1,5 @@
-"""CPU oracle for the Sparse-BitLinear forward path -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the Sparse-BitLinear forward path and its Dual-STE backward
+-- TEST INFRASTRUCTURE ONLY.
 
 This is the plain, slow, step-by-step definition of what the HIP library must
 compute. Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
@@ -42,6 +43,7 @@ __all__ = [
     "to_bf16", "linear_fwd", "packed_row_bytes", "packed_bytes", "pack",
     "unpack", "INDEX_FORM", "mask_words", "mask_flips", "group_threshold",
     "rms_scale", "rmsnorm_quant_act", "dropped_max",
+    "act_dequant_bf16", "linear_bwd_dx", "linear_bwd_dw",
 ]
 
 F32 = np.float32
@@ -248,6 +250,38 @@ def linear_fwd(x: np.ndarray, w: np.ndarray, N: int, M: int,
     y = dequant(acc, sx, sw)
     return dict(xq=xq, sx=sx, w_eff=w_eff, mask=mask, gamma=gamma, sw=sw,
                 acc=acc, y=y)
+
+
+# ---------------------------------------------------------------------------
+# a7. Backward under the Dual straight-through estimator
+# ---------------------------------------------------------------------------
+# [SB] "Gradient Estimation: The Dual Straight-Through Estimator" and the
+# backward steps of the Algorithm 1 walk-through: the forward is the product
+# y = x~ W~^T of x~ = sx * xq and W~ = sw * W_eff. The STE of Q_a hands the
+# gradient at x~ to x unchanged; the Dual STE hands the gradient at W~ (=
+# W_eff up to the scale) to every master weight unchanged -- pruned ones too,
+# no mask gating, and (Algorithm 2's backward returns its input gradient) no
+# clip window. The pages fix no precision; readings: dY is bf16 (the pages'
+# training dtype) and x~ enters the weight gradient as bf16 of fp32(sx * q).
+def act_dequant_bf16(xq: np.ndarray, sx: np.ndarray) -> np.ndarray:
+    """x~ as the weight gradient consumes it: fp32(xq * sx[t]), then rounded
+    to bf16 (nearest, ties to even). Returns bf16-exact float32 [T, K]."""
+    v = (np.asarray(xq).astype(F32) * np.asarray(sx, dtype=F32)[:, None]).astype(F32)
+    return to_bf16(v.astype(np.float64))
+
+
+def linear_bwd_dx(dy: np.ndarray, w_eff: np.ndarray, sw) -> np.ndarray:
+    """dX[t, k] = sum_o dY[t, o] * sw[o] * W_eff[o, k], in fp64: the gradient
+    at x~ of sum(dY * y). sw: scalar or per-row [O] (tensors concatenated)."""
+    w_eff = np.asarray(w_eff)
+    sw = np.broadcast_to(np.asarray(sw, dtype=np.float64), (w_eff.shape[0],))
+    return np.asarray(dy, dtype=np.float64) @ (w_eff.astype(np.float64) * sw[:, None])
+
+
+def linear_bwd_dw(dy: np.ndarray, xt: np.ndarray) -> np.ndarray:
+    """dW[o, k] = sum_t dY[t, o] * x~[t, k], in fp64, at every (o, k): the
+    gradient at W~, passed to the master weights whether kept or pruned."""
+    return np.asarray(dy, dtype=np.float64).T @ np.asarray(xt, dtype=np.float64)
 
 
 # ---------------------------------------------------------------------------

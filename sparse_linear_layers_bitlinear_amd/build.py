@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsbl.so")
 
-SOURCES = ["quant_act.hip", "weight_prep.hip", "gemm.hip", "gemv.hip", "sbl_api.cpp"]
+SOURCES = ["quant_act.hip", "weight_prep.hip", "gemm.hip", "gemv.hip", "backward.hip", "sbl_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

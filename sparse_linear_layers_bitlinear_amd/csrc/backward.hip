@@ -1,0 +1,441 @@
+// Backward of the Sparse-BitLinear layer under the Dual straight-through
+// estimator (Sparse-BitNet summary, section 3.4 "Gradient Estimation: The
+// Dual Straight-Through Estimator" and the backward walk-through of
+// Algorithm 1 / Algorithm 2): with the forward y = x~ W~^T, where
+// x~ = sx * xq is the dequantized int8 activation and W~ = sw * W_eff the
+// scaled ternary-and-masked weight,
+//   dX = dY W~            (gradient at x~; identity through Q_a)
+//   dW = dY^T x~          (gradient at W~, handed unchanged to every master
+//                          weight: neither the mask nor RoundClip blocks it)
+// Both are dense contractions, so they run on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation):
+//   dX: rows t, columns k, reduction over o. dY rows are read as they lie;
+//       W_eff is decoded from the packed record (either form) into bf16.
+//   dW: rows o, columns k, reduction over t. Both operands lie with the
+//       reduction index as their slow axis; they are staged as they lie and
+//       read transposed from LDS with ds_read_b64_tr_b16.
+// x~ enters dW in bf16: k_act_dequant rounds fp32(sx * q) to nearest even.
+//
+// Lane layouts (v_mfma_f32_16x16x32_bf16): lane l holds A[l%16][r(l/16, j)]
+// and B[r(l/16, j)][l%16] for j = 0..7 and returns C[4(l/16)+i][l%16],
+// i = 0..3. Any one-to-one r(g, j) works as long as A and B use the same:
+// kPermBlk8 takes r = 8g + j, kPermHalf r = 4g + j (j < 4), 16 + 4g + j - 4.
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte rows addressed by lanes 4j + i / 4 (j = 0..3); with
+// lane 4j + q pointing at row base + j, column 4q, lane i gets column i of
+// rows base..base+3.
+#include "sbl_internal.h"
+#include "device_util.cuh"
+
+#include <algorithm>
+#include <cstdlib>
+
+namespace sbl {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;   // 2 x 2 waves
+constexpr int kBR = 64;         // reduction rows per LDS stage (two MFMA depths)
+constexpr int kPadRM = 16;      // r-major tile row padding (elements)
+constexpr int kPitchMM = kBR + 8;   // m-major tile row pitch (elements)
+
+enum { kModeDxDense = 0, kModeDxIndex = 1, kModeDw = 2 };
+
+struct BwdArgs {
+  const uint16_t* dy;    // dY bf16 [T][ldy]
+  int64_t ldy;
+  const void* b;         // dX: packed W (concatenated rows); dW: x~ bf16 [T][ldb]
+  int64_t ldb;           // dX: packed row pitch in bytes; dW: x~ row stride in elements
+  const float* sw_rows;  // dX: sw of each packed row (one value per segment is read)
+  void* out;             // dX [T][ldo] / dW [O][ldo]
+  int64_t ldo;
+  int32_t T, O, K;
+  int32_t nseg;          // dX: reduction segments of constant sw; dW: 1
+  int32_t seg_end[4];    // end row of each segment (the first starts at 0)
+  int32_t ntm, ntn;      // tiles along the output rows / columns
+  int32_t out_bf16, accumulate;
+};
+
+__device__ __forceinline__ i16x4 lds_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 join(i16x4 lo, i16x4 hi) {
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Fragment of strip s (16 columns) and MFMA depth u (32 rows) of an r-major
+// tile [kBR][pitch] (rows = reduction index).
+template <bool HALF>
+__device__ __forceinline__ bf16x8 frag_rm(const uint16_t* tile, int pitch, int u, int s, int lane) {
+  const int g = lane >> 4, k = lane & 15;
+  const int r0 = u * 32 + (HALF ? 4 * g : 8 * g) + (k >> 2);
+  const int r1 = r0 + (HALF ? 16 : 4);
+  const int c = 16 * s + 4 * (k & 3);
+  return join(lds_tr(tile + r0 * pitch + c), lds_tr(tile + r1 * pitch + c));
+}
+
+// Fragment of strip s and depth u of an m-major tile [rows][kPitchMM]
+// (reduction index contiguous): one 16-byte read (kPermBlk8).
+__device__ __forceinline__ bf16x8 frag_mm(const uint16_t* tile, int u, int s, int lane) {
+  const uint4 v = *(const uint4*)(tile + (16 * s + (lane & 15)) * kPitchMM + u * 32 + 8 * (lane >> 4));
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Four 2-bit codes (one per byte of e) -> four bf16 (+1 = 0x3F80, -1 =
+// 0xBF80): the codes select from byte tables with v_perm.
+__device__ __forceinline__ uint2 codes4_bf16(uint32_t e) {
+  const uint32_t s01 = __builtin_amdgcn_perm(e, e, 0x01010000u) + 0x00040004u;
+  const uint32_t s23 = __builtin_amdgcn_perm(e, e, 0x03030202u) + 0x00040004u;
+  // selector 0-3: high byte from 0xBF003F00; 4-7: low byte from 0x80008000
+  return make_uint2(__builtin_amdgcn_perm(0x80008000u, 0xBF003F00u, s01),
+                    __builtin_amdgcn_perm(0x80008000u, 0xBF003F00u, s23));
+}
+
+// Dense-form code word (16 codes, k = 16c + u) -> 16 bf16 in k order.
+__device__ __forceinline__ void decode_dense16(uint32_t w, uint4& lo, uint4& hi) {
+  const uint2 a = codes4_bf16(w & 0x03030303u);
+  const uint2 b = codes4_bf16((w >> 2) & 0x03030303u);
+  const uint2 c = codes4_bf16((w >> 4) & 0x03030303u);
+  const uint2 d = codes4_bf16((w >> 6) & 0x03030303u);
+  lo = make_uint4(a.x, a.y, b.x, b.y);
+  hi = make_uint4(c.x, c.y, d.x, d.y);
+}
+
+// Index-form chunk (code word cw, index word iw) -> 16 bf16 of groups
+// 4h..4h+3 (k = 32c + 16h + 0..15).
+__device__ __forceinline__ void decode_index16(uint32_t cw, uint32_t iw, int h, uint4& lo, uint4& hi) {
+  uint32_t out[8];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int q = 4 * h + qq;
+    const uint32_t s0 = (iw >> (4 * q)) & 3u, s1 = (iw >> (4 * q + 2)) & 3u;
+    const uint32_t c0 = (cw >> field_shift(2 * q)) & 3u, c1 = (cw >> field_shift(2 * q + 1)) & 3u;
+    const uint32_t d = (c0 << (2 * s0)) | (c1 << (2 * s1));   // 4 slot codes, 2 bits each
+    const uint32_t e = (d & 3u) | ((d & 0xCu) << 6) | ((d & 0x30u) << 12) | ((d & 0xC0u) << 18);
+    const uint2 v = codes4_bf16(e);
+    out[2 * qq] = v.x;
+    out[2 * qq + 1] = v.y;
+  }
+  lo = make_uint4(out[0], out[1], out[2], out[3]);
+  hi = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
+// Block b of nb -> tile index, so that the blocks one XCD receives (b % 8)
+// cover a contiguous run of tiles (neighbours share operand tiles in L2).
+__device__ __forceinline__ int xcd_tile(int b, int nb) {
+  const int x = b & 7, i = b >> 3, q = nb >> 3, rem = nb & 7;
+  return x * q + min(x, rem) + i;
+}
+
+template <int MODE, int WMB, int WNB, bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_bwd(const BwdArgs a) {
+  constexpr int BM = 32 * WMB, BN = 32 * WNB;   // 2 x 2 waves of (16 WMB) x (16 WNB)
+  constexpr bool DX = MODE != kModeDw;
+  constexpr int PA = DX ? kPitchMM : BM + kPadRM;          // A tile pitch
+  constexpr int PB = BN + kPadRM;                          // B tile pitch (r-major)
+  constexpr int SA = DX ? BM * kPitchMM : kBR * PA;        // A tile elements
+  constexpr int SB = kBR * PB;
+  constexpr bool HALF = !DX;                               // r permutation (see header)
+  extern __shared__ __align__(16) uint16_t lds[];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nb = a.ntm * a.ntn;
+  const int tile = xcd_tile(blockIdx.x, nb);
+  const int tm = tile % a.ntm, tn = tile / a.ntm;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int Mrows = DX ? a.T : a.O;
+
+  // ---- staging: global -> registers -> LDS --------------------------------
+  constexpr int NVA = BM * kBR / 8 / kThreads;             // 16-byte vectors of A per thread
+  constexpr int NWB = kBR * (BN / 16) / kThreads;          // 16-element B pieces per thread
+  static_assert(NVA >= 1 && NWB >= 1, "tile too small for the block");
+  uint4 ra[NVA];
+  uint4 rb[MODE == kModeDw ? 2 * NWB : NWB];               // dW: 8-element vectors
+  (void)rb;
+
+  auto load = [&](int rs, int rend) {
+#pragma unroll
+    for (int i = 0; i < NVA; ++i) {
+      const int v = threadIdx.x + i * kThreads;
+      int row, col;                                        // in dY: (t, o)
+      bool ok;
+      if constexpr (DX) {
+        const int mr = v / (kBR / 8), cv = v % (kBR / 8);
+        row = m0 + mr; col = rs + 8 * cv;
+        ok = row < a.T && col < rend;
+      } else {
+        const int rr = v / (BM / 8), cv = v % (BM / 8);
+        row = rs + rr; col = m0 + 8 * cv;
+        ok = row < rend && col < a.O;
+      }
+      ra[i] = ok ? *(const uint4*)(a.dy + (int64_t)row * a.ldy + col) : make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (MODE == kModeDw) {
+#pragma unroll
+      for (int i = 0; i < 2 * NWB; ++i) {
+        const int v = threadIdx.x + i * kThreads;
+        const int rr = v / (BN / 8), cv = v % (BN / 8);
+        const int t = rs + rr, k = n0 + 8 * cv;
+        const bool ok = t < rend && k < a.K;
+        rb[i] = ok ? *(const uint4*)((const uint16_t*)a.b + (int64_t)t * a.ldb + k) : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NWB; ++i) {
+        const int v = threadIdx.x + i * kThreads;
+        const int rr = v / (BN / 16), cw = v % (BN / 16);
+        const int o = rs + rr, k = n0 + 16 * cw;
+        const uint8_t* row = (const uint8_t*)a.b + (int64_t)o * a.ldb;
+        if constexpr (MODE == kModeDxDense) {
+          const bool ok = o < rend && k < a.K;              // word k/16 lies in the code area
+          rb[i].x = ok ? *(const uint32_t*)(row + 4 * (k >> 4)) : 0u;
+        } else {
+          const bool ok = o < rend && (k & ~31) < a.K;      // chunk k/32 exists
+          const uint2 d = ok ? *(const uint2*)(row + 8 * (k >> 5)) : make_uint2(0u, 0u);
+          rb[i].x = d.x;
+          rb[i].y = d.y;
+        }
+      }
+    }
+  };
+  auto store = [&](uint16_t* A, uint16_t* B) {
+#pragma unroll
+    for (int i = 0; i < NVA; ++i) {
+      const int v = threadIdx.x + i * kThreads;
+      if constexpr (DX) {
+        const int mr = v / (kBR / 8), cv = v % (kBR / 8);
+        *(uint4*)(A + mr * PA + 8 * cv) = ra[i];
+      } else {
+        const int rr = v / (BM / 8), cv = v % (BM / 8);
+        *(uint4*)(A + rr * PA + 8 * cv) = ra[i];
+      }
+    }
+    if constexpr (MODE == kModeDw) {
+#pragma unroll
+      for (int i = 0; i < 2 * NWB; ++i) {
+        const int v = threadIdx.x + i * kThreads;
+        const int rr = v / (BN / 8), cv = v % (BN / 8);
+        *(uint4*)(B + rr * PB + 8 * cv) = rb[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NWB; ++i) {
+        const int v = threadIdx.x + i * kThreads;
+        const int rr = v / (BN / 16), cw = v % (BN / 16);
+        uint4 lo, hi;
+        if constexpr (MODE == kModeDxDense) decode_dense16(rb[i].x, lo, hi);
+        else decode_index16(rb[i].x, rb[i].y, ((n0 + 16 * cw) >> 4) & 1, lo, hi);
+        *(uint4*)(B + rr * PB + 16 * cw) = lo;
+        *(uint4*)(B + rr * PB + 16 * cw + 8) = hi;
+      }
+    }
+  };
+
+  f32x4 acc[WMB][WNB], tot[MULTI ? WMB : 1][MULTI ? WNB : 1];
+#pragma unroll
+  for (int i = 0; i < WMB; ++i)
+#pragma unroll
+    for (int j = 0; j < WNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (MULTI) {
+#pragma unroll
+    for (int i = 0; i < WMB; ++i)
+#pragma unroll
+      for (int j = 0; j < WNB; ++j) tot[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int nseg = DX ? a.nseg : 1;
+  int r_begin = 0;
+  float sw = 1.f;
+  for (int sg = 0; sg < nseg; ++sg) {
+    const int r_end = DX ? a.seg_end[sg] : a.T;
+    if constexpr (DX) sw = a.sw_rows[r_begin];
+    const int steps = (r_end - r_begin + kBR - 1) / kBR;
+    load(r_begin, r_end);
+    store(lds, lds + SA);
+    __syncthreads();
+    for (int st = 0; st < steps; ++st) {
+      const int buf = st & 1;
+      const uint16_t* A = lds + buf * (SA + SB);
+      const uint16_t* B = A + SA;
+      const bool more = st + 1 < steps;
+      if (more) load(r_begin + (st + 1) * kBR, r_end);
+#pragma unroll
+      for (int u = 0; u < kBR / 32; ++u) {
+        bf16x8 fa[WMB], fb[WNB];
+#pragma unroll
+        for (int i = 0; i < WMB; ++i) {
+          if constexpr (DX) fa[i] = frag_mm(A + wm * (16 * WMB) * PA, u, i, lane);
+          else fa[i] = frag_rm<HALF>(A + wm * (16 * WMB), PA, u, i, lane);
+        }
+#pragma unroll
+        for (int j = 0; j < WNB; ++j) fb[j] = frag_rm<HALF>(B + wn * (16 * WNB), PB, u, j, lane);
+#pragma unroll
+        for (int i = 0; i < WMB; ++i)
+#pragma unroll
+          for (int j = 0; j < WNB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+      if (more) {
+        uint16_t* An = lds + (buf ^ 1) * (SA + SB);
+        store(An, An + SA);
+      }
+      __syncthreads();
+    }
+    if constexpr (MULTI) {
+#pragma unroll
+      for (int i = 0; i < WMB; ++i)
+#pragma unroll
+        for (int j = 0; j < WNB; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            tot[i][j][e] += sw * acc[i][j][e];
+            acc[i][j][e] = 0.f;
+          }
+    }
+    r_begin = r_end;
+  }
+
+  // ---- epilogue: C[row][col] (dX: sw * acc; dW: acc) ---------------------
+  const int rbase = m0 + wm * (16 * WMB) + 4 * (lane >> 4);
+  const int cbase = n0 + wn * (16 * WNB) + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < WMB; ++i)
+#pragma unroll
+    for (int j = 0; j < WNB; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = rbase + 16 * i + e, col = cbase + 16 * j;
+        if (row >= Mrows || col >= a.K) continue;
+        float v;
+        if constexpr (MULTI) v = tot[i][j][e];
+        else v = DX ? sw * acc[i][j][e] : acc[i][j][e];
+        const int64_t off = (int64_t)row * a.ldo + col;
+        if (a.out_bf16) {
+          uint16_t* o = (uint16_t*)a.out + off;
+          if (a.accumulate) v += bf16_bits_to_f32(*o);
+          *o = (uint16_t)f32_to_bf16_bits(v);
+        } else {
+          float* o = (float*)a.out + off;
+          if (a.accumulate) v += *o;
+          *o = v;
+        }
+      }
+}
+
+// x~ = bf16_rne(fp32(q) * sx[t]); 8 codes per thread (K % 8 == 0).
+__global__ __launch_bounds__(256) void k_act_dequant(const int8_t* __restrict__ xq,
+                                                      const float* __restrict__ sx, int64_t T,
+                                                      int64_t K, uint16_t* __restrict__ xt) {
+  const int64_t per_row = K / 8;
+  const int64_t n = T * per_row;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / per_row, c = i - t * per_row;
+    const float s = sx[t];
+    const uint2 q = *(const uint2*)(xq + t * K + 8 * c);
+    const uint32_t w[2] = {q.x, q.y};
+    uint32_t o[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int32_t b0 = (int32_t)(w[h] << 24) >> 24, b1 = (int32_t)(w[h] << 16) >> 24;
+      const int32_t b2 = (int32_t)(w[h] << 8) >> 24, b3 = (int32_t)w[h] >> 24;
+      o[2 * h] = f32_to_bf16_bits((float)b0 * s) | (f32_to_bf16_bits((float)b1 * s) << 16);
+      o[2 * h + 1] = f32_to_bf16_bits((float)b2 * s) | (f32_to_bf16_bits((float)b3 * s) << 16);
+    }
+    *(uint4*)(xt + t * K + 8 * c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Tile shape for a problem: the largest of 128x128, 64x128, 64x64 that
+// still gives every compute unit about two tiles.
+int pick_cfg(int64_t rows, int64_t cols) {
+  // tuning override (read on every call so tests can force each configuration)
+  const char* ev = std::getenv("SBL_BWD_TILE");
+  const int forced = ev ? std::atoi(ev) : -1;
+  if (forced >= 0 && forced <= 2) return forced;
+  const int64_t cus = device_info().cus;
+  if (cdiv(rows, 128) * cdiv(cols, 128) >= 2 * cus) return 0;
+  if (cdiv(rows, 64) * cdiv(cols, 128) >= 2 * cus) return 1;
+  return 2;
+}
+
+template <int MODE, int WMB, int WNB, bool MULTI>
+hipError_t launch_cfg(BwdArgs a, hipStream_t s) {
+  constexpr int BM = 32 * WMB, BN = 32 * WNB;
+  constexpr bool DX = MODE != kModeDw;
+  constexpr size_t SA = DX ? (size_t)BM * kPitchMM : (size_t)kBR * (BM + kPadRM);
+  constexpr size_t SB = (size_t)kBR * (BN + kPadRM);
+  constexpr size_t lds = 2 * (SA + SB) * sizeof(uint16_t);
+  auto kern = k_bwd<MODE, WMB, WNB, MULTI>;
+  if (lds > 65536) {
+    static bool set = false;
+    if (!set) {
+      const hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      set = true;
+    }
+  }
+  a.ntm = (int32_t)cdiv(DX ? a.T : a.O, BM);
+  a.ntn = (int32_t)cdiv(a.K, BN);
+  const int64_t nb = (int64_t)a.ntm * a.ntn;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int MODE, bool MULTI>
+hipError_t launch_mode(const BwdArgs& a, int cfg, hipStream_t s) {
+  switch (cfg) {
+    case 0: return launch_cfg<MODE, 4, 4, MULTI>(a, s);
+    case 1: return launch_cfg<MODE, 2, 4, MULTI>(a, s);
+    default: return launch_cfg<MODE, 2, 2, MULTI>(a, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_act_dequant(const int8_t* xq, const float* sx, int64_t T, int64_t K,
+                              uint16_t* xt, hipStream_t s) {
+  const int64_t n = T * (K / 8);
+  const int64_t blocks = std::min<int64_t>(cdiv(n, 256), (int64_t)device_info().cus * 8);
+  hipLaunchKernelGGL(k_act_dequant, dim3((unsigned)blocks), dim3(256), 0, s, xq, sx, T, K, xt);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dx(const uint16_t* dy, int64_t ldy, const void* packed, const float* sw_rows,
+                         int64_t T, int64_t O, int64_t K, int N, int M, const int64_t* seg_end,
+                         int nseg, void* dx, bool dx_bf16, int64_t lddx, bool accumulate,
+                         int cfg, hipStream_t s) {
+  BwdArgs a{};
+  a.dy = dy; a.ldy = ldy; a.b = packed; a.ldb = row_pitch(K, N, M); a.sw_rows = sw_rows;
+  a.out = dx; a.ldo = lddx; a.T = (int32_t)T; a.O = (int32_t)O; a.K = (int32_t)K;
+  a.nseg = nseg;
+  for (int i = 0; i < nseg; ++i) a.seg_end[i] = (int32_t)seg_end[i];
+  a.out_bf16 = dx_bf16; a.accumulate = accumulate;
+  if (cfg < 0) cfg = pick_cfg(T, K);
+  const bool idx = index_form(N, M);
+  if (nseg > 1)
+    return idx ? launch_mode<kModeDxIndex, true>(a, cfg, s) : launch_mode<kModeDxDense, true>(a, cfg, s);
+  return idx ? launch_mode<kModeDxIndex, false>(a, cfg, s) : launch_mode<kModeDxDense, false>(a, cfg, s);
+}
+
+hipError_t launch_bwd_dw(const uint16_t* dy, int64_t ldy, const uint16_t* xt, int64_t ldxt,
+                         int64_t T, int64_t O, int64_t K, void* dw, bool dw_bf16, int64_t lddw,
+                         int cfg, hipStream_t s) {
+  BwdArgs a{};
+  a.dy = dy; a.ldy = ldy; a.b = xt; a.ldb = ldxt; a.sw_rows = nullptr;
+  a.out = dw; a.ldo = lddw; a.T = (int32_t)T; a.O = (int32_t)O; a.K = (int32_t)K;
+  a.nseg = 1; a.seg_end[0] = (int32_t)T;
+  a.out_bf16 = dw_bf16; a.accumulate = 0;
+  if (cfg < 0) cfg = pick_cfg(O, K);
+  return launch_mode<kModeDw, false>(a, cfg, s);
+}
+
+}  // namespace sbl

@@ -7,6 +7,7 @@
 #include <cfloat>
 #include <cstdio>
 #include <cstdlib>
+#include <climits>
 #include <mutex>
 
 static_assert(sbl::kMaxPrepBatch == SBL_MAX_PREP_BATCH, "batch limit of the ABI");
@@ -58,6 +59,14 @@ sbl_status check_wshape(int64_t O, int64_t K, int N, int M) {
   if (!nm_ok(N, M)) return SBL_ERR_NM;
   if (O < 0 || K < 1 || K > kMaxK || K % M != 0) return SBL_ERR_SHAPE;
   if (O > (int64_t(1) << 31)) return SBL_ERR_SHAPE;
+  return SBL_OK;
+}
+
+// Shapes shared by the two gradient products.
+sbl_status check_bwd_shape(int64_t ldy, int64_t T, int64_t O, int64_t K) {
+  if (T < 0 || T > INT32_MAX || O < 8 || O > INT32_MAX || O % 8 != 0) return SBL_ERR_SHAPE;
+  if (K < 8 || K > kMaxK || K % 8 != 0) return SBL_ERR_SHAPE;
+  if (ldy < O || ldy % 8 != 0) return SBL_ERR_SHAPE;
   return SBL_OK;
 }
 
@@ -309,6 +318,57 @@ sbl_status sbl_linear_fwd(const void* x, sbl_dtype xdt, const void* w_master, sb
   return hip_status(launch_gemm(xq, sx, packed, sw, inc, T, O, K, N, M, y, ydt == SBL_BF16,
                                 nullptr, stream),
                     "linear_fwd/gemm");
+}
+
+// ---- backward (Dual STE) ------------------------------------------------
+sbl_status sbl_act_dequant(const int8_t* xq, const float* sx, int64_t T, int64_t K, void* xt,
+                           hipStream_t stream) {
+  if (T < 0 || T > INT32_MAX || K < 8 || K > kMaxK || K % 8 != 0) return SBL_ERR_SHAPE;
+  if (T == 0) return SBL_OK;
+  if (!xq || !sx || !xt) return SBL_ERR_NULL;
+  if (!aligned16(xq) || !aligned16(sx) || !aligned16(xt)) return SBL_ERR_ALIGN;
+  return hip_status(launch_act_dequant(xq, sx, T, K, (uint16_t*)xt, stream), "sbl_act_dequant");
+}
+
+sbl_status sbl_linear_bwd_dx(const void* dy, int64_t ldy, const void* packed, const float* sw_rows,
+                             int64_t T, int64_t O, int64_t K, int N, int M, const int64_t* seg_rows,
+                             int nseg, void* dx, sbl_dtype dxdt, int64_t lddx, int accumulate,
+                             hipStream_t stream) {
+  if (!dtype_ok(dxdt)) return SBL_ERR_DTYPE;
+  if (!nm_ok(N, M)) return SBL_ERR_NM;
+  sbl_status st = check_bwd_shape(ldy, T, O, K);
+  if (st != SBL_OK) return st;
+  if (K % M != 0 || lddx < K) return SBL_ERR_SHAPE;
+  if (nseg < 1 || nseg > 4) return SBL_ERR_SHAPE;
+  if (nseg > 1 && !seg_rows) return SBL_ERR_NULL;
+  int64_t ends[4];
+  int64_t sum = 0;
+  for (int i = 0; i < nseg; ++i) {
+    const int64_t r = seg_rows ? seg_rows[i] : O;
+    if (r < 8 || r % 8 != 0) return SBL_ERR_SHAPE;
+    sum += r;
+    ends[i] = sum;
+  }
+  if (sum != O) return SBL_ERR_SHAPE;
+  if (T == 0) return SBL_OK;
+  if (!dy || !packed || !sw_rows || !dx) return SBL_ERR_NULL;
+  if (!aligned16(dy) || !aligned16(packed) || !aligned16(sw_rows) || !aligned16(dx))
+    return SBL_ERR_ALIGN;
+  return hip_status(launch_bwd_dx((const uint16_t*)dy, ldy, packed, sw_rows, T, O, K, N, M, ends,
+                                  nseg, dx, dxdt == SBL_BF16, lddx, accumulate != 0, -1, stream),
+                    "sbl_linear_bwd_dx");
+}
+
+sbl_status sbl_linear_bwd_dw(const void* dy, int64_t ldy, const void* xt, int64_t T, int64_t O,
+                             int64_t K, void* dw, sbl_dtype dwdt, hipStream_t stream) {
+  if (!dtype_ok(dwdt)) return SBL_ERR_DTYPE;
+  sbl_status st = check_bwd_shape(ldy, T, O, K);
+  if (st != SBL_OK) return st;
+  if (!dw || (T > 0 && (!dy || !xt))) return SBL_ERR_NULL;
+  if ((dy && !aligned16(dy)) || (xt && !aligned16(xt)) || !aligned16(dw)) return SBL_ERR_ALIGN;
+  return hip_status(launch_bwd_dw((const uint16_t*)dy, ldy, (const uint16_t*)xt, K, T, O, K, dw,
+                                  dwdt == SBL_BF16, K, -1, stream),
+                    "sbl_linear_bwd_dw");
 }
 
 }  // extern "C"

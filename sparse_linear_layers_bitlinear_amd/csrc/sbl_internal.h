@@ -78,6 +78,20 @@ hipError_t launch_unpack(const void* packed, int64_t O, int64_t K, int N, int M,
 // Decode path (1 <= T <= 16). xmode 0: xq int8 [T,K] and sx given; 1 / 2:
 // x bf16 / fp32 [T,K], quantized per token inside the kernel with eps.
 // decode_fits() tells whether a shape takes it (else the tiled GEMM runs).
+// Backward (Dual STE). x~ bf16 [T,K] from xq, sx (K % 8 == 0).
+hipError_t launch_act_dequant(const int8_t* xq, const float* sx, int64_t T, int64_t K,
+                              uint16_t* xt, hipStream_t s);
+// dX [T,K] (+)= sum over segments of sw(seg) * dY[:, seg] W_eff[seg, :];
+// seg_end: end row of each of nseg (<= 4) segments; cfg < 0 picks the tile.
+hipError_t launch_bwd_dx(const uint16_t* dy, int64_t ldy, const void* packed, const float* sw_rows,
+                         int64_t T, int64_t O, int64_t K, int N, int M, const int64_t* seg_end,
+                         int nseg, void* dx, bool dx_bf16, int64_t lddx, bool accumulate,
+                         int cfg, hipStream_t s);
+// dW [O,K] = dY^T x~ (dY [T, ldy] bf16, x~ [T, ldxt] bf16).
+hipError_t launch_bwd_dw(const uint16_t* dy, int64_t ldy, const uint16_t* xt, int64_t ldxt,
+                         int64_t T, int64_t O, int64_t K, void* dw, bool dw_bf16, int64_t lddw,
+                         int cfg, hipStream_t s);
+
 bool decode_fits(int64_t T, int64_t O, int64_t K, int N, int M, int xmode);
 hipError_t launch_decode(const void* x, int xmode, const float* sx, float eps, const void* packed,
                          const float* sw, int64_t sw_inc, int64_t T, int64_t O, int64_t K, int N,

@@ -64,6 +64,10 @@ def _load():
         "sbl_gemm": ([P, P, P, P, I64, I64, I64, I64, I, I, P, I, P, P], I),
         "sbl_linear_fwd_workspace": ([I64, I64, I64, I, I, I, ctypes.POINTER(S)], I),
         "sbl_linear_fwd": ([P, I, P, I, P, P, I64, I64, I64, I64, I, I, F, F, P, I, P, S, P], I),
+        "sbl_act_dequant": ([P, P, I64, I64, P, P], I),
+        "sbl_linear_bwd_dx": ([P, I64, P, P, I64, I64, I64, I, I, ctypes.POINTER(I64), I, P, I,
+                               I64, I, P], I),
+        "sbl_linear_bwd_dw": ([P, I64, P, I64, I64, I64, P, I, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -276,3 +280,43 @@ def sbl_linear_fwd(x: torch.Tensor, N: int, M: int, w_master=None, prepacked=Non
         _ptr(x), _dt(x.dtype), _ptr(w_master), wdt, _ptr(prepacked), _ptr(sw), sw_inc,
         T, O, K, N, M, eps_a, eps_w, _ptr(y), _dt(y.dtype), _ptr(ws), ws.numel(), _stream(dev)))
     return y
+
+
+# ---- backward (Dual STE) ----------------------------------------------------
+def sbl_act_dequant(xq: torch.Tensor, sx: torch.Tensor, xt=None):
+    """x~ in bf16: bf16_rne(fp32(xq) * sx[t]), [T, K]."""
+    T, K = xq.shape
+    xt = torch.empty((T, K), dtype=torch.bfloat16, device=xq.device) if xt is None else xt
+    _check("sbl_act_dequant", _lib.sbl_act_dequant(_ptr(xq), _ptr(sx), T, K, _ptr(xt),
+                                                   _stream(xq.device)))
+    return xt
+
+
+def sbl_linear_bwd_dx(dy: torch.Tensor, packed: torch.Tensor, sw_rows: torch.Tensor, K: int,
+                      N: int, M: int, seg_rows=None, O: int | None = None,
+                      out_dtype=torch.bfloat16, dx=None, accumulate=False):
+    """dX = sum over segments of sw * dY[:, seg] W_eff[seg]; dy bf16 [T, >= O]
+    (row stride dy.stride(0)); seg_rows: rows of each weight tensor in the
+    concatenated packed buffer (default: one segment of O rows)."""
+    T = dy.shape[0]
+    O = dy.shape[1] if O is None else O
+    dev = dy.device
+    dx = torch.empty((T, K), dtype=out_dtype, device=dev) if dx is None else dx
+    segs = list(seg_rows) if seg_rows is not None else [O]
+    arr = (ctypes.c_int64 * len(segs))(*segs)
+    _check("sbl_linear_bwd_dx", _lib.sbl_linear_bwd_dx(
+        _ptr(dy), dy.stride(0), _ptr(packed), _ptr(sw_rows), T, O, K, N, M, arr, len(segs),
+        _ptr(dx), _dt(dx.dtype), dx.stride(0), int(bool(accumulate)), _stream(dev)))
+    return dx
+
+
+def sbl_linear_bwd_dw(dy: torch.Tensor, xt: torch.Tensor, O: int | None = None,
+                      out_dtype=torch.float32, dw=None):
+    """dW = dY^T x~ ([O, K]); dy bf16 [T, >= O], xt bf16 [T, K]."""
+    T, K = xt.shape
+    O = dy.shape[1] if O is None else O
+    dev = xt.device
+    dw = torch.empty((O, K), dtype=out_dtype, device=dev) if dw is None else dw
+    _check("sbl_linear_bwd_dw", _lib.sbl_linear_bwd_dw(
+        _ptr(dy), dy.stride(0), _ptr(xt), T, O, K, _ptr(dw), _dt(dw.dtype), _stream(dev)))
+    return dw

@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
               "sbl_linear_fwd", "sbl_packed_bytes", "sbl_quant_mask_weight_workspace",
               "sbl_linear_fwd_workspace", "sbl_status_string", "sbl_version",
               "sbl_quant_mask_weight_batch", "sbl_quant_mask_weight_batch_workspace",
-              "sbl_rmsnorm_quant_act"]:
+              "sbl_rmsnorm_quant_act", "sbl_act_dequant", "sbl_linear_bwd_dx",
+              "sbl_linear_bwd_dw"]:
         assert n in names
 
 
@@ -183,3 +184,43 @@ def test_weight_batch_validation(S):
     assert L.sbl_quant_mask_weight_batch_workspace(1, ctypes.byref(n)) == 0 and n.value == single.value
     assert L.sbl_quant_mask_weight_batch_workspace(0, ctypes.byref(n)) == 2
     assert L.sbl_quant_mask_weight_batch_workspace(9, ctypes.byref(n)) == 2
+
+
+def test_backward_validation(S):
+    """Host-side checks of the Dual-STE backward calls (no launch happens)."""
+    L = S.lib
+    I64 = ctypes.c_int64
+    segs = lambda *r: (I64 * max(1, len(r)))(*r)
+    dx = lambda dy=FAKE, ldy=256, pk=FAKE, sw=FAKE, T=32, O=256, K=128, N=6, M=8, sg=None, ns=1, \
+        out=FAKE, dt=0, ld=128, acc=0: L.sbl_linear_bwd_dx(dy, ldy, pk, sw, T, O, K, N, M, sg, ns,
+                                                         out, dt, ld, acc, None)
+    assert dx(dt=3) == 4                                    # dtype
+    assert dx(N=9) == 3                                     # N:M
+    assert dx(O=252, ldy=256) == 2                          # O % 8
+    assert dx(K=124) == 2                                   # K % 8
+    assert dx(K=132, ld=132, M=8) == 2                      # K % 8 (and % M)
+    assert dx(ldy=250) == 2                                 # ldy < O
+    assert dx(ld=64) == 2                                   # lddx < K
+    assert dx(ns=5) == 2                                    # too many segments
+    assert dx(ns=2) == 1                                    # segments missing
+    assert dx(ns=2, sg=segs(128, 120)) == 2                 # do not sum to O
+    assert dx(ns=2, sg=segs(124, 132)) == 2                 # not multiples of 8
+    assert dx(T=0, dy=None, pk=None, sw=None, out=None) == 0  # empty call
+    assert dx(dy=None) == 1
+    assert dx(sw=None) == 1
+    assert dx(out=MIS) == 5
+    assert dx(dy=MIS) == 5
+    dw = lambda dy=FAKE, ldy=256, xt=FAKE, T=32, O=256, K=128, out=FAKE, dt=1: \
+        L.sbl_linear_bwd_dw(dy, ldy, xt, T, O, K, out, dt, None)
+    assert dw(dt=2) == 4
+    assert dw(O=0) == 2
+    assert dw(K=100) == 2
+    assert dw(T=-1) == 2
+    assert dw(out=None) == 1
+    assert dw(xt=None) == 1
+    assert dw(xt=MIS) == 5
+    assert L.sbl_act_dequant(FAKE, FAKE, 4, 12, FAKE, None) == 2   # K % 8
+    assert L.sbl_act_dequant(FAKE, FAKE, 0, 16, None, None) == 0   # empty
+    assert L.sbl_act_dequant(FAKE, None, 4, 16, FAKE, None) == 1
+    assert L.sbl_act_dequant(FAKE, FAKE, 4, 16, MIS, None) == 5
+
