@@ -34,11 +34,12 @@ if ROOT not in sys.path:
 
 from sparse_linear_layers_bitlinear_amd import sbl  # noqa: E402
 from sparse_linear_layers_bitlinear_amd.workloads import (  # noqa: E402
-    WORKLOADS, make_workload)
+    WORKLOADS, bf16_round, make_workload)
 
 # MI355X published peaks
 PEAK_INT8_DENSE_TOPS = 5000.0     # dense int8 MFMA, TOPS
 PEAK_HBM_GBS = 8000.0             # HBM3E, GB/s
+PEAK_BF16_DENSE_TFLOPS = 2500.0   # dense bf16 MFMA, TFLOP/s
 
 
 def parse():
@@ -59,6 +60,9 @@ def parse():
                         "(sbl_rmsnorm_quant_act) instead of Q_a(x)")
     p.add_argument("--mask-from-ternary", action="store_true",
                    help="prefill: the ablated recipe, mask ranked on the ternary codes")
+    p.add_argument("--backward", action="store_true",
+                   help="prefill: the step adds the Dual-STE backward of every projection (x~ in "
+                        "bf16, dX and dW on the bf16 matrix cores) to the forward: a training step")
     p.add_argument("--mask-then-quant", action="store_true",
                    help="prefill: the composition-order ablation, gamma over the kept weights only")
     p.add_argument("--diagnostics", action="store_true",
@@ -71,9 +75,11 @@ def parse():
 
 # ---------------------------------------------------------------- prefill --
 class PrefillStep:
-    def __init__(self, wl_name, N, M, diagnostics=False, fused_norm=False, variant=0):
+    def __init__(self, wl_name, N, M, diagnostics=False, fused_norm=False, variant=0,
+                 backward=False):
         wl = WORKLOADS[wl_name]
         self.wl, self.N, self.M, self.diag, self.norm = wl, N, M, diagnostics, fused_norm
+        self.bwd = backward
         W, X = make_workload(wl_name)
         dev = torch.device("cuda:0")
         self.T = wl.T
@@ -128,6 +134,16 @@ class PrefillStep:
                 it["group_thr"] = torch.empty((O, K // M), dtype=torch.float32, device=dev)
             torch.cuda.synchronize()
         self.ops = sum(2.0 * self.T * l.O * l.K for l in wl.linears)
+        if backward:
+            # upstream gradient of each group's output (seeded bf16 N(0,1)), x~, dX and dW
+            self.dy, self.xt, self.dx, self.dw = {}, {}, {}, {}
+            for xn, lins in self.groups.items():
+                K, O = self.K_of[xn], sum(l.O for l in lins)
+                self.dy[xn] = torch.randn((self.T, O), generator=gen, device=dev).to(torch.bfloat16)
+                self.xt[xn] = torch.empty((self.T, K), dtype=torch.bfloat16, device=dev)
+                self.dx[xn] = torch.empty((self.T, K), dtype=torch.bfloat16, device=dev)
+                self.dw[xn] = torch.empty((O, K), dtype=torch.float32, device=dev)
+            self.ops *= 3.0       # forward + dX + dW, each 2 T O K per projection
 
     def calls(self):
         """The step as an ordered list of (name, launch) pairs."""
@@ -147,6 +163,16 @@ class PrefillStep:
             out.append((f"gemm[{'+'.join(l.name for l in lins)}]",
                         lambda xn=xn, O=O: sbl.sbl_gemm(self.xq[xn], self.sx[xn], self.packed[xn],
                                                         self.swr[xn], O, N, M, y=self.y[xn])))
+        if self.bwd:
+            for xn, lins in reversed(list(self.groups.items())):
+                K, tag = self.K_of[xn], '+'.join(l.name for l in lins)
+                out.append((f"act_dequant[{xn}]", lambda xn=xn: sbl.sbl_act_dequant(
+                    self.xq[xn], self.sx[xn], xt=self.xt[xn])))
+                out.append((f"bwd_dx[{tag}]", lambda xn=xn, K=K, lins=lins: sbl.sbl_linear_bwd_dx(
+                    self.dy[xn], self.packed[xn], self.swr[xn], K, N, M,
+                    seg_rows=[l.O for l in lins], dx=self.dx[xn])))
+                out.append((f"bwd_dw[{tag}]", lambda xn=xn: sbl.sbl_linear_bwd_dw(
+                    self.dy[xn], self.xt[xn], dw=self.dw[xn])))
         return out
 
     cold_weights = False   # inputs of every call were just written by the step: cache-hot
@@ -160,6 +186,7 @@ class PrefillStep:
         for xn in self.groups:
             order += [c for c in calls if c[0] in (f"quant_act[{xn}]",) or
                       (c[0].startswith("gemm[") and c[0] == self._gemm_name(xn))]
+        order += [c for c in calls if c[0].split("[")[0] in ("act_dequant", "bwd_dx", "bwd_dw")]
         run_all(order)
 
     def _gemm_name(self, xn):
@@ -168,6 +195,13 @@ class PrefillStep:
     def call_info(self, name):
         """(bound, algorithmic units per launch, unit) of a named call."""
         T = self.T
+        if name.startswith("bwd_"):
+            tag = name[name.index("[") + 1:-1]
+            ops = sum(2.0 * T * l.O * l.K for l in self.wl.linears if l.name in tag.split("+"))
+            return "mfma_bf16", ops, "flops"
+        if name.startswith("act_dequant["):
+            K = self.K_of[name[12:-1]]
+            return "hbm", 3.0 * T * K + 4.0 * T, "bytes"
         if name.startswith("gemm["):
             xn = [k for k, ls in self.groups.items()
                   if name == f"gemm[{'+'.join(l.name for l in ls)}]"][0]
@@ -340,7 +374,7 @@ def per_call_times(step, reps):
     return out, per_step
 
 
-def cpu_baseline(wl_name, N, M, seconds, decode_T=None):
+def cpu_baseline(wl_name, N, M, seconds, decode_T=None, backward=False):
     import oracle as o
     from threadpoolctl import threadpool_info
     if wl_name == "bitnet_decode":
@@ -358,13 +392,19 @@ def cpu_baseline(wl_name, N, M, seconds, decode_T=None):
     else:
         W, X = make_workload(wl_name)
         wl = WORKLOADS[wl_name]
+        rng = np.random.default_rng(7)
+        dys = {l.name: bf16_round(rng.standard_normal((wl.T, l.O)).astype(np.float32))
+               for l in wl.linears} if backward else {}
         def one():
             for l in wl.linears:
-                o.linear_fwd(X[l.x_name], W[l.name], N, M)
-        units = sum(2.0 * wl.T * l.O * l.K for l in wl.linears)
+                r = o.linear_fwd(X[l.x_name], W[l.name], N, M)
+                if backward:
+                    o.linear_bwd_dx(dys[l.name], r["w_eff"], r["sw"])
+                    o.linear_bwd_dw(dys[l.name], o.act_dequant_bf16(r["xq"], r["sx"]))
+        units = sum(2.0 * wl.T * l.O * l.K for l in wl.linears) * (3.0 if backward else 1.0)
         unit = "TOPS"
         sample = (f"full {wl_name} step (T={wl.T}, {N}:{M}, every projection, mask "
-                  f"recomputed), repeated")
+                  f"recomputed{', forward + backward' if backward else ''}), repeated")
     times = []
     t_end = time.time() + seconds
     while time.time() < t_end or len(times) < 2:
@@ -436,7 +476,7 @@ def traffic_tag(a, N, M):
         return f"bitnet_decode T={a.decode_T} L={a.layers}"
     return (f"{a.workload} T={WORKLOADS[a.workload].T} {N}:{M}" + (" diag" if a.diagnostics else "")
             + (" norm" if a.fused_norm else "") + (" ternary-mask" if a.mask_from_ternary else "")
-            + (" mask-then-quant" if a.mask_then_quant else ""))
+            + (" mask-then-quant" if a.mask_then_quant else "") + (" backward" if a.backward else ""))
 
 
 def per_call_rates(step, per_call):
@@ -449,6 +489,9 @@ def per_call_rates(step, per_call):
         if bound == "hbm":
             out[k] = {"us": round(ms * 1e3, 2), "GB/s": round(rate / 1e9, 1),
                       "frac": round(rate / 1e9 / PEAK_HBM_GBS, 4)}
+        elif bound == "mfma_bf16":
+            out[k] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(rate / 1e12, 1),
+                      "frac": round(rate / 1e12 / PEAK_BF16_DENSE_TFLOPS, 4)}
         else:
             out[k] = {"us": round(ms * 1e3, 2), "TOPS": round(rate / 1e12, 1),
                       "frac": round(rate / 1e12 / PEAK_INT8_DENSE_TOPS, 4)}
@@ -475,7 +518,8 @@ def main():
         step = DecodeStep(a.decode_T, a.layers)
     else:
         step = PrefillStep(a.workload, N, M, a.diagnostics, a.fused_norm,
-                           1 if a.mask_from_ternary else 2 if a.mask_then_quant else 0)
+                           1 if a.mask_from_ternary else 2 if a.mask_then_quant else 0,
+                           a.backward)
     ms = time_steps(step, a.steps, a.warmup, a.eager)
     per_call, calls_per_step = per_call_times(step, max(5, min(a.steps, 20)))
     share = {k: per_call[k] * calls_per_step[k] for k in per_call}
@@ -485,6 +529,9 @@ def main():
     if bound == "mfma":
         roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 2),
                 "peak": PEAK_INT8_DENSE_TOPS, "unit": "TFLOP/s"}
+    elif bound == "mfma_bf16":
+        roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 2),
+                "peak": PEAK_BF16_DENSE_TFLOPS, "unit": "TFLOP/s", "dtype": "bf16"}
     else:
         roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
@@ -502,19 +549,22 @@ def main():
                   "weights_per_layer": step.weights}
     else:
         value = step.ops / (ms * 1e-3) / 1e12
-        metric = "Sparse-BitLinear effective TOPS (prefill)"
+        metric = ("Sparse-BitLinear effective TOPS (training step: prefill forward + Dual-STE "
+                  "backward)" if a.backward else "Sparse-BitLinear effective TOPS (prefill)")
         unit = "TOPS"
         config = {"workload": a.workload, "tokens": step.T, "nm": f"{N}:{M}",
                   "mask_diagnostics": bool(a.diagnostics), "fused_rmsnorm": bool(a.fused_norm),
                   "mask_from": "ternary codes (ablation)" if a.mask_from_ternary else "master |W|",
                   "composition": "mask-then-quant (ablation)" if a.mask_then_quant else "quant-then-mask",
                   "projections": [f"{l.name} {l.O}x{l.K}" for l in wl.linears],
-                  "mask": "recomputed every step", "dense_equiv_ops_per_step": step.ops}
+                  "mask": "recomputed every step", "dense_equiv_ops_per_step": step.ops,
+                  "backward": bool(a.backward)}
     out = {
         "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8xternary->int32 (bf16 in/out)", "data": "synthetic",
+        "dtype": ("int8xternary->int32 fwd, bf16 MFMA (fp32 acc) bwd" if getattr(a, "backward", False)
+                  else "int8xternary->int32 (bf16 in/out)"), "data": "synthetic",
         "config": config, "roofline": roof,
         "breakdown_ms": {k: round(share[k], 5) for k in share},
         "per_call": per_call_rates(step, per_call),
@@ -522,7 +572,8 @@ def main():
         "timing": "eager launches" if a.eager else "HIP graph replay",
     }
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(a.workload, N, M, a.cpu_seconds, a.decode_T)
+        out["cpu_baseline"] = cpu_baseline(a.workload, N, M, a.cpu_seconds, a.decode_T,
+                                           a.backward and a.workload != "bitnet_decode")
     print(json.dumps(out))
 
 

@@ -353,17 +353,21 @@ __global__ __launch_bounds__(256) void k_act_dequant(const int8_t* __restrict__ 
   }
 }
 
-// Tile shape for a problem: the largest of 128x128, 64x128, 64x64 that
-// still gives every compute unit about two tiles.
+// Workgroup tiles (rows x columns of the output; 2 x 2 waves each):
+//   0: 128x128, 1: 64x128, 2: 64x64, 3: 256x128, 4: 128x256.
+// Measured on the FFN shapes (T = 2048 and 4096): 128x128 (three waves per
+// SIMD) is fastest whenever it gives about three quarters of the compute
+// units a workgroup; below that 64x64 (more workgroups) wins. The two large
+// tiles need 384 registers per lane -- one wave per SIMD, too little to hide
+// the staging loads -- and stay selectable for tuning only.
+constexpr int kNumBwdCfg = 5;
 int pick_cfg(int64_t rows, int64_t cols) {
   // tuning override (read on every call so tests can force each configuration)
   const char* ev = std::getenv("SBL_BWD_TILE");
   const int forced = ev ? std::atoi(ev) : -1;
-  if (forced >= 0 && forced <= 2) return forced;
-  const int64_t cus = device_info().cus;
-  if (cdiv(rows, 128) * cdiv(cols, 128) >= 2 * cus) return 0;
-  if (cdiv(rows, 64) * cdiv(cols, 128) >= 2 * cus) return 1;
-  return 2;
+  if (forced >= 0 && forced < kNumBwdCfg) return forced;
+  const int64_t want = device_info().cus * 3 / 4;
+  return cdiv(rows, 128) * cdiv(cols, 128) >= want ? 0 : 2;
 }
 
 template <int MODE, int WMB, int WNB, bool MULTI>
@@ -395,6 +399,8 @@ hipError_t launch_mode(const BwdArgs& a, int cfg, hipStream_t s) {
   switch (cfg) {
     case 0: return launch_cfg<MODE, 4, 4, MULTI>(a, s);
     case 1: return launch_cfg<MODE, 2, 4, MULTI>(a, s);
+    case 3: return launch_cfg<MODE, 8, 4, MULTI>(a, s);
+    case 4: return launch_cfg<MODE, 4, 8, MULTI>(a, s);
     default: return launch_cfg<MODE, 2, 2, MULTI>(a, s);
   }
 }

@@ -96,7 +96,7 @@ def test_bwd_dx_parity(S, N, M, out_bf16):
         _dx_case(S, T, O, K, N, M, out_bf16, seed=T + O + N)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("N,M", [(6, 8), (2, 4)])
 def test_bwd_dx_every_tile_config(S, cfg, N, M, monkeypatch):
     monkeypatch.setenv("SBL_BWD_TILE", str(cfg))
@@ -137,7 +137,7 @@ def test_bwd_dw_parity(S, out_bf16):
         _dw_case(S, T, O, K, out_bf16, seed=T + O)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_bwd_dw_every_tile_config(S, cfg, monkeypatch):
     monkeypatch.setenv("SBL_BWD_TILE", str(cfg))
     for T, O, K in [(150, 264, 392), (64, 520, 136)]:
