@@ -134,7 +134,7 @@ __device__ __forceinline__ int xcd_tile(int b, int nb) {
 }
 
 template <int MODE, int WMB, int WNB, bool MULTI>
-__global__ __launch_bounds__(kThreads) void k_bwd(const BwdArgs a) {
+__global__ __launch_bounds__(kThreads, (WMB * WNB > 16) ? 1 : 2) void k_bwd(const BwdArgs a) {
   constexpr int BM = 32 * WMB, BN = 32 * WNB;   // 2 x 2 waves of (16 WMB) x (16 WNB)
   constexpr bool DX = MODE != kModeDw;
   constexpr int PA = DX ? kPitchMM : BM + kPadRM;          // A tile pitch
@@ -156,14 +156,18 @@ __global__ __launch_bounds__(kThreads) void k_bwd(const BwdArgs a) {
   constexpr int NVA = BM * kBR / 8 / kThreads;             // 16-byte vectors of A per thread
   constexpr int NWB = kBR * (BN / 16) / kThreads;          // 16-element B pieces per thread
   static_assert(NVA >= 1 && NWB >= 1, "tile too small for the block");
-  uint4 ra[NVA];
-  uint4 rb[MODE == kModeDw ? 2 * NWB : NWB];               // dW: 8-element vectors
-  (void)rb;
+  // Two register stages: the loads of step s + 1 are issued two steps ahead,
+  // so their latency is covered by two compute phases, not one.
+  struct Stage {
+    uint4 ra[NVA];
+    uint4 rb[MODE == kModeDw ? 2 * NWB : NWB];             // dW: 8-element vectors
+  };
+  Stage S0, S1;
 
   // (Loads are guarded per lane. A branch-free form -- clamped addresses and
   // a select -- measured 7-28% slower: the address arithmetic costs more than
   // the exec-mask branches, which are almost never taken.)
-  auto load = [&](int rs, int rend) {
+  auto load = [&](Stage& g, int rs, int rend) {
 #pragma unroll
     for (int i = 0; i < NVA; ++i) {
       const int v = threadIdx.x + i * kThreads;
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd(const BwdArgs a) {
         row = rs + rr; col = m0 + 8 * cv;
         ok = row < rend && col < a.O;
       }
-      ra[i] = ok ? *(const uint4*)(a.dy + (int64_t)row * a.ldy + col) : make_uint4(0, 0, 0, 0);
+      g.ra[i] = ok ? *(const uint4*)(a.dy + (int64_t)row * a.ldy + col) : make_uint4(0, 0, 0, 0);
     }
     if constexpr (MODE == kModeDw) {
 #pragma unroll
@@ -187,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd(const BwdArgs a) {
         const int rr = v / (BN / 8), cv = v % (BN / 8);
         const int t = rs + rr, k = n0 + 8 * cv;
         const bool ok = t < rend && k < a.K;
-        rb[i] = ok ? *(const uint4*)((const uint16_t*)a.b + (int64_t)t * a.ldb + k) : make_uint4(0, 0, 0, 0);
+        g.rb[i] = ok ? *(const uint4*)((const uint16_t*)a.b + (int64_t)t * a.ldb + k) : make_uint4(0, 0, 0, 0);
       }
     } else {
 #pragma unroll
@@ -198,26 +202,26 @@ __global__ __launch_bounds__(kThreads) void k_bwd(const BwdArgs a) {
         const uint8_t* row = (const uint8_t*)a.b + (int64_t)o * a.ldb;
         if constexpr (MODE == kModeDxDense) {
           const bool ok = o < rend && k < a.K;              // word k/16 lies in the code area
-          rb[i].x = ok ? *(const uint32_t*)(row + 4 * (k >> 4)) : 0u;
+          g.rb[i].x = ok ? *(const uint32_t*)(row + 4 * (k >> 4)) : 0u;
         } else {
           const bool ok = o < rend && (k & ~31) < a.K;      // chunk k/32 exists
           const uint2 d = ok ? *(const uint2*)(row + 8 * (k >> 5)) : make_uint2(0u, 0u);
-          rb[i].x = d.x;
-          rb[i].y = d.y;
+          g.rb[i].x = d.x;
+          g.rb[i].y = d.y;
         }
       }
     }
   };
-  auto store = [&](uint16_t* A, uint16_t* B) {
+  auto store = [&](const Stage& g, uint16_t* A, uint16_t* B) {
 #pragma unroll
     for (int i = 0; i < NVA; ++i) {
       const int v = threadIdx.x + i * kThreads;
       if constexpr (DX) {
         const int mr = v / (kBR / 8), cv = v % (kBR / 8);
-        *(uint4*)(A + mr * PA + 8 * cv) = ra[i];
+        *(uint4*)(A + mr * PA + 8 * cv) = g.ra[i];
       } else {
         const int rr = v / (BM / 8), cv = v % (BM / 8);
-        *(uint4*)(A + rr * PA + 8 * cv) = ra[i];
+        *(uint4*)(A + rr * PA + 8 * cv) = g.ra[i];
       }
     }
     if constexpr (MODE == kModeDw) {
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd(const BwdArgs a) {
       for (int i = 0; i < 2 * NWB; ++i) {
         const int v = threadIdx.x + i * kThreads;
         const int rr = v / (BN / 8), cv = v % (BN / 8);
-        *(uint4*)(B + rr * PB + 8 * cv) = rb[i];
+        *(uint4*)(B + rr * PB + 8 * cv) = g.rb[i];
       }
     } else {
 #pragma unroll
@@ -233,8 +237,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd(const BwdArgs a) {
         const int v = threadIdx.x + i * kThreads;
         const int rr = v / (BN / 16), cw = v % (BN / 16);
         uint4 lo, hi;
-        if constexpr (MODE == kModeDxDense) decode_dense16(rb[i].x, lo, hi);
-        else decode_index16(rb[i].x, rb[i].y, ((n0 + 16 * cw) >> 4) & 1, lo, hi);
+        if constexpr (MODE == kModeDxDense) decode_dense16(g.rb[i].x, lo, hi);
+        else decode_index16(g.rb[i].x, g.rb[i].y, ((n0 + 16 * cw) >> 4) & 1, lo, hi);
         *(uint4*)(B + rr * PB + 16 * cw) = lo;
         *(uint4*)(B + rr * PB + 16 * cw + 8) = hi;
       }
@@ -264,15 +268,17 @@ __global__ __launch_bounds__(kThreads) void k_bwd(const BwdArgs a) {
       r_begin = r_end;
       continue;
     }
-    load(r_begin, r_end);
-    store(lds, lds + SA);
+    load(S0, r_begin, r_end);
+    store(S0, lds, lds + SA);
+    if (steps > 1) load(S1, r_begin + kBR, r_end);
+    if (steps > 2) load(S0, r_begin + 2 * kBR, r_end);
     __syncthreads();
-    for (int st = 0; st < steps; ++st) {
+    // step st: compute from LDS buffer st & 1; g holds step st + 1, which goes
+    // to the other buffer, and then takes the loads of step st + 3
+    auto step = [&](int st, Stage& g) {
       const int buf = st & 1;
       const uint16_t* A = lds + buf * (SA + SB);
       const uint16_t* B = A + SA;
-      const bool more = st + 1 < steps;
-      if (more) load(r_begin + (st + 1) * kBR, r_end);
 #pragma unroll
       for (int u = 0; u < kBR / 32; ++u) {
         bf16x8 fa[WMB], fb[WNB];
@@ -289,11 +295,16 @@ __global__ __launch_bounds__(kThreads) void k_bwd(const BwdArgs a) {
           for (int j = 0; j < WNB; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
-      if (more) {
+      if (st + 1 < steps) {
         uint16_t* An = lds + (buf ^ 1) * (SA + SB);
-        store(An, An + SA);
+        store(g, An, An + SA);
+        if (st + 3 < steps) load(g, r_begin + (st + 3) * kBR, r_end);
       }
       __syncthreads();
+    };
+    for (int st = 0; st < steps; st += 2) {
+      step(st, S1);
+      if (st + 1 < steps) step(st + 1, S0);
     }
     if constexpr (MULTI) {
 #pragma unroll
@@ -403,12 +414,14 @@ hipError_t launch_cfg(BwdArgs a, hipStream_t s) {
 
 template <int MODE, bool MULTI>
 hipError_t launch_mode(const BwdArgs& a, int cfg, hipStream_t s) {
+  if constexpr (!MULTI) {   // (the large tiles with a second accumulator set would spill)
+    if (cfg == 3) return launch_cfg<MODE, 8, 4, MULTI>(a, s);
+    if (cfg == 4) return launch_cfg<MODE, 4, 8, MULTI>(a, s);
+  }
   switch (cfg) {
-    case 0: return launch_cfg<MODE, 4, 4, MULTI>(a, s);
     case 1: return launch_cfg<MODE, 2, 4, MULTI>(a, s);
-    case 3: return launch_cfg<MODE, 8, 4, MULTI>(a, s);
-    case 4: return launch_cfg<MODE, 4, 8, MULTI>(a, s);
-    default: return launch_cfg<MODE, 2, 2, MULTI>(a, s);
+    case 2: return launch_cfg<MODE, 2, 2, MULTI>(a, s);
+    default: return launch_cfg<MODE, 4, 4, MULTI>(a, s);
   }
 }
 
