@@ -57,6 +57,7 @@ struct BwdArgs {
   int32_t nseg;          // dX: reduction segments of constant sw; dW: 1
   int32_t seg_end[4];    // end row of each segment (the first starts at 0)
   int32_t ntm, ntn;      // tiles along the output rows / columns
+  int32_t gm;            // tile rows per group of the tile order (see tile_of)
   int32_t out_bf16, accumulate;
 };
 
@@ -126,11 +127,24 @@ __device__ __forceinline__ void decode_index16(uint32_t cw, uint32_t iw, int h, 
   hi = make_uint4(out[4], out[5], out[6], out[7]);
 }
 
-// Block b of nb -> tile index, so that the blocks one XCD receives (b % 8)
-// cover a contiguous run of tiles (neighbours share operand tiles in L2).
+// Block b of nb -> position in the tile order, so that the blocks one XCD
+// receives (b % 8) take a contiguous run of it.
 __device__ __forceinline__ int xcd_tile(int b, int nb) {
   const int x = b & 7, i = b >> 3, q = nb >> 3, rem = nb & 7;
   return x * q + min(x, rem) + i;
+}
+
+// Position t of the tile order -> (tile row, tile column). Groups of gm tile
+// rows are taken one after another; inside a group the row index runs
+// fastest, so the workgroups an XCD runs at the same time cover gm rows and a
+// few columns and share both operands' panels in its L2 (gm is chosen on the
+// host from the panel sizes). A row-major order would re-read the whole of
+// the row operand from HBM once per few columns.
+__device__ __forceinline__ void tile_of(int t, int ntm, int ntn, int gm, int& tm, int& tn) {
+  const int g = t / (gm * ntn), r = t - g * gm * ntn;
+  const int rows = min(gm, ntm - g * gm);
+  tm = g * gm + r % rows;
+  tn = r / rows;
 }
 
 template <int MODE, int WMB, int WNB, bool MULTI>
@@ -147,8 +161,8 @@ __global__ __launch_bounds__(kThreads, (WMB * WNB > 16) ? 1 : 2) void k_bwd(cons
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int nb = a.ntm * a.ntn;
-  const int tile = xcd_tile(blockIdx.x, nb);
-  const int tm = tile % a.ntm, tn = tile / a.ntm;
+  int tm, tn;
+  tile_of(xcd_tile(blockIdx.x, nb), a.ntm, a.ntn, a.gm, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int Mrows = DX ? a.T : a.O;
 
@@ -407,6 +421,25 @@ hipError_t launch_cfg(BwdArgs a, hipStream_t s) {
   }
   a.ntm = (int32_t)cdiv(DX ? a.T : a.O, BM);
   a.ntn = (int32_t)cdiv(a.K, BN);
+  // Tile-order group: about `conc` workgroups run at once on an XCD (two or
+  // four per CU, 32 CUs); a group of gm rows lets them share gm row panels
+  // and conc / gm column panels. Pick gm to minimize the panel bytes fetched
+  // beyond L2: each row panel once per conc/gm columns, each column panel
+  // once per group.
+  {
+    const int64_t R = DX ? a.O : a.T;
+    const double rowp = (double)BM * R * 2;                          // dY panel
+    const double colp = DX ? (double)BN * R / 4 : (double)BN * R * 2;  // W codes / x~ panel
+    const int conc = 32 * (BM * BN >= 128 * 128 ? 2 : 4);
+    double best = 0;
+    for (int gm = 1; gm <= 64; gm *= 2) {
+      const int g = (int)std::min<int64_t>(gm, a.ntm);
+      const int gn = std::max(1, conc / g);
+      const double cost = a.ntm * rowp * (double)cdiv(a.ntn, gn) + a.ntn * colp * (double)cdiv(a.ntm, g);
+      if (gm == 1 || cost < best) { best = cost; a.gm = g; }
+    }
+    if (const char* ev = std::getenv("SBL_BWD_GROUP")) a.gm = std::max(1, std::min(std::atoi(ev), a.ntm));
+  }
   const int64_t nb = (int64_t)a.ntm * a.ntn;
   hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(kThreads), lds, s, a);
   return hipGetLastError();

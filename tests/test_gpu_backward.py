@@ -145,6 +145,17 @@ def test_bwd_dw_every_tile_config(S, cfg, monkeypatch):
         _dw_case(S, T, O, K, False, seed=cfg + T)
 
 
+@pytest.mark.parametrize("group", [1, 3, 7, 64])
+def test_bwd_tile_order_groups(S, group, monkeypatch):
+    """The grouped tile order forced to several group sizes (ragged last
+    groups included): every tile is computed exactly once."""
+    monkeypatch.setenv("SBL_BWD_GROUP", str(group))
+    log_case("bwd tile order", group)
+    _dx_case(S, 300, 264, 520, 6, 8, False, seed=group)
+    _dx_case(S, 130, 392, 264, 2, 4, False, seed=group + 1)
+    _dw_case(S, 150, 520, 392, False, seed=group + 2)
+
+
 def test_bwd_empty_and_zero_tokens(S):
     """T = 0: dW is all zeros (an empty sum); dX is left as it is."""
     log_case("bwd empty")
