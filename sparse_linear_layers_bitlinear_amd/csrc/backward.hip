@@ -28,6 +28,7 @@
 #include "device_util.cuh"
 
 #include <algorithm>
+#include <type_traits>
 #include <cstdlib>
 
 namespace sbl {
@@ -361,6 +362,157 @@ __global__ __launch_bounds__(kThreads, (WMB * WNB > 16) ? 1 : 2) void k_bwd(cons
       }
 }
 
+// ---------------------------------------------------------------------------
+// dW with direct global-to-LDS loads. Staging through registers (load, wait,
+// write LDS) costs about as much as the products themselves here; the LDS DMA
+// (global_load_lds, 16 bytes per lane) lands the operands without the waves'
+// instructions, so the ring can run kDmaStages steps ahead.
+//   Tile 128x128 (2 x 2 waves of 64x64), steps of 32 rows of T.
+//   LDS: kDmaStages slots of {dY tile, x~ tile}, each 32 rows x 256 bytes, no
+//   padding (one DMA instruction fills 4 whole rows); bank conflicts of the
+//   transposed reads are avoided by XOR-swizzling the 16-byte chunks of a
+//   row: chunk c of row r sits at c ^ (2 (r mod 8)).
+//   Rows past the tile edges are loaded from clamped (valid) addresses: they
+//   only reach outputs that are not written. Rows past T in the last step
+//   would reach real outputs, so that step's x~ rows past T are zeroed in
+//   LDS after their loads land.
+// ---------------------------------------------------------------------------
+constexpr int kDmaBR = 32, kDmaStages = 4;
+constexpr int kDmaSlotElems = 2 * kDmaBR * 128;            // dY tile + x~ tile
+
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (2 * (r & 7)); }
+
+__device__ __forceinline__ void dma16(const void* g, uint16_t* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Wait until at most N DMAs of this wave are outstanding (and all its LDS
+// operations are done), then barrier. The empty asm statements keep the
+// compiler from moving memory accesses across.
+template <int N>
+__device__ __forceinline__ void dma_wait_barrier() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Transposed fragment (kPermHalf) of strip s from a swizzled 32 x 128 tile.
+__device__ __forceinline__ bf16x8 frag_swz(const uint16_t* tile, int col0, int s, int lane) {
+  const int g = lane >> 4, k = lane & 15;
+  const int r0 = 4 * g + (k >> 2), r1 = r0 + 16;
+  const int col = col0 + 16 * s + 4 * (k & 3);
+  const int c = col >> 3, e = col & 7;
+  return join(lds_tr(tile + r0 * 128 + 8 * swz(r0, c) + e), lds_tr(tile + r1 * 128 + 8 * swz(r1, c) + e));
+}
+
+// The four ring slots are separate LDS objects, each named at compile time
+// (the loop is unrolled by four): the compiler then knows that a read of one
+// slot does not depend on the DMAs still landing in the others, and does not
+// drain them before every read.
+__shared__ __align__(16) uint16_t dma_slot0[kDmaSlotElems];
+__shared__ __align__(16) uint16_t dma_slot1[kDmaSlotElems];
+__shared__ __align__(16) uint16_t dma_slot2[kDmaSlotElems];
+__shared__ __align__(16) uint16_t dma_slot3[kDmaSlotElems];
+static_assert(kDmaStages == 4, "one named slot per stage");
+
+template <int I>
+__device__ __forceinline__ uint16_t* dma_slot() {
+  if constexpr (I == 0) return dma_slot0;
+  else if constexpr (I == 1) return dma_slot1;
+  else if constexpr (I == 2) return dma_slot2;
+  else return dma_slot3;
+}
+
+__global__ __launch_bounds__(kThreads, 2) void k_bwd_dw_dma(const BwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_of(xcd_tile(blockIdx.x, a.ntm * a.ntn), a.ntm, a.ntn, a.gm, tm, tn);
+  const int m0 = tm * 128, n0 = tn * 128;
+  const int T = a.T, steps = (T + kDmaBR - 1) / kDmaBR;
+  const uint16_t* __restrict__ xt = (const uint16_t*)a.b;
+
+  // DMA i of the wave fills rows 4 (2 wave + i) .. + 3 of a tile; lane l
+  // takes row + l / 16, physical chunk l % 16 (logical chunk swz of it)
+  auto issue = [&](uint16_t* slot, int st) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 4 * (2 * wave + i) + (lane >> 4);
+      const int c = swz(r, lane & 15);
+      const int t = min(st * kDmaBR + r, T - 1);
+      const int o = min(m0 + 8 * c, a.O - 8), k = min(n0 + 8 * c, a.K - 8);
+      dma16(a.dy + (int64_t)t * a.ldy + o, slot + 4 * (2 * wave + i) * 128);
+      dma16(xt + (int64_t)t * a.ldb + k, slot + kDmaBR * 128 + 4 * (2 * wave + i) * 128);
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // step st (st % 4 == I): wait for its slot, refill the slot of step st - 1
+  // with step st + 3, compute
+  auto body = [&](auto I_, int st) {
+    constexpr int I = decltype(I_)::value;
+    if (st >= steps) return;
+    // at most the DMAs of the later issued steps (4 per step and wave) may
+    // still be outstanding
+    const int later = min(kDmaStages - 2, steps - 1 - st);
+    if (later >= 2) dma_wait_barrier<8>();
+    else if (later == 1) dma_wait_barrier<4>();
+    else dma_wait_barrier<0>();
+    if (st + kDmaStages - 1 < steps) issue(dma_slot<(I + kDmaStages - 1) % kDmaStages>(), st + kDmaStages - 1);
+    uint16_t* slot = dma_slot<I>();
+    const int valid = T - st * kDmaBR;
+    if (valid < kDmaBR) {                                    // last step: zero x~ rows >= T
+      uint16_t* xs = slot + kDmaBR * 128;
+      for (int v = threadIdx.x; v < (kDmaBR - valid) * 16; v += kThreads)
+        *(uint4*)(xs + (valid + v / 16) * 128 + 8 * (v % 16)) = make_uint4(0, 0, 0, 0);
+      __syncthreads();
+    }
+    bf16x8 fa[4], fb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = frag_swz(slot, wm * 64, i, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = frag_swz(slot + kDmaBR * 128, wn * 64, j, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  if (steps > 0) issue(dma_slot<0>(), 0);
+  if (steps > 1) issue(dma_slot<1>(), 1);
+  if (steps > 2) issue(dma_slot<2>(), 2);
+  for (int st = 0; st < steps; st += 4) {
+    body(std::integral_constant<int, 0>{}, st);
+    body(std::integral_constant<int, 1>{}, st + 1);
+    body(std::integral_constant<int, 2>{}, st + 2);
+    body(std::integral_constant<int, 3>{}, st + 3);
+  }
+
+  const int rbase = m0 + wm * 64 + 4 * (lane >> 4);
+  const int cbase = n0 + wn * 64 + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = rbase + 16 * i + e, col = cbase + 16 * j;
+        if (row >= a.O || col >= a.K) continue;
+        const int64_t off = (int64_t)row * a.ldo + col;
+        if (a.out_bf16) ((uint16_t*)a.out)[off] = (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
+        else ((float*)a.out)[off] = acc[i][j][e];
+      }
+}
+
 // x~ = bf16_rne(fp32(q) * sx[t]); 8 codes per thread (K % 8 == 0).
 __global__ __launch_bounds__(256) void k_act_dequant(const int8_t* __restrict__ xq,
                                                       const float* __restrict__ sx, int64_t T,
@@ -402,23 +554,7 @@ int pick_cfg(int64_t rows, int64_t cols) {
   return cdiv(rows, 128) * cdiv(cols, 128) >= want ? 0 : 2;
 }
 
-template <int MODE, int WMB, int WNB, bool MULTI>
-hipError_t launch_cfg(BwdArgs a, hipStream_t s) {
-  constexpr int BM = 32 * WMB, BN = 32 * WNB;
-  constexpr bool DX = MODE != kModeDw;
-  constexpr size_t SA = DX ? (size_t)BM * kPitchMM : (size_t)kBR * (BM + kPadRM);
-  constexpr size_t SB = (size_t)kBR * (BN + kPadRM);
-  constexpr size_t lds = 2 * (SA + SB) * sizeof(uint16_t);
-  auto kern = k_bwd<MODE, WMB, WNB, MULTI>;
-  if (lds > 65536) {
-    static bool set = false;
-    if (!set) {
-      const hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      set = true;
-    }
-  }
+void set_order(BwdArgs& a, int BM, int BN, bool DX) {
   a.ntm = (int32_t)cdiv(DX ? a.T : a.O, BM);
   a.ntn = (int32_t)cdiv(a.K, BN);
   // Tile-order group: about `conc` workgroups run at once on an XCD (two or
@@ -440,6 +576,26 @@ hipError_t launch_cfg(BwdArgs a, hipStream_t s) {
     }
     if (const char* ev = std::getenv("SBL_BWD_GROUP")) a.gm = std::max(1, std::min(std::atoi(ev), a.ntm));
   }
+}
+
+template <int MODE, int WMB, int WNB, bool MULTI>
+hipError_t launch_cfg(BwdArgs a, hipStream_t s) {
+  constexpr int BM = 32 * WMB, BN = 32 * WNB;
+  constexpr bool DX = MODE != kModeDw;
+  constexpr size_t SA = DX ? (size_t)BM * kPitchMM : (size_t)kBR * (BM + kPadRM);
+  constexpr size_t SB = (size_t)kBR * (BN + kPadRM);
+  constexpr size_t lds = 2 * (SA + SB) * sizeof(uint16_t);
+  auto kern = k_bwd<MODE, WMB, WNB, MULTI>;
+  if (lds > 65536) {
+    static bool set = false;
+    if (!set) {
+      const hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      set = true;
+    }
+  }
+  set_order(a, BM, BN, DX);
   const int64_t nb = (int64_t)a.ntm * a.ntn;
   hipLaunchKernelGGL(kern, dim3((unsigned)nb), dim3(kThreads), lds, s, a);
   return hipGetLastError();
@@ -494,6 +650,12 @@ hipError_t launch_bwd_dw(const uint16_t* dy, int64_t ldy, const uint16_t* xt, in
   a.nseg = 1; a.seg_end[0] = (int32_t)T;
   a.out_bf16 = dw_bf16; a.accumulate = 0;
   if (cfg < 0) cfg = pick_cfg(O, K);
+  const char* ev = std::getenv("SBL_BWD_DMA");   // tuning: 0 keeps the register-staged kernel
+  if (cfg == 0 && !(ev && ev[0] == '0')) {
+    set_order(a, 128, 128, false);
+    hipLaunchKernelGGL(k_bwd_dw_dma, dim3((unsigned)(a.ntm * a.ntn)), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
   return launch_mode<kModeDw, false>(a, cfg, s);
 }
 

@@ -140,9 +140,23 @@ def test_bwd_dw_parity(S, out_bf16):
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_bwd_dw_every_tile_config(S, cfg, monkeypatch):
     monkeypatch.setenv("SBL_BWD_TILE", str(cfg))
+    monkeypatch.setenv("SBL_BWD_DMA", "0")                 # the register-staged kernel
     for T, O, K in [(150, 264, 392), (64, 520, 136)]:
         log_case("bwd_dw tile", cfg, T, O, K)
         _dw_case(S, T, O, K, False, seed=cfg + T)
+
+
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_bwd_dw_dma_kernel(S, out_bf16, monkeypatch):
+    """The 128x128 dW kernel with direct-to-LDS loads: T tails of every size
+    class (one row, one past a step, many steps), tiles smaller than O and K
+    (clamped edge loads), several tile-order groups."""
+    monkeypatch.setenv("SBL_BWD_TILE", "0")
+    for T, O, K, grp in [(1, 8, 8, 1), (33, 136, 264, 1), (150, 264, 392, 3), (97, 8, 16, 1),
+                         (300, 392, 520, 2), (256, 128, 128, 1)]:
+        monkeypatch.setenv("SBL_BWD_GROUP", str(grp))
+        log_case("bwd_dw dma", out_bf16, T, O, K, grp)
+        _dw_case(S, T, O, K, out_bf16, seed=T + O + K)
 
 
 @pytest.mark.parametrize("group", [1, 3, 7, 64])
