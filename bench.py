@@ -63,6 +63,9 @@ def parse():
     p.add_argument("--backward", action="store_true",
                    help="prefill: the step adds the Dual-STE backward of every projection (x~ in "
                         "bf16, dX and dW on the bf16 matrix cores) to the forward: a training step")
+    p.add_argument("--mask-gated-grad", action="store_true",
+                   help="with --backward: the ablated estimator, dW gated by the mask (the weight "
+                        "preparation also writes the keep bits)")
     p.add_argument("--mask-then-quant", action="store_true",
                    help="prefill: the composition-order ablation, gamma over the kept weights only")
     p.add_argument("--diagnostics", action="store_true",
@@ -76,10 +79,10 @@ def parse():
 # ---------------------------------------------------------------- prefill --
 class PrefillStep:
     def __init__(self, wl_name, N, M, diagnostics=False, fused_norm=False, variant=0,
-                 backward=False):
+                 backward=False, gated=False):
         wl = WORKLOADS[wl_name]
         self.wl, self.N, self.M, self.diag, self.norm = wl, N, M, diagnostics, fused_norm
-        self.bwd = backward
+        self.bwd, self.gated = backward, gated and backward
         W, X = make_workload(wl_name)
         dev = torch.device("cuda:0")
         self.T = wl.T
@@ -144,6 +147,18 @@ class PrefillStep:
                 self.dx[xn] = torch.empty((self.T, K), dtype=torch.bfloat16, device=dev)
                 self.dw[xn] = torch.empty((O, K), dtype=torch.float32, device=dev)
             self.ops *= 3.0       # forward + dX + dW, each 2 T O K per projection
+            self.keep = {}
+            if self.gated:
+                # the preparation writes each weight's keep bits into its group's buffer
+                items = iter(self.prep_items)
+                for xn, lins in self.groups.items():
+                    C = -(-self.K_of[xn] // 128) * 4
+                    self.keep[xn] = torch.empty((sum(l.O for l in lins), C), dtype=torch.int32,
+                                                device=dev)
+                    off = 0
+                    for l in lins:
+                        next(items)["mask_bits"] = self.keep[xn][off:off + l.O]
+                        off += l.O
 
     def calls(self):
         """The step as an ordered list of (name, launch) pairs."""
@@ -172,7 +187,7 @@ class PrefillStep:
                     self.dy[xn], self.packed[xn], self.swr[xn], K, N, M,
                     seg_rows=[l.O for l in lins], dx=self.dx[xn])))
                 out.append((f"bwd_dw[{tag}]", lambda xn=xn: sbl.sbl_linear_bwd_dw(
-                    self.dy[xn], self.xt[xn], dw=self.dw[xn])))
+                    self.dy[xn], self.xt[xn], dw=self.dw[xn], keep_bits=self.keep.get(xn))))
         return out
 
     cold_weights = False   # inputs of every call were just written by the step: cache-hot
@@ -213,7 +228,8 @@ class PrefillStep:
         # weight preparation: W read twice (absmean pass, mask/code pass), packed written;
         # with diagnostics also the keep bits written, the previous ones read, the thresholds
         diag = sum(2.0 * 4 * l.O * (-(-l.K // 128) * 4) + 4.0 * l.O * l.K / self.M
-                   for l in self.wl.linears) if self.diag else 0.0
+                   for l in self.wl.linears) if self.diag else (
+            sum(4.0 * l.O * (-(-l.K // 128) * 4) for l in self.wl.linears) if self.gated else 0.0)
         return "hbm", diag + sum(2.0 * l.O * l.K * self.W[l.name].element_size() +
                                  sbl.sbl_packed_bytes(l.O, l.K, self.N, self.M)
                                  for l in self.wl.linears), "bytes"
@@ -477,7 +493,8 @@ def traffic_tag(a, N, M):
         return f"bitnet_decode T={a.decode_T} L={a.layers}"
     return (f"{a.workload} T={WORKLOADS[a.workload].T} {N}:{M}" + (" diag" if a.diagnostics else "")
             + (" norm" if a.fused_norm else "") + (" ternary-mask" if a.mask_from_ternary else "")
-            + (" mask-then-quant" if a.mask_then_quant else "") + (" backward" if a.backward else ""))
+            + (" mask-then-quant" if a.mask_then_quant else "") + (" backward" if a.backward else "")
+            + (" gated" if a.mask_gated_grad and a.backward else ""))
 
 
 def per_call_rates(step, per_call):
@@ -520,7 +537,7 @@ def main():
     else:
         step = PrefillStep(a.workload, N, M, a.diagnostics, a.fused_norm,
                            1 if a.mask_from_ternary else 2 if a.mask_then_quant else 0,
-                           a.backward)
+                           a.backward, a.mask_gated_grad)
     ms = time_steps(step, a.steps, a.warmup, a.eager)
     per_call, calls_per_step = per_call_times(step, max(5, min(a.steps, 20)))
     share = {k: per_call[k] * calls_per_step[k] for k in per_call}
@@ -559,7 +576,9 @@ def main():
                   "composition": "mask-then-quant (ablation)" if a.mask_then_quant else "quant-then-mask",
                   "projections": [f"{l.name} {l.O}x{l.K}" for l in wl.linears],
                   "mask": "recomputed every step", "dense_equiv_ops_per_step": step.ops,
-                  "backward": bool(a.backward)}
+                  "backward": bool(a.backward),
+                  "gradient": ("mask-gated (ablation)" if a.mask_gated_grad and a.backward else
+                               "dense (Dual STE)") if a.backward else None}
     out = {
         "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),

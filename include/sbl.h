@@ -318,9 +318,16 @@ sbl_status sbl_linear_bwd_dx(const void* dy, int64_t ldy, const void* packed, co
  * dy: device bf16 [T, ldy]; xt: device bf16 [T,K] from sbl_act_dequant;
  * dw: device [O,K] of dwdt, overwritten (T = 0 writes zeros; dy and xt may
  * then be NULL).
+ * keep_bits: NULL for the method. Non-NULL selects the gated estimator the
+ * pages ablate against it (section 3.4 "Gradient Estimation", the
+ * mask-gated gradients of prior sparse training, "mask without grad" in
+ * Figure 3): dW = M (.) dY^T x~, zero wherever the mask prunes. Layout as
+ * sbl_weight_prep.mask_bits: device uint32 [O][ceil(K/128)*4], bit e of word
+ * c of row o = M[o, 32c + e].
  */
 sbl_status sbl_linear_bwd_dw(const void* dy, int64_t ldy, const void* xt, int64_t T, int64_t O,
-                             int64_t K, void* dw, sbl_dtype dwdt, hipStream_t stream);
+                             int64_t K, const uint32_t* keep_bits, void* dw, sbl_dtype dwdt,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

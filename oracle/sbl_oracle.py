@@ -278,10 +278,15 @@ def linear_bwd_dx(dy: np.ndarray, w_eff: np.ndarray, sw) -> np.ndarray:
     return np.asarray(dy, dtype=np.float64) @ (w_eff.astype(np.float64) * sw[:, None])
 
 
-def linear_bwd_dw(dy: np.ndarray, xt: np.ndarray) -> np.ndarray:
+def linear_bwd_dw(dy: np.ndarray, xt: np.ndarray, mask=None) -> np.ndarray:
     """dW[o, k] = sum_t dY[t, o] * x~[t, k], in fp64, at every (o, k): the
-    gradient at W~, passed to the master weights whether kept or pruned."""
-    return np.asarray(dy, dtype=np.float64).T @ np.asarray(xt, dtype=np.float64)
+    gradient at W~, passed to the master weights whether kept or pruned.
+
+    mask: the estimator [SB] "Gradient Estimation" ablates against (the
+    mask-gated gradients of prior N:M training; "mask without grad" in
+    Figure 3): dW = M (.) dY^T x~, zero at every pruned weight."""
+    dw = np.asarray(dy, dtype=np.float64).T @ np.asarray(xt, dtype=np.float64)
+    return dw if mask is None else dw * (np.asarray(mask) != 0)
 
 
 # ---------------------------------------------------------------------------

@@ -60,7 +60,17 @@ struct BwdArgs {
   int32_t ntm, ntn;      // tiles along the output rows / columns
   int32_t gm;            // tile rows per group of the tile order (see tile_of)
   int32_t out_bf16, accumulate;
+  const uint32_t* keep;  // dW only: keep bits [O][keep_pitch] (gated ablation) or null
+  int32_t keep_pitch;
 };
+
+// The gated-gradient ablation: dW is kept only where the mask keeps the
+// weight (bit col % 32 of word col / 32 of the row's keep bits).
+__device__ __forceinline__ float gate_keep(const BwdArgs& a, int row, int col, float v) {
+  if (a.keep == nullptr) return v;
+  const uint32_t w = a.keep[(int64_t)row * a.keep_pitch + (col >> 5)];
+  return ((w >> (col & 31)) & 1u) ? v : 0.f;
+}
 
 __device__ __forceinline__ i16x4 lds_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
@@ -348,7 +358,7 @@ __global__ __launch_bounds__(kThreads, (WMB * WNB > 16) ? 1 : 2) void k_bwd(cons
         if (row >= Mrows || col >= a.K) continue;
         float v;
         if constexpr (MULTI) v = tot[i][j][e];
-        else v = DX ? sw * acc[i][j][e] : acc[i][j][e];
+        else v = DX ? sw * acc[i][j][e] : gate_keep(a, row, col, acc[i][j][e]);
         const int64_t off = (int64_t)row * a.ldo + col;
         if (a.out_bf16) {
           uint16_t* o = (uint16_t*)a.out + off;
@@ -508,8 +518,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dw_dma(const BwdArgs a) {
         const int row = rbase + 16 * i + e, col = cbase + 16 * j;
         if (row >= a.O || col >= a.K) continue;
         const int64_t off = (int64_t)row * a.ldo + col;
-        if (a.out_bf16) ((uint16_t*)a.out)[off] = (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
-        else ((float*)a.out)[off] = acc[i][j][e];
+        const float v = gate_keep(a, row, col, acc[i][j][e]);
+        if (a.out_bf16) ((uint16_t*)a.out)[off] = (uint16_t)f32_to_bf16_bits(v);
+        else ((float*)a.out)[off] = v;
       }
 }
 
@@ -642,9 +653,11 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t ldy, const void* packed, co
 }
 
 hipError_t launch_bwd_dw(const uint16_t* dy, int64_t ldy, const uint16_t* xt, int64_t ldxt,
-                         int64_t T, int64_t O, int64_t K, void* dw, bool dw_bf16, int64_t lddw,
-                         int cfg, hipStream_t s) {
+                         int64_t T, int64_t O, int64_t K, const uint32_t* keep, void* dw,
+                         bool dw_bf16, int64_t lddw, int cfg, hipStream_t s) {
   BwdArgs a{};
+  a.keep = keep;
+  a.keep_pitch = (int32_t)row_chunks(K);
   a.dy = dy; a.ldy = ldy; a.b = xt; a.ldb = ldxt; a.sw_rows = nullptr;
   a.out = dw; a.ldo = lddw; a.T = (int32_t)T; a.O = (int32_t)O; a.K = (int32_t)K;
   a.nseg = 1; a.seg_end[0] = (int32_t)T;

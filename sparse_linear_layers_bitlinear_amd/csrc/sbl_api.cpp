@@ -360,14 +360,17 @@ sbl_status sbl_linear_bwd_dx(const void* dy, int64_t ldy, const void* packed, co
 }
 
 sbl_status sbl_linear_bwd_dw(const void* dy, int64_t ldy, const void* xt, int64_t T, int64_t O,
-                             int64_t K, void* dw, sbl_dtype dwdt, hipStream_t stream) {
+                             int64_t K, const uint32_t* keep_bits, void* dw, sbl_dtype dwdt,
+                             hipStream_t stream) {
   if (!dtype_ok(dwdt)) return SBL_ERR_DTYPE;
   sbl_status st = check_bwd_shape(ldy, T, O, K);
   if (st != SBL_OK) return st;
   if (!dw || (T > 0 && (!dy || !xt))) return SBL_ERR_NULL;
-  if ((dy && !aligned16(dy)) || (xt && !aligned16(xt)) || !aligned16(dw)) return SBL_ERR_ALIGN;
-  return hip_status(launch_bwd_dw((const uint16_t*)dy, ldy, (const uint16_t*)xt, K, T, O, K, dw,
-                                  dwdt == SBL_BF16, K, -1, stream),
+  if ((dy && !aligned16(dy)) || (xt && !aligned16(xt)) || !aligned16(dw) ||
+      (keep_bits && !aligned16(keep_bits)))
+    return SBL_ERR_ALIGN;
+  return hip_status(launch_bwd_dw((const uint16_t*)dy, ldy, (const uint16_t*)xt, K, T, O, K,
+                                  keep_bits, dw, dwdt == SBL_BF16, K, -1, stream),
                     "sbl_linear_bwd_dw");
 }
 

@@ -87,10 +87,11 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t ldy, const void* packed, co
                          int64_t T, int64_t O, int64_t K, int N, int M, const int64_t* seg_end,
                          int nseg, void* dx, bool dx_bf16, int64_t lddx, bool accumulate,
                          int cfg, hipStream_t s);
-// dW [O,K] = dY^T x~ (dY [T, ldy] bf16, x~ [T, ldxt] bf16).
+// dW [O,K] = dY^T x~ (dY [T, ldy] bf16, x~ [T, ldxt] bf16); keep: optional
+// keep bits [O][row_chunks(K)] gating dW (the ablated estimator).
 hipError_t launch_bwd_dw(const uint16_t* dy, int64_t ldy, const uint16_t* xt, int64_t ldxt,
-                         int64_t T, int64_t O, int64_t K, void* dw, bool dw_bf16, int64_t lddw,
-                         int cfg, hipStream_t s);
+                         int64_t T, int64_t O, int64_t K, const uint32_t* keep, void* dw,
+                         bool dw_bf16, int64_t lddw, int cfg, hipStream_t s);
 
 bool decode_fits(int64_t T, int64_t O, int64_t K, int N, int M, int xmode);
 hipError_t launch_decode(const void* x, int xmode, const float* sx, float eps, const void* packed,

@@ -67,7 +67,7 @@ def _load():
         "sbl_act_dequant": ([P, P, I64, I64, P, P], I),
         "sbl_linear_bwd_dx": ([P, I64, P, P, I64, I64, I64, I, I, ctypes.POINTER(I64), I, P, I,
                                I64, I, P], I),
-        "sbl_linear_bwd_dw": ([P, I64, P, I64, I64, I64, P, I, P], I),
+        "sbl_linear_bwd_dw": ([P, I64, P, I64, I64, I64, P, P, I, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -311,12 +311,15 @@ def sbl_linear_bwd_dx(dy: torch.Tensor, packed: torch.Tensor, sw_rows: torch.Ten
 
 
 def sbl_linear_bwd_dw(dy: torch.Tensor, xt: torch.Tensor, O: int | None = None,
-                      out_dtype=torch.float32, dw=None):
-    """dW = dY^T x~ ([O, K]); dy bf16 [T, >= O], xt bf16 [T, K]."""
+                      out_dtype=torch.float32, dw=None, keep_bits=None):
+    """dW = dY^T x~ ([O, K]); dy bf16 [T, >= O], xt bf16 [T, K]. keep_bits
+    (uint32/int32 [O, ceil(K/128)*4], as the weight preparation's mask_bits)
+    selects the mask-gated ablation."""
     T, K = xt.shape
     O = dy.shape[1] if O is None else O
     dev = xt.device
     dw = torch.empty((O, K), dtype=out_dtype, device=dev) if dw is None else dw
     _check("sbl_linear_bwd_dw", _lib.sbl_linear_bwd_dw(
-        _ptr(dy), dy.stride(0), _ptr(xt), T, O, K, _ptr(dw), _dt(dw.dtype), _stream(dev)))
+        _ptr(dy), dy.stride(0), _ptr(xt), T, O, K, _ptr(keep_bits), _ptr(dw), _dt(dw.dtype),
+        _stream(dev)))
     return dw

@@ -210,8 +210,8 @@ def test_backward_validation(S):
     assert dx(sw=None) == 1
     assert dx(out=MIS) == 5
     assert dx(dy=MIS) == 5
-    dw = lambda dy=FAKE, ldy=256, xt=FAKE, T=32, O=256, K=128, out=FAKE, dt=1: \
-        L.sbl_linear_bwd_dw(dy, ldy, xt, T, O, K, out, dt, None)
+    dw = lambda dy=FAKE, ldy=256, xt=FAKE, T=32, O=256, K=128, out=FAKE, dt=1, keep=None: \
+        L.sbl_linear_bwd_dw(dy, ldy, xt, T, O, K, keep, out, dt, None)
     assert dw(dt=2) == 4
     assert dw(O=0) == 2
     assert dw(K=100) == 2
@@ -219,6 +219,7 @@ def test_backward_validation(S):
     assert dw(out=None) == 1
     assert dw(xt=None) == 1
     assert dw(xt=MIS) == 5
+    assert dw(keep=MIS) == 5                                # keep bits misaligned
     assert L.sbl_act_dequant(FAKE, FAKE, 4, 12, FAKE, None) == 2   # K % 8
     assert L.sbl_act_dequant(FAKE, FAKE, 0, 16, None, None) == 0   # empty
     assert L.sbl_act_dequant(FAKE, None, 4, 16, FAKE, None) == 1

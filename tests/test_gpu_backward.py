@@ -170,12 +170,41 @@ def test_bwd_tile_order_groups(S, group, monkeypatch):
     _dw_case(S, 150, 520, 392, False, seed=group + 2)
 
 
+@pytest.mark.parametrize("N,M", [(6, 8), (2, 4), (8, 8)])
+@pytest.mark.parametrize("cfg", [0, 2])
+def test_bwd_dw_mask_gated(S, N, M, cfg, monkeypatch):
+    """The gated-gradient ablation: dW with the weight preparation's keep bits
+    equals the oracle's M (.) dW (M from the oracle's own mask), and is the
+    dense dW exactly wherever the mask keeps the weight."""
+    monkeypatch.setenv("SBL_BWD_TILE", str(cfg))
+    rng = np.random.default_rng(N + cfg)
+    for T, O, K in [(150, 264, 392), (33, 136, 264)]:
+        if K % M:
+            continue
+        log_case("bwd_dw gated", N, M, cfg, T, O, K)
+        W, x = make_linear_inputs(T, O, K, seed=T + N)
+        x = bf16_round(x)
+        prep = S.sbl_quant_mask_weight_batch([{"w": to_dev(W), "want_mask_bits": True}], N, M)[0]
+        xq, sx = S.sbl_quant_act(bf16_tensor(x))
+        xt = S.sbl_act_dequant(xq, sx)
+        dy = _dy(rng, T, O)
+        dyt = bf16_tensor(dy)
+        gated = host(S.sbl_linear_bwd_dw(dyt, xt, keep_bits=prep["mask_bits"]))
+        dense = host(S.sbl_linear_bwd_dw(dyt, xt))
+        mask = o.nm_mask(W, N, M)
+        assert np.array_equal(gated, np.where(mask == 1, dense, 0.0).astype(np.float32))
+        oxt = o.act_dequant_bf16(*o.quant_act(x))
+        ref = o.linear_bwd_dw(dy, oxt, mask=mask)
+        abs_sum = o.linear_bwd_dw(np.abs(dy), np.abs(oxt), mask=mask)
+        assert_grad_close(gated, ref, abs_sum, T, False)
+
+
 def test_bwd_empty_and_zero_tokens(S):
     """T = 0: dW is all zeros (an empty sum); dX is left as it is."""
     log_case("bwd empty")
     dev = torch.device("cuda:0")
     dw = torch.full((16, 24), 7.0, device=dev)
-    S.lib.sbl_linear_bwd_dw(None, 16, None, 0, 16, 24, S._ptr(dw), S.SBL_FP32, None)
+    S.lib.sbl_linear_bwd_dw(None, 16, None, 0, 16, 24, None, S._ptr(dw), S.SBL_FP32, None)
     assert np.array_equal(host(dw), np.zeros((16, 24), F32))
     dx = torch.full((0, 24), 1.0, device=dev)
     dy = torch.zeros((0, 16), dtype=torch.bfloat16, device=dev)

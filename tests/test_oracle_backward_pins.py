@@ -152,3 +152,30 @@ def test_act_dequant_bf16_rounding():
     assert np.all(err <= ulp / 2)                               # half a bf16 step
     assert np.any(err > ulp / 4)                                # and not exact
     assert np.array_equal(r.astype(F32), bf16_round(v))   # bf16-representable
+
+
+def test_bwd_mask_gated_estimator():
+    """The gated ablation: exact finite differences of the loss in W~ where
+    the mask keeps the weight, zero where it prunes; with N = M it is the
+    dense gradient."""
+    rng = np.random.default_rng(16)
+    T, O, K, N, M = 3, 4, 8, 6, 8
+    W, _ = make_linear_inputs(T, O, K, seed=9)
+    w_eff, mask, gamma, sw = o.quant_mask_weight(W, N, M)
+    xq = rng.integers(-128, 128, size=(T, K)).astype(np.int8)
+    xt = o.act_dequant_bf16(xq, np.array([0.5, 0.25, 2.0], F32))
+    dy = rng.integers(-3, 4, size=(T, O)).astype(np.float64)
+    gated = o.linear_bwd_dw(dy, xt, mask=mask)
+    DY, XT, WT = _fr(dy), _fr(xt), _fr(w_eff.astype(np.float64) * float(sw))
+    L0 = _loss(DY, XT, WT)
+    for oo in range(O):
+        for k in range(K):
+            if mask[oo, k]:
+                WT[oo][k] += 1
+                assert _loss(DY, XT, WT) - L0 == Fraction(float(gated[oo, k]))
+                WT[oo][k] -= 1
+            else:
+                assert gated[oo, k] == 0
+    full = o.nm_mask(W, 8, 8)
+    assert np.array_equal(o.linear_bwd_dw(dy, xt, mask=full), o.linear_bwd_dw(dy, xt))
+
