@@ -513,13 +513,13 @@ def per_call_rates(step, per_call):
         else:
             # effective (dense-equivalent) TOPS against the dense int8 peak; also the
             # algorithmic rate (kept weights only, x N/M) and, where the GEMM runs on
-            # the 2:4 sparse instruction (2:4), the fraction of its 2x peak
+            # the 2:4 sparse instruction (2:4, 2:8), the fraction of its 2x peak
             N, M = getattr(step, "N", None), getattr(step, "M", None)
             out[k] = {"us": round(ms * 1e3, 2), "TOPS": round(rate / 1e12, 1),
                       "frac": round(rate / 1e12 / PEAK_INT8_DENSE_TOPS, 4)}
             if N and M:
                 out[k]["algorithmic_TOPS"] = round(rate * N / M / 1e12, 1)
-                if (N, M) == (2, 4):
+                if (N, M) in ((2, 4), (2, 8)):
                     out[k]["frac_of_sparse_peak"] = round(rate / 1e12 / (2 * PEAK_INT8_DENSE_TOPS), 4)
     return out
 

@@ -36,12 +36,17 @@
  *     per byte, so one byte-permute turns them into four int8 values.
  *   Each row of W is one record of fixed pitch (sbl_packed_bytes / O), so
  *   packed buffers of several tensors with the same K concatenate along O.
- *   INDEX FORM (N=2, M=4; feeds the gfx950 2:4 sparse MFMA directly):
- *     pitch = ceil(K/128)*32 bytes. Chunk c (k in [32c, 32c+32), 8 groups q of
- *     4) is two little-endian uint32: word 0 holds, as byte-sliced field
- *     v = 2q + j, the code of the j-th kept slot (ascending) of group q;
- *     word 1 holds the kept slot indices: bits [4q+1:4q] first, [4q+3:4q+2]
- *     second. Groups past K: slots (0,1), codes 0. 2 bits per weight.
+ *   INDEX FORM (N=2 with M=4 or M=8; feeds the gfx950 2:4 sparse MFMA
+ *     directly -- every 2:8 pattern is also a 2:4 pattern):
+ *     pitch = ceil(K/128)*32 bytes (+ ceil(K/128)*16 for M=8). Chunk c (k in
+ *     [32c, 32c+32), 8 groups q of 4) is two little-endian uint32: word 0
+ *     holds, as byte-sliced field v = 2q + j, the code of the j-th selected
+ *     slot (ascending) of group q; word 1 holds the selected slot indices:
+ *     bits [4q+1:4q] first, [4q+3:4q+2] second. The selected slots are the
+ *     kept ones; for 2:8 a group of 4 holding fewer than two kept slots is
+ *     completed with its lowest free slots (code 0), and ceil(K/128)*4 mask
+ *     words follow the chunks (bit j of word c = mask[32c + j]). Groups past
+ *     K: slots (0,1), codes 0. 2 bits per weight (2:8: 3).
  *   DENSE FORM (every other N:M):
  *     pitch = ceil(K/64)*16 + ceil(K/128)*16 bytes. First ceil(K/64)*4 uint32
  *     byte-sliced words of W_eff codes (word c: k = 16c + u as field u), then

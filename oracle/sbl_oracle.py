@@ -301,18 +301,23 @@ def linear_bwd_dw(dy: np.ndarray, xt: np.ndarray, mask=None) -> np.ndarray:
 # Byte-sliced word: 16 two-bit fields; field u sits at bit 8*(u%4) + 2*(u//4).
 # Rows are records of fixed pitch, concatenable along O.
 #
-# INDEX FORM (M = 4, N = 2): pitch = ceil(K/128) * 32 bytes. Chunk c covers
-#   k in [32c, 32c+32) = 8 groups q of 4; it is two little-endian uint32:
-#   word 0 (codes): compressed value v = 2q + j (j = 0, 1) holds the code of
-#   the j-th kept slot of group q (ascending), as field v of a byte-sliced
-#   word; word 1 (indices): bits [4q+1:4q] = first kept slot, [4q+3:4q+2] =
-#   second kept slot. Groups past K: slots (0, 1), codes 0.
+# INDEX FORM (N = 2 with M = 4 or M = 8): pitch = ceil(K/128) * 32 bytes,
+#   plus ceil(K/128) * 16 for M = 8. Chunk c covers k in [32c, 32c+32) = 8
+#   groups q of 4; it is two little-endian uint32: word 0 (codes): compressed
+#   value v = 2q + j (j = 0, 1) holds the code of the j-th selected slot of
+#   group q (ascending), as field v of a byte-sliced word; word 1 (indices):
+#   bits [4q+1:4q] = first selected slot, [4q+3:4q+2] = second. For 2:4 the
+#   selected slots are the kept ones. For 2:8 a group of 4 holds 0, 1 or 2 kept
+#   slots: they are selected, then the lowest unselected slots until there are
+#   two (their code is 0), and the mask follows the chunks as in the dense form
+#   (bit j of word c = mask[32c + j]), since the selection alone does not tell
+#   which slots were kept. Groups past K: slots (0, 1), codes 0.
 # DENSE FORM (every other N:M): pitch = ceil(K/64)*16 + ceil(K/128)*16 bytes.
 #   First ceil(K/64)*4 uint32 code words: word c holds W_eff codes of
 #   k = 16c + u as field u (byte-sliced); then ceil(K/128)*4 uint32 mask
 #   words: bit j of word c = mask[32c + j]. Everything past K is zero.
 def INDEX_FORM(N: int, M: int) -> bool:
-    return M == 4 and N == 2
+    return N == 2 and M in (4, 8)
 
 
 def _ceil(a, b):
@@ -321,7 +326,7 @@ def _ceil(a, b):
 
 def packed_row_bytes(K: int, N: int, M: int) -> int:
     if INDEX_FORM(N, M):
-        return _ceil(K, 128) * 32
+        return _ceil(K, 128) * 32 + (_ceil(K, 128) * 16 if M == 8 else 0)
     return _ceil(K, 64) * 16 + _ceil(K, 128) * 16
 
 
@@ -350,7 +355,12 @@ def pack(w_eff: np.ndarray, mask: np.ndarray, N: int, M: int) -> np.ndarray:
         pad.reshape(O, -1, 4)[:, :, :2] = 1                 # padding groups keep (0, 1)
         mk[:, K:] = pad
         g_c = c2.reshape(O, Kc // 4, 4)
-        g_m = mk.reshape(O, Kc // 4, 4)
+        g_m = mk.reshape(O, Kc // 4, 4).copy()
+        for _ in range(2):                                  # 2:8: select the lowest free slots
+            short = g_m.sum(axis=2) < 2
+            free = np.argmax(g_m == 0, axis=2)
+            rows, grp = np.nonzero(short)
+            g_m[rows, grp, free[rows, grp]] = 1
         assert np.all(g_m.sum(axis=2) == 2)
         i0 = np.argmax(g_m, axis=2)                         # first kept slot
         i1 = 3 - np.argmax(g_m[:, :, ::-1], axis=2)         # last kept slot
@@ -365,6 +375,12 @@ def pack(w_eff: np.ndarray, mask: np.ndarray, N: int, M: int) -> np.ndarray:
         cw = np.bitwise_or.reduce((c0 << _field_shift(2 * q))
                                   | (c1 << _field_shift(2 * q + 1)), axis=2)
         rec = np.stack([cw, idx], axis=2).reshape(O, -1).astype("<u4")
+        if M == 8:                                          # the 2:8 mask follows the chunks
+            mk8 = np.zeros((O, Kc), np.uint32)
+            mk8[:, :K] = mask
+            mw = np.bitwise_or.reduce(mk8.reshape(O, Kc // 32, 32)
+                                      << np.arange(32, dtype=np.uint32), axis=2)
+            rec = np.concatenate([rec, mw.astype("<u4")], axis=1)
         return rec.view(np.uint8).reshape(O, -1)
     Kc = _ceil(K, 64) * 64
     Km = _ceil(K, 128) * 128
@@ -391,9 +407,9 @@ def unpack(packed: np.ndarray, O: int, K: int, N: int, M: int):
     words = np.ascontiguousarray(np.asarray(packed, np.uint8).reshape(O, pitch))
     words = words.view("<u4").astype(np.uint32)
     if INDEX_FORM(N, M):
-        nch = pitch // 8
-        cw = words[:, 0::2]
-        idx = words[:, 1::2]
+        nch = _ceil(K, 128) * 4
+        cw = words[:, 0:2 * nch:2]
+        idx = words[:, 1:2 * nch:2]
         q = np.arange(8, dtype=np.uint32)
         i0 = (idx[:, :, None] >> (4 * q)) & 3
         i1 = (idx[:, :, None] >> (4 * q + 2)) & 3
@@ -410,6 +426,9 @@ def unpack(packed: np.ndarray, O: int, K: int, N: int, M: int):
         np.put_along_axis(w, i1[:, :, None].astype(np.int64), c1[:, :, None], 2)
         np.put_along_axis(mk, i0[:, :, None].astype(np.int64), 1, 2)
         np.put_along_axis(mk, i1[:, :, None].astype(np.int64), 1, 2)
+        if M == 8:                                          # the mask is stored, not implied
+            mw = words[:, 2 * nch:]
+            mk = ((mw[:, :, None] >> np.arange(32, dtype=np.uint32)) & 1).astype(np.uint8)
         return w.reshape(O, -1)[:, :K].copy(), mk.reshape(O, -1)[:, :K].copy()
     ncw = _ceil(K, 64) * 4
     cw = words[:, :ncw]

@@ -1080,7 +1080,8 @@ static hipError_t launch_sel(int cfg, const Args& a, hipStream_t s) {
 //  - dense N:M, K >= 2048 and at least two 256x128 tiles per CU: 256x128
 //    (wave tile 64x128, half the code-expansion work per MFMA);
 //  - dense N:M otherwise: 256x64;
-//  - 2:4: 256x96 (wave tile 64x96) below K = 4096, 512x64 (8 waves) above.
+//  - 2:4 and 2:8 (sparse MFMA): 256x96 (wave tile 64x96) below K = 4096; above,
+//    256x128 when there are at least two such tiles per CU, else 512x64 (8 waves).
 static int choose_cfg(int64_t T, int64_t O, int64_t K, bool sp) {
   // tuning override (read on every call so tests can force each configuration)
   const char* ev = std::getenv("SBL_GEMM_TILE");
@@ -1091,7 +1092,10 @@ static int choose_cfg(int64_t T, int64_t O, int64_t K, bool sp) {
   const int64_t t64 = cdiv(O, 256) * cdiv(T, 64);
   const int64_t t128 = cdiv(O, 256) * cdiv(T, 128);
   if (t64 < cus) return kR128x64k2;
-  if (sp) return K >= 4096 ? kR512x64w8 : kR256x96;
+  if (sp) {
+    if (K < 4096) return kR256x96;
+    return t128 >= 2 * cus ? kR256x128 : kR512x64w8;
+  }
   if (K >= 2048 && t128 >= 2 * cus) return kR256x128;
   return kR256x64;
 }

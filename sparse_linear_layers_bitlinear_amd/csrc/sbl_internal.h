@@ -9,14 +9,21 @@
 namespace sbl {
 
 // ---- packed-format geometry (see include/sbl.h) ---------------------------
-__host__ __device__ inline bool index_form(int N, int M) { return M == 4 && N == 2; }
+// 2:4 and 2:8 use the index form (the 2:4 sparse MFMA operand; every 2:8
+// pattern is also a 2:4 pattern); 2:8 records add the mask words.
+__host__ __device__ inline bool index_form(int N, int M) { return N == 2 && (M == 4 || M == 8); }
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // bytes of the code area of a dense-form row (ceil(K/64) * 16)
 __host__ __device__ inline int64_t dense_code_bytes(int64_t K) { return cdiv(K, 64) * 16; }
 // bytes of the mask area of a dense-form row (ceil(K/128) * 16)
 __host__ __device__ inline int64_t dense_mask_bytes(int64_t K) { return cdiv(K, 128) * 16; }
 __host__ __device__ inline int64_t row_pitch(int64_t K, int N, int M) {
-  return index_form(N, M) ? cdiv(K, 128) * 32 : dense_code_bytes(K) + dense_mask_bytes(K);
+  return index_form(N, M) ? cdiv(K, 128) * 32 + (M == 8 ? dense_mask_bytes(K) : 0)
+                          : dense_code_bytes(K) + dense_mask_bytes(K);
+}
+// byte offset of the mask words in a record (dense form, or 2:8 index form)
+__host__ __device__ inline int64_t mask_area_offset(int64_t K, int N, int M) {
+  return index_form(N, M) ? cdiv(K, 128) * 32 : dense_code_bytes(K);
 }
 // 32-wide chunks per packed row record (both forms cover ceil(K/128)*4 chunks)
 __host__ __device__ inline int64_t row_chunks(int64_t K) { return cdiv(K, 128) * 4; }

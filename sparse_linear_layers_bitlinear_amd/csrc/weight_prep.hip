@@ -472,6 +472,15 @@ __device__ __forceinline__ uint32_t drop_low_keep_bits8(const uint32_t* a) {
   return 0xFFu & ~(b1 | b2);
 }
 
+// The two slots an index-form group of 4 selects: its kept slots (bits 0..3
+// of kb), completed by the lowest free slots while fewer than two are set.
+__device__ __forceinline__ uint32_t select2(uint32_t kb) {
+  kb &= 0xFu;
+  if (__popc(kb) < 2) kb |= ~kb & (kb + 1u);
+  if (__popc(kb) < 2) kb |= ~kb & (kb + 1u);
+  return kb & 0xFu;
+}
+
 // Byte-slice 16 two-bit fields: bit u of lo (u = 4b + a) -> bit 8a + 2b, and
 // the same for hi one position up; i.e. a 4x4 transpose of 2-bit cells.
 __device__ __forceinline__ uint32_t byte_slice16(uint32_t lo, uint32_t hi) {
@@ -776,11 +785,13 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
   if (!packed) return;
   uint8_t* rec = packed + (int64_t)o * pitch;
   if constexpr (IDX) {
-    // 8 groups of 4: kept slots i0 < i1 (exactly two; padding groups keep 0,1)
+    // 8 groups of 4: selected slots i0 < i1 -- the kept ones (2:4: exactly
+    // two; padding groups keep 0,1), for 2:8 completed by the lowest free
+    // slots (code 0); the 2:8 mask itself goes to the mask words
     uint32_t iw = 0, lo = 0, hi = 0;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const uint32_t kb = (keep >> (4 * q)) & 0xFu;
+      const uint32_t kb = M == 8 ? select2(keep >> (4 * q)) : (keep >> (4 * q)) & 0xFu;
       const uint32_t i0 = __builtin_ctz(kb | 0x10u);
       const uint32_t i1 = 31u - __builtin_clz(kb | 1u);
       iw |= (i0 | (i1 << 2)) << (4 * q);
@@ -788,6 +799,7 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
       hi |= ((kneg >> (4 * q + i0)) & 1u) << (2 * q) | ((kneg >> (4 * q + i1)) & 1u) << (2 * q + 1);
     }
     *(uint2*)(rec + 8 * c) = make_uint2(byte_slice16(lo, hi), iw);
+    if constexpr (M == 8) *(uint32_t*)(rec + mask_off + 4 * c) = keep & valid;
   } else {
     const uint32_t w0 = byte_slice16(kn & 0xFFFFu, kneg & 0xFFFFu);
     const uint32_t w1 = byte_slice16(kn >> 16, kneg >> 16);
@@ -847,7 +859,7 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
     k.C = (int32_t)row_chunks(t.K);
     k.pitch = (int32_t)row_pitch(t.K, N, M);
     k.code_chunks = (int32_t)(dense_code_bytes(t.K) / 8);
-    k.mask_off = (int32_t)dense_code_bytes(t.K);
+    k.mask_off = (int32_t)mask_area_offset(t.K, N, M);
     // about one batch of loads per thread (the exact accumulation is VALU
     // work: spread it over many waves)
     // (variant 2: one chunk of 32 per thread and step)
@@ -896,11 +908,11 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
   else if (N == 6) SBL_QMP(BV, 8, false, 2); \
   else SBL_QMP(BV, 8, false, 0)
   if (bf16) {
-    if (index_form(N, M)) SBL_QMP(true, 4, true, 0);
+    if (index_form(N, M)) { if (M == 4) SBL_QMP(true, 4, true, 0); else SBL_QMP(true, 8, true, 0); }
     else if (M == 4) SBL_QMP(true, 4, false, 0);
     else SBL_QMP8(true);
   } else {
-    if (index_form(N, M)) SBL_QMP(false, 4, true, 0);
+    if (index_form(N, M)) { if (M == 4) SBL_QMP(false, 4, true, 0); else SBL_QMP(false, 8, true, 0); }
     else if (M == 4) SBL_QMP(false, 4, false, 0);
     else SBL_QMP8(false);
   }
@@ -918,7 +930,7 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
 // Standalone pack / unpack, one thread per 32-wide chunk of a row record.
 // ---------------------------------------------------------------------------
 template <bool IDX>
-__global__ __launch_bounds__(256) void k_pack(const int8_t* __restrict__ w_eff,
+__global__ __launch_bounds__(256) void k_pack(bool with_mask, const int8_t* __restrict__ w_eff,
                                               const uint8_t* __restrict__ mask, int64_t O,
                                               int64_t K, int64_t C, uint8_t* __restrict__ packed,
                                               int64_t pitch, int64_t code_chunks, int64_t mask_off) {
@@ -937,11 +949,12 @@ __global__ __launch_bounds__(256) void k_pack(const int8_t* __restrict__ w_eff,
   auto f = [&](uint32_t e) -> uint32_t { return (uint32_t)(fw >> (2 * e)) & 3u; };
   uint8_t* rec = packed + o * pitch;
   if constexpr (IDX) {
+    if (with_mask) *(uint32_t*)(rec + mask_off + 4 * c) = keep;   // 2:8: the mask itself
     if (k0 >= K) keep = 0x33333333u;            // padding groups keep slots (0, 1)
     else if (K - k0 < 32) keep |= 0x33333333u & ~((1u << (K - k0)) - 1u);
     uint32_t cw = 0, iw = 0;
     for (int q = 0; q < 8; ++q) {
-      const uint32_t kb = (keep >> (4 * q)) & 0xFu;
+      const uint32_t kb = select2(keep >> (4 * q));     // (2:4 groups already hold two)
       const uint32_t i0 = __builtin_ctz(kb | 0x10u);
       const uint32_t i1 = 31u - __builtin_clz(kb | 1u);
       iw |= (i0 | (i1 << 2)) << (4 * q);
@@ -961,7 +974,7 @@ __global__ __launch_bounds__(256) void k_pack(const int8_t* __restrict__ w_eff,
 }
 
 template <bool IDX>
-__global__ __launch_bounds__(256) void k_unpack(const uint8_t* __restrict__ packed, int64_t O,
+__global__ __launch_bounds__(256) void k_unpack(bool with_mask, const uint8_t* __restrict__ packed, int64_t O,
                                                 int64_t K, int64_t C, int64_t pitch,
                                                 int64_t mask_off, int8_t* __restrict__ w_eff,
                                                 uint8_t* __restrict__ mask) {
@@ -982,6 +995,7 @@ __global__ __launch_bounds__(256) void k_unpack(const uint8_t* __restrict__ pack
       wv[4 * q + i1] = (int8_t)(f1 == 3u ? -1 : (int)f1);
       keep |= ((1u << i0) | (1u << i1)) << (4 * q);
     }
+    if (with_mask) keep = *(const uint32_t*)(rec + mask_off + 4 * c);   // 2:8
   } else {
     const uint2 r = *(const uint2*)(rec + 8 * c);
     for (int u = 0; u < 16; ++u) {
@@ -1002,12 +1016,15 @@ hipError_t launch_pack(const int8_t* w_eff, const uint8_t* mask, int64_t O, int6
                        int M, void* packed, hipStream_t s) {
   const int64_t C = row_chunks(K);
   const dim3 grid((unsigned)cdiv(O * C, 256)), block(256);
+  const bool with_mask = index_form(N, M) && M == 8;
   if (index_form(N, M))
-    hipLaunchKernelGGL((k_pack<true>), grid, block, 0, s, w_eff, mask, O, K, C, (uint8_t*)packed,
-                       row_pitch(K, N, M), dense_code_bytes(K) / 8, dense_code_bytes(K));
+    hipLaunchKernelGGL((k_pack<true>), grid, block, 0, s, with_mask, w_eff, mask, O, K, C,
+                       (uint8_t*)packed, row_pitch(K, N, M), dense_code_bytes(K) / 8,
+                       mask_area_offset(K, N, M));
   else
-    hipLaunchKernelGGL((k_pack<false>), grid, block, 0, s, w_eff, mask, O, K, C, (uint8_t*)packed,
-                       row_pitch(K, N, M), dense_code_bytes(K) / 8, dense_code_bytes(K));
+    hipLaunchKernelGGL((k_pack<false>), grid, block, 0, s, false, w_eff, mask, O, K, C,
+                       (uint8_t*)packed, row_pitch(K, N, M), dense_code_bytes(K) / 8,
+                       mask_area_offset(K, N, M));
   return hipGetLastError();
 }
 
@@ -1015,12 +1032,13 @@ hipError_t launch_unpack(const void* packed, int64_t O, int64_t K, int N, int M,
                          uint8_t* mask, hipStream_t s) {
   const int64_t C = row_chunks(K);
   const dim3 grid((unsigned)cdiv(O * C, 256)), block(256);
+  const bool with_mask = index_form(N, M) && M == 8;
   if (index_form(N, M))
-    hipLaunchKernelGGL((k_unpack<true>), grid, block, 0, s, (const uint8_t*)packed, O, K, C,
-                       row_pitch(K, N, M), dense_code_bytes(K), w_eff, mask);
+    hipLaunchKernelGGL((k_unpack<true>), grid, block, 0, s, with_mask, (const uint8_t*)packed, O,
+                       K, C, row_pitch(K, N, M), mask_area_offset(K, N, M), w_eff, mask);
   else
-    hipLaunchKernelGGL((k_unpack<false>), grid, block, 0, s, (const uint8_t*)packed, O, K, C,
-                       row_pitch(K, N, M), dense_code_bytes(K), w_eff, mask);
+    hipLaunchKernelGGL((k_unpack<false>), grid, block, 0, s, false, (const uint8_t*)packed, O, K,
+                       C, row_pitch(K, N, M), mask_area_offset(K, N, M), w_eff, mask);
   return hipGetLastError();
 }
 

@@ -86,7 +86,7 @@ def _dx_case(S, T, O, K, N, M, out_bf16, seed, accumulate=False, nseg=1):
     assert_grad_close(host(dx), ref, abs_sum, O * nseg, out_bf16)
 
 
-@pytest.mark.parametrize("N,M", [(6, 8), (2, 4), (1, 4), (8, 8), (3, 8), (7, 8)])
+@pytest.mark.parametrize("N,M", [(6, 8), (2, 4), (1, 4), (8, 8), (3, 8), (7, 8), (2, 8)])
 @pytest.mark.parametrize("out_bf16", [False, True])
 def test_bwd_dx_parity(S, N, M, out_bf16):
     for T, O, K in [(50, 136, 264), (130, 392, 520), (1, 8, 8)]:

@@ -572,7 +572,8 @@ def _x_host(x, xdt):
 @pytest.mark.parametrize("T", [1, 3, 8, 16])
 @pytest.mark.parametrize("xdt", ["bf16", "fp32"])
 @pytest.mark.parametrize("N,M,O,K", [(2, 4, 200, 2560), (6, 8, 37, 1000), (2, 4, 64, 6912),
-                                     (6, 8, 130, 8192), (2, 4, 48, 264), (1, 4, 16, 128)])
+                                     (6, 8, 130, 8192), (2, 4, 48, 264), (1, 4, 16, 128),
+                                     (2, 8, 96, 1000)])
 def test_decode_fused_linear(S, T, xdt, N, M, O, K):
     """Decode-sized batches: sbl_linear_fwd quantizes the activations inside
     the GEMV. Against the oracle, and bit-identical to the separate

@@ -392,6 +392,8 @@ def test_pack_bits_per_weight():
     # 2:4 index form is 2 bits/weight; dense form 2 + 1 bits/weight
     assert o.packed_bytes(1, 1024, 2, 4) * 8 == 2 * 1024
     assert o.packed_bytes(1, 1024, 6, 8) * 8 == 3 * 1024
+    # 2:8 in the index form: 2 bits/weight of selected codes + indices, 1 of mask
+    assert o.packed_bytes(1, 1024, 2, 8) * 8 == 3 * 1024
 
 
 def test_pack_hand_encoded_rows(golden_dir):
