@@ -1079,7 +1079,8 @@ static hipError_t launch_sel(int cfg, const Args& a, hipStream_t s) {
 //    split between two wave groups (register-W kernel);
 //  - dense N:M, K >= 2048 and at least two 256x128 tiles per CU: 256x128
 //    (wave tile 64x128, half the code-expansion work per MFMA);
-//  - dense N:M otherwise: 256x64;
+//  - dense N:M otherwise: 256x96 (the 0.5B gate+up projection: 29.8 us
+//    against 33.7 with 256x64);
 //  - 2:4 and 2:8 (sparse MFMA): 256x96 (wave tile 64x96) below K = 4096; above,
 //    256x128 when there are at least two such tiles per CU, else 512x64 (8 waves).
 static int choose_cfg(int64_t T, int64_t O, int64_t K, bool sp) {
@@ -1097,7 +1098,7 @@ static int choose_cfg(int64_t T, int64_t O, int64_t K, bool sp) {
     return t128 >= 2 * cus ? kR256x128 : kR512x64w8;
   }
   if (K >= 2048 && t128 >= 2 * cus) return kR256x128;
-  return kR256x64;
+  return kR256x96;
 }
 
 hipError_t launch_gemm(const int8_t* xq, const float* sx, const void* packed, const float* sw,

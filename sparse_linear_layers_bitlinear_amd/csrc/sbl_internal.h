@@ -30,16 +30,15 @@ __host__ __device__ inline int64_t row_chunks(int64_t K) { return cdiv(K, 128) *
 
 // Max workgroups of the absmean partial pass (over a whole batch of
 // weights); fixes the workspace size.
-constexpr int kAbsmeanMaxBlocks = 1024;
+constexpr int kAbsmeanMaxBlocks = 256;
 // Most weight tensors one batched preparation handles.
 constexpr int kMaxPrepBatch = 8;
-// Workspace of the weight-prep path: partial exponent bins of every block,
-// then the 16 summed bins of each weight (two fit the single-weight size).
-constexpr size_t kPrepScalarBytes = 256;
+// Workspace of the weight-prep path: the 16 partial exponent bins of every
+// workgroup of the partial pass, then a 4-word compact record of each (any
+// batch size).
 inline size_t prep_workspace_bytes(int count = 1) {
-  const size_t bins = (size_t)count * 16 * sizeof(unsigned long long);
-  return (size_t)kAbsmeanMaxBlocks * 16 * sizeof(unsigned long long) +
-         (bins > kPrepScalarBytes ? (bins + 255) / 256 * 256 : kPrepScalarBytes);
+  (void)count;
+  return (size_t)kAbsmeanMaxBlocks * 20 * sizeof(unsigned long long);
 }
 
 // One weight tensor of a (batched) preparation, as the library's launcher

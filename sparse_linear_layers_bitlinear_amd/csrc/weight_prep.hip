@@ -9,9 +9,9 @@
 // Pipeline (all on the caller's stream, no host sync):
 //   k_absmean_partial  grid-stride over W; exact sum of |W| as integer
 //                      mantissa bins per 32-exponent window (order-free),
-//                      one vector of bins per block
-//   k_absmean_reduce   one workgroup sums the vectors into 16 bins
-//   k_qmp              a fifth wave per block turns the bins into an exact big
+//                      one vector of bins per block (at most 128 per tensor)
+//   k_qmp              an extra wave per block sums the tensor's partial
+//                      vectors into 16 bins and turns them into an exact big
 //                      integer -> RN fp64 -> / n -> fp32 gamma, sw = gamma +
 //                      eps, and the RoundClip threshold t (smallest |w| whose
 //                      code is +-1); meanwhile one thread per 32-wide chunk of
@@ -139,11 +139,14 @@ __device__ __forceinline__ void abs_accumulate_other(unsigned long long* bins, u
 // register slot; zeros add nothing; any other term only marks its lane. A
 // marked lane re-reads its vectors afterwards and adds exactly those other
 // terms to the LDS bins (the exact sum is order-free, so the split is exact).
-constexpr int kAbsThreads = 256;
+// Few, large blocks: every mask-pass workgroup sums its tensor's partial
+// vectors itself, so their number stays small.
+constexpr int kAbsThreads = 1024;
 constexpr int kAbsBatch = 8;
-constexpr int kAbsBlocks = 1024;  // partial vectors (at most)
-static_assert(kAbsBlocks <= kAbsmeanMaxBlocks && 16 * 8 <= kPrepScalarBytes,
-              "partials and summed bins must fit the weight-prep workspace");
+constexpr int kAbsBlocks = 256;        // partial vectors of a batch (at most)
+constexpr int kAbsPerTensor = 128;     // partial vectors of one tensor (at most)
+static_assert(kAbsBlocks <= kAbsmeanMaxBlocks,
+              "partials must fit the weight-prep workspace");
 
 // window-3 term of a sign-cleared |w| (0 outside window 3); `other` set if
 // the value is nonzero and outside window 3
@@ -154,6 +157,26 @@ __device__ __forceinline__ uint64_t abs_term3(uint32_t u, bool& other) {
   return (uint64_t)m << ((u >> 23) & 31u);
 }
 
+// A block's partial result (block p of the batch): its 16 bins, and a
+// compact record {bin 2w, bin 2w + 1, any other bin nonzero, 0} of window
+// w = 3, where practically every weight lies. The mask pass reads the
+// 32-byte records and falls back to the full vectors only when a flag is set.
+__device__ __forceinline__ void write_partial(unsigned long long* __restrict__ partials_all, int64_t p,
+                                              const unsigned long long* bins) {
+  if (threadIdx.x < 16) partials_all[p * 16 + threadIdx.x] = bins[threadIdx.x];
+  if (threadIdx.x == 0) {
+    unsigned long long other = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j != 2 * (int)kAbsWindow && j != 2 * (int)kAbsWindow + 1) other |= bins[j];
+    unsigned long long* const c = partials_all + (int64_t)kAbsmeanMaxBlocks * 16 + p * 4;
+    c[0] = bins[2 * kAbsWindow];
+    c[1] = bins[2 * kAbsWindow + 1];
+    c[2] = other != 0 ? 1ull : 0ull;
+    c[3] = 0;
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(kAbsThreads) void k_absmean_partial(const PrepBatchK batch,
                                                                  unsigned long long* __restrict__ partials_all) {
@@ -162,7 +185,6 @@ __global__ __launch_bounds__(kAbsThreads) void k_absmean_partial(const PrepBatch
   const void* __restrict__ wv = pi.w;
   const int64_t n = pi.O * pi.K;
   const uint32_t lb = blockIdx.x - pi.blk1, nblk = pi.nparts;      // block within the tensor
-  unsigned long long* __restrict__ partials = partials_all + (int64_t)pi.part0 * 16;
   __shared__ unsigned long long bins[16];
   if (threadIdx.x < 16) bins[threadIdx.x] = 0;
   __syncthreads();
@@ -251,7 +273,7 @@ __global__ __launch_bounds__(kAbsThreads) void k_absmean_partial(const PrepBatch
     atomicAdd(&bins[2 * st.tag + 1], (unsigned long long)st.a1 | ((unsigned long long)st.a2 << 32));
   }
   __syncthreads();
-  if (threadIdx.x < 16) partials[(int64_t)lb * 16 + threadIdx.x] = bins[threadIdx.x];
+  write_partial(partials_all, (int64_t)pi.part0 + lb, bins);
 }
 
 // Per-tensor scalars of the weight quantization.
@@ -333,62 +355,6 @@ __device__ PrepScalars scalars_from_bins(const unsigned long long* bins, int64_t
   r.t_bits = __float_as_uint(roundclip_threshold(r.sw));
   r.pad = 0;
   return r;
-}
-
-// Sum of the per-block partial vectors into the 16 bins (one workgroup; the
-// serial part that turns the bins into gamma and the threshold runs in the
-// mask/pack kernel, overlapped with its W staging). The partials were written
-// by workgroups all over the chip and come from beyond this XCD's L2, so every
-// thread issues the loads of all its (at most 4) partial vectors at once.
-constexpr int kReduceThreads = 256;
-constexpr int kReducePer = kAbsmeanMaxBlocks / kReduceThreads;
-static_assert(kAbsmeanMaxBlocks % kReduceThreads == 0, "partials per reduce thread");
-__global__ __launch_bounds__(kReduceThreads) void k_absmean_reduce(const PrepBatchK batch,
-                                                        const unsigned long long* __restrict__ partials_all,
-                                                        unsigned long long* __restrict__ bins_all) {
-  const PrepItemK pi = prep_item(batch, blockIdx.x);     // one block per tensor
-  const unsigned long long* __restrict__ partials = partials_all + (int64_t)pi.part0 * 16;
-  const int nparts = pi.nparts;
-  unsigned long long* __restrict__ bins_out = bins_all + (int64_t)blockIdx.x * 16;
-  if (threadIdx.x == 0 && pi.flips) *pi.flips = 0;     // accumulated by the mask pass
-  uint4 v[kReducePer][8];
-#pragma unroll
-  for (int u = 0; u < kReducePer; ++u) {
-    const int b = min((int)threadIdx.x + kReduceThreads * u, nparts - 1);   // in bounds
-    const uint4* p = (const uint4*)(partials + (int64_t)b * 16);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) v[u][q] = p[q];
-  }
-  unsigned long long acc[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0;
-#pragma unroll
-  for (int u = 0; u < kReducePer; ++u) {
-    const unsigned long long keep = (int)threadIdx.x + kReduceThreads * u < nparts ? ~0ull : 0ull;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      acc[2 * q] += ((unsigned long long)v[u][q].x | ((unsigned long long)v[u][q].y << 32)) & keep;
-      acc[2 * q + 1] += ((unsigned long long)v[u][q].z | ((unsigned long long)v[u][q].w << 32)) & keep;
-    }
-  }
-  // 256 x 16 -> 16 x 16 -> 16 through LDS (independent accesses)
-  __shared__ unsigned long long part[16 * 257];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) part[j * 257 + threadIdx.x] = acc[j];
-  __syncthreads();
-  const int col = threadIdx.x & 15, grp = threadIdx.x >> 4;
-  unsigned long long sum = 0;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) sum += part[col * 257 + grp * 16 + r];
-  __syncthreads();
-  part[col * 257 + grp] = sum;
-  __syncthreads();
-  if (threadIdx.x < 16) {
-    unsigned long long t = 0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) t += part[threadIdx.x * 257 + r];
-    bins_out[threadIdx.x] = t;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -519,7 +485,6 @@ __global__ __launch_bounds__(kAbsThreads) void k_absmean_partial_kept(
   const PrepItemK pi = prep_item(batch, item);
   const void* __restrict__ wv = pi.w;
   const uint32_t lb = blockIdx.x - pi.blk1, nblk = pi.nparts;
-  unsigned long long* __restrict__ partials = partials_all + (int64_t)pi.part0 * 16;
   __shared__ unsigned long long bins[16];
   if (threadIdx.x < 16) bins[threadIdx.x] = 0;
   __syncthreads();
@@ -589,21 +554,26 @@ __global__ __launch_bounds__(kAbsThreads) void k_absmean_partial_kept(
     atomicAdd(&bins[2 * kAbsWindow + 1], shi);
   }
   __syncthreads();
-  if (threadIdx.x < 16) partials[(int64_t)lb * 16 + threadIdx.x] = bins[threadIdx.x];
+  write_partial(partials_all, (int64_t)pi.part0 + lb, bins);
 }
 
-// Workgroup: one thread per chunk and one more wave that turns the summed
-// absmean bins into gamma, sw and the threshold (a serial computation) while
-// the others stage W and rank the groups; the threshold is needed only for
-// the codes.
+// Workgroup: one thread per chunk and one more wave that sums the tensor's
+// partial records into the absmean bins and turns them into gamma, sw and the
+// threshold (a serial computation) while the others stage W and rank the
+// groups; the threshold is needed only for the codes.
 constexpr int kQmpThreads = kChunksPerBlock + 64;
+// Loads in flight when the extra wave sums full partial vectors (few
+// registers: the wave shares the kernel's allocation).
+constexpr int kSumUnroll = 8;
+static_assert(kAbsPerTensor % 64 == 0, "compact records: whole loads per lane");
 
 // SEL: how the mask is found -- 0: rank rule (any N); for M = 8 also
 // 1: drop the lowest slot (N = 7), 2: drop the two lowest (N = 6), 3: keep
 // all (N = 8).
+
 template <bool BF16, int M, bool IDX, int SEL>
 __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int N,
-                                                     const unsigned long long* __restrict__ bins_all,
+                                                     const unsigned long long* __restrict__ partials_all,
                                                      float eps) {
   const int item = prep_index(batch, blockIdx.x, true);
   const PrepItemK pi = prep_item(batch, item);
@@ -615,18 +585,74 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
   uint8_t* __restrict__ packed = pi.packed;
   float* __restrict__ gamma_sw = pi.gamma_sw;
   float* __restrict__ sw_rows = pi.sw_rows;
-  const unsigned long long* __restrict__ bins = bins_all + (int64_t)item * 16;
   const uint32_t lb = blockIdx.x - pi.blk3;                // block within the tensor
   __shared__ __attribute__((aligned(16))) uint32_t lds[kChunksPerBlock * kLdsStride];
   __shared__ unsigned long long red[16];
   __shared__ PrepScalars scal;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (wave == kChunksPerBlock / 64) {
-    // ---- scalar wave: the 16 summed bins -> gamma, sw, threshold ----
+    // ---- scalar wave: partials -> 16 bins -> gamma, sw, threshold ----
     const int lane = threadIdx.x & 63;
-    if (lane < 16) red[lane] = bins[lane];
-    __builtin_amdgcn_wave_barrier();
-    __syncthreads();                                    // (1) W staged by the other waves
+    const int np = pi.nparts;
+    const unsigned long long* __restrict__ cp =
+        partials_all + (int64_t)kAbsmeanMaxBlocks * 16 + (int64_t)pi.part0 * 4;
+    unsigned long long s0 = 0, s1 = 0, fl = 0;
+    {
+      uint4 a[kAbsPerTensor / 64], f[kAbsPerTensor / 64];   // all loads in flight
+#pragma unroll
+      for (int u = 0; u < kAbsPerTensor / 64; ++u) {
+        const int64_t r = min(lane + 64 * u, np - 1);
+        a[u] = *(const uint4*)(cp + r * 4);
+        f[u] = *(const uint4*)(cp + r * 4 + 2);
+      }
+      // (1) W staged by the other waves. A plain barrier: this wave wrote
+      // nothing they read, and its loads stay in flight across it, so the
+      // sums below overlap the other waves' ranking.
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int u = 0; u < kAbsPerTensor / 64; ++u) {
+        const unsigned long long m = lane + 64 * u < np ? ~0ull : 0ull;
+        s0 += (((unsigned long long)a[u].y << 32) | a[u].x) & m;
+        s1 += (((unsigned long long)a[u].w << 32) | a[u].z) & m;
+        fl |= (unsigned long long)(f[u].x | f[u].y) & m;
+      }
+    }
+    if (__ballot(fl != 0) == 0) {
+      // every block's terms lie in window 3 (or are zero)
+      s0 = wave_sum_u64(s0);
+      s1 = wave_sum_u64(s1);
+      if (lane < 16) red[lane] = lane == 2 * (int)kAbsWindow ? s0 : lane == 2 * (int)kAbsWindow + 1 ? s1 : 0ull;
+    } else {
+      // some block has terms elsewhere: sum the full vectors, 8 lanes per
+      // vector (16 bytes, two bins, each), 8 vectors per load instruction
+      const uint4* __restrict__ pv = (const uint4*)(partials_all + (int64_t)pi.part0 * 16);
+      const int e = lane & 7, v0 = lane >> 3;
+      s0 = s1 = 0;                                        // bins 2e, 2e + 1
+      for (int b = 0; b < np; b += 8 * kSumUnroll) {
+        uint4 d[kSumUnroll];
+#pragma unroll
+        for (int u = 0; u < kSumUnroll; ++u) d[u] = pv[min(b + v0 + 8 * u, np - 1) * 8 + e];
+#pragma unroll
+        for (int u = 0; u < kSumUnroll; ++u) {
+          const unsigned long long m = b + v0 + 8 * u < np ? ~0ull : 0ull;
+          s0 += (((unsigned long long)d[u].y << 32) | d[u].x) & m;
+          s1 += (((unsigned long long)d[u].w << 32) | d[u].z) & m;
+        }
+      }
+#pragma unroll
+      for (int off = 8; off < 64; off <<= 1) {            // sum over the 8 vector slots
+        s0 += ((unsigned long long)(uint32_t)__shfl_xor((int)(uint32_t)(s0 >> 32), off, 64) << 32) |
+              (uint32_t)__shfl_xor((int)(uint32_t)s0, off, 64);
+        s1 += ((unsigned long long)(uint32_t)__shfl_xor((int)(uint32_t)(s1 >> 32), off, 64) << 32) |
+              (uint32_t)__shfl_xor((int)(uint32_t)s1, off, 64);
+      }
+      if (lane < 8) {
+        red[2 * lane] = s0;
+        red[2 * lane + 1] = s1;
+      }
+    }
+    if (lb == 0 && lane == 0 && pi.flips) *pi.flips = 0;   // accumulated by the flips pass
+    __builtin_amdgcn_wave_barrier();                    // red written (one wave: in order)
     if (lane == 0) {
       const int64_t n = pi.variant == 2 ? O * (K / M) * N : O * K;   // kept weights only
       const PrepScalars sc = scalars_from_bins(red, n, eps);
@@ -728,7 +754,7 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
       keep |= kb << (g * M);
     }
   }
-  __syncthreads();                                    // (2) scalars from the fifth wave
+  __syncthreads();                                    // (2) scalars from the extra wave
   if (!active) return;
   const PrepScalars sc = scal;
   const uint32_t tb = sc.t_bits;
@@ -811,7 +837,7 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
 // Mask flips against the previous step's keep bits (both in the word layout
 // of mask_bits), for the tensors that ask for them: a grid-stride popcount
 // of (cur ^ prev), summed in LDS, one atomic per workgroup (the counter was
-// zeroed by the reduce kernel). Same-address atomics from every workgroup of
+// zeroed by the mask pass). Same-address atomics from every workgroup of
 // the mask pass would serialize; kFlipBlocks per tensor keeps them few.
 constexpr int kFlipBlocks = 64;
 __global__ __launch_bounds__(256) void k_mask_flips(const PrepBatchK batch) {
@@ -837,7 +863,7 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
   PrepBatchK b{};
   b.count = count;
   const int V = bf16 ? 8 : 4;
-  const int cap = kAbsBlocks / count;          // partial vectors per tensor, at most
+  const int cap = std::min(kAbsPerTensor, kAbsBlocks / count);   // partial vectors per tensor
   int parts = 0, blk3 = 0;
   for (int i = 0; i < count; ++i) {
     const PrepTensor& t = items[i];
@@ -874,7 +900,6 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
     blk3 += (int)cdiv(t.O * (int64_t)k.C, kChunksPerBlock);
   }
   auto* partials = (unsigned long long*)ws;
-  auto* bins = partials + (size_t)kAbsmeanMaxBlocks * 16;
   if (items[0].variant == 2) {   // a batch is all of variant 2 or none (checked by the caller)
     bool vec = true;               // (w itself is 16-byte aligned)
     for (int i = 0; i < count; ++i) vec = vec && (items[i].K * (bf16 ? 2 : 4)) % 16 == 0;
@@ -896,12 +921,9 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_absmean_reduce, dim3(count), dim3(kReduceThreads), 0, s, b, partials, bins);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)blk3), block(kQmpThreads);
 #define SBL_QMP(BV, MV, IV, SV) \
-  hipLaunchKernelGGL((k_qmp<BV, MV, IV, SV>), grid, block, 0, s, b, N, bins, eps)
+  hipLaunchKernelGGL((k_qmp<BV, MV, IV, SV>), grid, block, 0, s, b, N, partials, eps)
 #define SBL_QMP8(BV)                        \
   if (N == 8) SBL_QMP(BV, 8, false, 3);     \
   else if (N == 7) SBL_QMP(BV, 8, false, 1); \

@@ -369,6 +369,39 @@ def test_absmean_extreme_ranges(S):
             assert np.array_equal(host(r["w_eff"]), w_eff), name
 
 
+@pytest.mark.parametrize("dt", [np.float32, "bf16"])
+def test_absmean_outliers_in_some_blocks(S, dt):
+    """Tensors large enough for many partial-pass workgroups, with a few
+    magnitudes outside [2^-31, 2) (and zeros) in some of them only: gamma
+    stays exact whether every workgroup's terms lie in that window or not,
+    alone and in a batch that mixes both kinds of tensor."""
+    log_case("absmean outliers in some blocks", dt)
+    rng = np.random.default_rng(6)
+    clean = (rng.standard_normal((1536, 1024)) * 0.02).astype(F32)
+    dirty = clean.copy()
+    flat = dirty.reshape(-1)
+    pos = rng.choice(flat.size, 7, replace=False)
+    flat[pos] = np.array([3.0, -1e5, 2.0, 1e-20, -3e-30, 0.0, 7e3], F32)
+    if dt == "bf16":
+        clean, dirty = bf16_round(clean), bf16_round(dirty)
+    dev = lambda a: to_dev(a) if dt == np.float32 else to_dev(a).to(torch.bfloat16)
+    wide = (rng.standard_normal((512, 1024)) * 0.02).astype(F32)
+    wide[::37, ::53] *= F32(1e6)
+    if dt == "bf16":
+        wide = bf16_round(wide)
+    for W in (clean, dirty, wide):
+        g_ref, sw_ref = o.absmean(W)
+        r = S.sbl_quant_mask_weight(dev(W), 6, 8)
+        gs = host(r["gamma_sw"])
+        assert f32_bits(gs[0]) == f32_bits(g_ref) and f32_bits(gs[1]) == f32_bits(sw_ref)
+    for order in ((clean, dirty, wide), (dirty, clean), (clean, clean, wide, clean)):
+        outs = S.sbl_quant_mask_weight_batch([{"w": dev(W)} for W in order], 6, 8)
+        for W, r in zip(order, outs):
+            g_ref, sw_ref = o.absmean(W)
+            gs = host(r["gamma_sw"])
+            assert f32_bits(gs[0]) == f32_bits(g_ref) and f32_bits(gs[1]) == f32_bits(sw_ref)
+
+
 @pytest.mark.parametrize("M", [8, 4])
 def test_mask_every_tie_pattern(S, M):
     """Every group of M magnitudes drawn from {0, 1, 2} (M = 8: 6561 groups)
