@@ -7,6 +7,7 @@
 namespace sbl {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 // bf16 bit pattern -> fp32 (exact)

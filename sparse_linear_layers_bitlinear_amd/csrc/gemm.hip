@@ -556,7 +556,8 @@ void k_gemm_dma(const int8_t* __restrict__ xq, const float* __restrict__ sx,
 // loads of a tile's first K-steps are issued before the previous tile's
 // epilogue, so their latency hides behind it. The bf16 epilogue stages the
 // dequantized tile in LDS and writes each output row segment with contiguous
-// 8-byte lanes (BM * 2 bytes per row and instruction).
+// 16-byte lanes; the stores are non-temporal (y is not read again here, so it
+// should not push the re-read W and xq panels out of the caches).
 // ---------------------------------------------------------------------------
 constexpr int kPitchR = 144;   // LDS bytes per staged xq row (128 k + 16 pad)
 
@@ -565,7 +566,7 @@ struct RaCfg {
   static constexpr int NTQ = 64 * WO, NT = NTQ * KS, NW = WO * KS;
   static constexpr int BM = WO * 16 * FI, BN = 16 * FJ;
   static constexpr int BUF = BN * kPitchR;
-  static constexpr int PO = BM * 2 + 8;          // LDS bytes per staged output row
+  static constexpr int PO = BM * 2 + 16;         // LDS bytes per staged output row
   static constexpr size_t LDS_B = (size_t)KS * 2 * BUF;
   static constexpr size_t LDS_RED = KS > 1 ? (size_t)WO * FI * FJ * 64 * 16 : 0;
   static constexpr size_t LDS_OUT = (size_t)BN * PO;
@@ -868,30 +869,32 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
       constexpr int RC = RW < 8 ? RW : 8;             // rows in flight per wave
       constexpr int CPR = BM / 4;                     // 8-byte chunks per row
       constexpr int CL = (CPR + 63) / 64;             // chunks per lane and row
-      constexpr int LPR = CPR < 64 ? CPR : 64;        // lanes per row (full-tile path)
+      constexpr int CP16 = BM / 8;                    // 16-byte chunks per row (full-tile path)
+      constexpr int LPR = CP16 < 64 ? CP16 : 64;      // lanes per row
       constexpr int RPI = 64 / LPR;                   // rows per wave instruction
       constexpr int RWF = BN / (NW * RPI);            // row groups per wave
       constexpr int RF = largest_divisor_upto8(RWF);          // row groups in flight
-      constexpr bool FULL_OK = CPR % LPR == 0 && BN % (NW * RPI) == 0 && RWF % RF == 0 && RWF > 0;
-      if (FULL_OK && (Oi & 3) == 0 && eo0 + BM <= Oi && et0 + BN <= Ti) {
-        // whole tile inside y: straight-line reads and 8-byte stores
-        constexpr int CF = CPR / LPR;
+      constexpr bool FULL_OK = CP16 % LPR == 0 && BN % (NW * RPI) == 0 && RWF % RF == 0 && RWF > 0;
+      if (FULL_OK && (Oi & 7) == 0 && eo0 + BM <= Oi && et0 + BN <= Ti) {
+        // whole tile inside y: straight-line reads and 16-byte stores
+        constexpr int CF = CP16 / LPR;
         const int lr = lane / LPR, lc = lane % LPR;
 #pragma unroll
         for (int m0 = 0; m0 < RWF; m0 += RF) {
-          uint2 v[RF][CF];
+          v4u v[RF][CF];
 #pragma unroll
           for (int m = 0; m < RF; ++m)
 #pragma unroll
             for (int c = 0; c < CF; ++c)
-              v[m][c] = *(const uint2*)(ot + ((wave + NW * (m0 + m)) * RPI + lr) * C::PO +
-                                        8 * (lc + LPR * c));
+              v[m][c] = *(const v4u*)(ot + ((wave + NW * (m0 + m)) * RPI + lr) * C::PO +
+                                      16 * (lc + LPR * c));
 #pragma unroll
           for (int m = 0; m < RF; ++m) {
             uint16_t* yr = (uint16_t*)y +
                            (int64_t)(et0 + (wave + NW * (m0 + m)) * RPI + lr) * Oi + eo0;
 #pragma unroll
-            for (int c = 0; c < CF; ++c) *(uint2*)(yr + 4 * (lc + LPR * c)) = v[m][c];
+            for (int c = 0; c < CF; ++c)
+              __builtin_nontemporal_store(v[m][c], (v4u*)(yr + 8 * (lc + LPR * c)));
           }
         }
       } else {
