@@ -171,4 +171,37 @@ __device__ __forceinline__ void store_tile(void* __restrict__ y, int32_t* __rest
   }
 }
 
+// store_tile with the four weight scales of rows o..o+3 already in registers
+// (sw[r] for row min(o + r, O - 1)).
+template <bool YBF16>
+__device__ __forceinline__ void store_tile_sw(void* __restrict__ y, int32_t* __restrict__ acc_out,
+                                           const v4i& c, int t, int o, int O, float s_t,
+                                           const float (&sw)[4]) {
+  float v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float a = (float)c[r] * s_t;
+    v[r] = a * sw[r];
+  }
+  const int64_t base = (int64_t)t * O + o;
+  if (o + 3 < O && (O & 3) == 0) {
+    if constexpr (YBF16) {
+      const uint32_t lo = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+      const uint32_t hi = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+      *(uint2*)((uint16_t*)y + base) = make_uint2(lo, hi);
+    } else {
+      *(float4*)((float*)y + base) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    if (acc_out) *(int4*)(acc_out + base) = make_int4(c[0], c[1], c[2], c[3]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (o + r >= O) break;
+      if constexpr (YBF16) ((uint16_t*)y)[base + r] = (uint16_t)f32_to_bf16_bits(v[r]);
+      else ((float*)y)[base + r] = v[r];
+      if (acc_out) acc_out[base + r] = c[r];
+    }
+  }
+}
+
 }  // namespace sbl

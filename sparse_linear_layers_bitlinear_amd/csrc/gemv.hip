@@ -18,9 +18,10 @@
 //    16 rows x two K-steps), issued at the start so the whole weight stream is
 //    in flight at once;
 //  - the T activation rows are quantized by all 512 threads together (a token
-//    is shared by 512 / T' threads, T' = T rounded up to a power of two), into
-//    int8 rows in LDS -- the same arithmetic as the stand-alone quantizer, so
-//    the codes are identical -- or, when xq is given, copied by LDS-DMA;
+//    is shared by 512 / T' threads, T' = T rounded up to a power of two; with
+//    one wavefront per token its maximum needs no barrier), into int8 rows in
+//    LDS -- the same arithmetic as the stand-alone quantizer, so the codes are
+//    identical -- or, when xq is given, copied by LDS-DMA;
 //  - the waves then split the K-steps of each tile (MFMA A operand = 8 bytes of
 //    packed W per lane and K-step, the operand layout of the prefill kernel;
 //    B = the int8 rows, columns t >= T read row T-1 and are never stored),
@@ -48,6 +49,8 @@ struct DecodeArgs {
   const float* sw;        // weight scale(s), element o at o * sw_inc
   int sw_inc;
   int T, O, K, R;         // R: most tiles of one workgroup
+  int tq, trem;           // tiles per workgroup: tq, one more for the first trem
+  int lg;                 // log2 of the threads per token (dec_group)
   void* y;                // [T, O] bf16 or fp32
   int32_t* acc;           // optional [T, O] int32
 };
@@ -107,20 +110,29 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
-  // this workgroup's tiles [tb, tb + ntb) of the (O + 15) / 16 (even split)
-  const int ntiles = (O + 15) >> 4;
-  const int tb = (int)((int64_t)blockIdx.x * ntiles / gridDim.x);
-  const int ntb = (int)((int64_t)(blockIdx.x + 1) * ntiles / gridDim.x) - tb;
+  // this workgroup's tiles [tb, tb + ntb) of the (O + 15) / 16 (even split,
+  // quotient and remainder from the host: no division here)
+  const int bx = blockIdx.x;
+  const int tb = bx * a.tq + min(bx, a.trem);
+  const int ntb = a.tq + (bx < a.trem ? 1 : 0);
+  // the weight scales of this thread's first output item (loaded now, so the
+  // epilogue does not wait for them)
+  float swp[4];
+  {
+    const int o = (tb + (tid >> 6)) * 16 + 4 * ((tid >> 4) & 3);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) swp[r] = a.sw[(int64_t)min(o + r, O - 1) * a.sw_inc];
+  }
 
   // activations of the thread's token (XM 1 / 2), loaded first: waiting for
   // them then does not wait for the W copies issued after them
   constexpr bool BF = XM == 1;
   constexpr int EV = XM == 0 ? 16 : BF ? 8 : 4;         // elements per 16-byte vector
   const int nvr = K / EV;                                // vectors per row
-  const int G = dec_group(T);                            // threads per token
-  const int tt = min(tid / G, T - 1), col = tid % G;     // token and first vector
-  const bool tok = tid / G < T;                          // thread has a token
-  const int nvt = (nvr + G - 1) / G;                     // vectors per thread (uniform)
+  const int lg = a.lg, G = 1 << lg;                      // threads per token
+  const int tt = min(tid >> lg, T - 1), col = tid & (G - 1);   // token and first vector
+  const bool tok = (tid >> lg) < T;                      // thread has a token
+  const int nvt = (nvr + G - 1) >> lg;                   // vectors per thread (uniform)
   uint4 v[kDecMaxVec];
   if constexpr (XM != 0) {
     const uint4* const row = (const uint4*)a.x + (int64_t)tt * nvr;
@@ -132,12 +144,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   // packed W -> LDS: job j = (tile j / np, pair j % np), one DMA per wave and
   // job. Lane l moves 16 bytes of row l % 16 at byte 64 p + 16 (l / 16); the
   // second step of a last odd pair re-reads the first (it is never computed).
-  for (int j = wave; j < ntb * np; j += kDecWaves) {
-    const int r = j / np, p = j - r * np;
+  for (int j = wave, r = wave / np, p = wave - (wave / np) * np; j < ntb * np; j += kDecWaves) {
     const int ch = lane >> 4;
     const int chs = (2 * p + (ch >> 1) < ns) ? ch : ch - 2;
     const int o = min((tb + r) * 16 + r16, O - 1);
     dma16(a.packed + (int64_t)o * a.pitch + 64 * p + 16 * chs, wsm + j * 1024);
+    for (p += kDecWaves; p >= np; p -= np) ++r;          // (r, p) of job j + kDecWaves
   }
   for (int i = tid; i < ntb * 256; i += kDecThreads) red[i] = 0;
 
@@ -163,17 +175,31 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x142, 0xA, 0xF, false));
     if (G >= 64) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x143, 0xC, 0xF, false));
     const uint32_t m_lo = __builtin_amdgcn_readlane(m, 31), m_hi = __builtin_amdgcn_readlane(m, 63);
-    if (lane == 0) {
-      pmax[2 * wave] = G >= 64 ? m_hi : m_lo;
-      pmax[2 * wave + 1] = m_hi;
-    }
-    __syncthreads();
-    uint32_t mt = 0;
-    if (G >= 64) {
-      const int wpt = G >> 6;                            // waves per token
-      for (int k = 0; k < wpt; ++k) mt = max(mt, pmax[2 * (tt * wpt + k)]);
-    } else {
-      mt = pmax[tt];
+    uint32_t mt = m_hi;                                  // G == 64: one wave per token
+    if (G != 64) {                                       // (uniform over the workgroup)
+      if (lane == 0) {
+        pmax[2 * wave] = G >= 64 ? m_hi : m_lo;
+        pmax[2 * wave + 1] = m_hi;
+      }
+      __syncthreads();
+      // all 16 partial maxima at once (constant indices: no dependent reads)
+      uint32_t pm[16];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 q4 = *(const uint4*)(pmax + 4 * k);
+        pm[4 * k] = q4.x; pm[4 * k + 1] = q4.y; pm[4 * k + 2] = q4.z; pm[4 * k + 3] = q4.w;
+      }
+      mt = 0;
+      if (G > 64) {
+        const int w0 = tt << (lg - 6), w1 = (tt + 1) << (lg - 6);   // the token's waves
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w)
+          if (w >= w0 && w < w1) mt = max(mt, pm[2 * w]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (k == tt) mt = pm[k];
+      }
     }
     const ActScale sc = act_scale(mt, a.eps);
     if (col == 0 && tok) sxs[tt] = sc.s;
@@ -237,8 +263,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   // lane l of tile r: outputs o = 16 (tb + r) + 4 (l / 16) + 0..3 of token l % 16
   for (int i = tid; i < ntb * 64; i += kDecThreads) {
     const int t = i & 15, o = (tb + (i >> 6)) * 16 + 4 * ((i >> 4) & 3);
+    if (i != tid) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) swp[r] = a.sw[(int64_t)min(o + r, O - 1) * a.sw_inc];
+    }
     if (t < T && o < O)
-      store_tile<YBF16>(a.y, a.acc, *(const v4i*)(red + 4 * i), t, o, O, sxs[t], a.sw, a.sw_inc);
+      store_tile_sw<YBF16>(a.y, a.acc, *(const v4i*)(red + 4 * i), t, o, O, sxs[t], swp);
   }
 }
 
@@ -293,8 +323,12 @@ hipError_t launch_decode(const void* x, int xmode, const float* sx, float eps, c
   if (!decode_fits(T, O, K, N, M, xmode)) return hipErrorInvalidValue;
   const int blocks = dec_blocks(O);
   const int R = (int)cdiv(cdiv(O, 16), blocks);
+  const int ntiles = (int)cdiv(O, 16);
+  int lg = 0;                                  // log2 of the threads per token
+  while ((1 << lg) < dec_group((int)T)) ++lg;
   const DecodeArgs a{x, sx, eps, (const uint8_t*)packed, (int)row_pitch(K, N, M), sw,
-                     (int)sw_inc, (int)T, (int)O, (int)K, R, y, acc};
+                     (int)sw_inc, (int)T, (int)O, (int)K, R, ntiles / blocks, ntiles % blocks, lg,
+                     y, acc};
   if (index_form(N, M))
     return y_bf16 ? dispatch_x<true, true>(xmode, a, blocks, s)
                   : dispatch_x<true, false>(xmode, a, blocks, s);
