@@ -17,11 +17,14 @@
 //    straight into LDS with 16-byte LDS-DMA loads (one instruction moves 1 KB:
 //    16 rows x two K-steps), issued at the start so the whole weight stream is
 //    in flight at once;
-//  - the T activation rows are quantized by all 512 threads together (a token
-//    is shared by 512 / T' threads, T' = T rounded up to a power of two; with
+//  - the T activation rows are quantized by the first XW wavefronts (a token
+//    is shared by 64 XW / T' threads, T' = T rounded up to a power of two; with
 //    one wavefront per token its maximum needs no barrier), into int8 rows in
 //    LDS -- the same arithmetic as the stand-alone quantizer, so the codes are
-//    identical -- or, when xq is given, copied by LDS-DMA;
+//    identical -- or, when xq is given, copied by LDS-DMA. For T <= 4, XW = 4
+//    and the other four wavefronts issue the weight copies: a wave's loads
+//    complete in order, so the quantizing waves then wait for x alone and
+//    quantize while the weights are in flight;
 //  - the waves then split the K-steps of each tile (MFMA A operand = 8 bytes of
 //    packed W per lane and K-step, the operand layout of the prefill kernel;
 //    B = the int8 rows, columns t >= T read row T-1 and are never stored),
@@ -51,6 +54,7 @@ struct DecodeArgs {
   int T, O, K, R;         // R: most tiles of one workgroup
   int tq, trem;           // tiles per workgroup: tq, one more for the first trem
   int lg;                 // log2 of the threads per token (dec_group)
+  int xw;                 // wavefronts that quantize x (4 or 8; the rest copy W)
   void* y;                // [T, O] bf16 or fp32
   int32_t* acc;           // optional [T, O] int32
 };
@@ -66,11 +70,11 @@ __host__ __device__ inline int dec_off_sx(int T, int K, int R) {
 __host__ __device__ inline int dec_lds(int T, int K, int R) {
   return dec_off_sx(T, K, R) + 64 + 64 + R * 1024;
 }
-// threads per token: 512 / (T rounded up to a power of two)
-__host__ __device__ inline int dec_group(int T) {
+// threads per token: (quantizing threads) / (T rounded up to a power of two)
+__host__ __device__ inline int dec_group(int T, int threads = kDecThreads) {
   int tp = 1;
   while (tp < T) tp <<= 1;
-  return kDecThreads / tp;
+  return threads / tp;
 }
 
 // max over each row of 16 lanes, left in the row's lane 15 (row_shr 1, 2, 4, 8;
@@ -129,27 +133,35 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   constexpr bool BF = XM == 1;
   constexpr int EV = XM == 0 ? 16 : BF ? 8 : 4;         // elements per 16-byte vector
   const int nvr = K / EV;                                // vectors per row
+  const int XW = XM == 0 ? kDecWaves : a.xw;             // quantizing wavefronts
+  const bool xwave = wave < XW;                          // (wave-uniform)
   const int lg = a.lg, G = 1 << lg;                      // threads per token
   const int tt = min(tid >> lg, T - 1), col = tid & (G - 1);   // token and first vector
   const bool tok = (tid >> lg) < T;                      // thread has a token
   const int nvt = (nvr + G - 1) >> lg;                   // vectors per thread (uniform)
   uint4 v[kDecMaxVec];
   if constexpr (XM != 0) {
-    const uint4* const row = (const uint4*)a.x + (int64_t)tt * nvr;
+    if (xwave) {
+      const uint4* const row = (const uint4*)a.x + (int64_t)tt * nvr;
 #pragma unroll
-    for (int i = 0; i < kDecMaxVec; ++i)
-      if (i < nvt) v[i] = row[min(col + G * i, nvr - 1)];   // clamped duplicates are harmless
+      for (int i = 0; i < kDecMaxVec; ++i)
+        if (i < nvt) v[i] = row[min(col + G * i, nvr - 1)];   // clamped duplicates are harmless
+    }
   }
 
   // packed W -> LDS: job j = (tile j / np, pair j % np), one DMA per wave and
   // job. Lane l moves 16 bytes of row l % 16 at byte 64 p + 16 (l / 16); the
   // second step of a last odd pair re-reads the first (it is never computed).
-  for (int j = wave, r = wave / np, p = wave - (wave / np) * np; j < ntb * np; j += kDecWaves) {
+  // (by the wavefronts that do not quantize, when XW = 4: a wave's loads
+  // complete in order, so the quantizing waves then wait for x alone)
+  const int dw0 = XW < kDecWaves ? XW : 0, ndw = kDecWaves - dw0;
+  if (wave >= dw0)
+  for (int j = wave - dw0, r = j / np, p = j - r * np; j < ntb * np; j += ndw) {
     const int ch = lane >> 4;
     const int chs = (2 * p + (ch >> 1) < ns) ? ch : ch - 2;
     const int o = min((tb + r) * 16 + r16, O - 1);
     dma16(a.packed + (int64_t)o * a.pitch + 64 * p + 16 * chs, wsm + j * 1024);
-    for (p += kDecWaves; p >= np; p -= np) ++r;          // (r, p) of job j + kDecWaves
+    for (p += ndw; p >= np; p -= np) ++r;                // (r, p) of job j + ndw
   }
   for (int i = tid; i < ntb * 256; i += kDecThreads) red[i] = 0;
 
@@ -170,14 +182,14 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
     uint32_t m = 0;
 #pragma unroll
     for (int i = 0; i < kDecMaxVec; ++i)
-      if (i < nvt) m = max(m, absmax_vec<BF>(v[i]));
+      if (xwave && i < nvt) m = max(m, absmax_vec<BF>(v[i]));
     m = row_max_dpp(m);
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x142, 0xA, 0xF, false));
     if (G >= 64) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x143, 0xC, 0xF, false));
     const uint32_t m_lo = __builtin_amdgcn_readlane(m, 31), m_hi = __builtin_amdgcn_readlane(m, 63);
     uint32_t mt = m_hi;                                  // G == 64: one wave per token
     if (G != 64) {                                       // (uniform over the workgroup)
-      if (lane == 0) {
+      if (lane == 0 && xwave) {
         pmax[2 * wave] = G >= 64 ? m_hi : m_lo;
         pmax[2 * wave + 1] = m_hi;
       }
@@ -202,12 +214,12 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
       }
     }
     const ActScale sc = act_scale(mt, a.eps);
-    if (col == 0 && tok) sxs[tt] = sc.s;
+    if (col == 0 && tok && xwave) sxs[tt] = sc.s;
     int8_t* const xrow = xs + tt * XP;
 #pragma unroll
     for (int i = 0; i < kDecMaxVec; ++i) {
       const int c = col + G * i;
-      if (i < nvt && c < nvr && tok) {
+      if (xwave && i < nvt && c < nvr && tok) {
         const uint2 q = act_codes_vec<BF>(v[i], sc.q);
         if constexpr (BF) *(uint2*)(xrow + c * EV) = q;
         else *(uint32_t*)(xrow + c * EV) = q.x;
@@ -324,11 +336,16 @@ hipError_t launch_decode(const void* x, int xmode, const float* sx, float eps, c
   const int blocks = dec_blocks(O);
   const int R = (int)cdiv(cdiv(O, 16), blocks);
   const int ntiles = (int)cdiv(O, 16);
+  // four quantizing wavefronts when a token gets at least one of them (T <= 4)
+  // and its vectors fit their registers; else all eight (T = 5..8: one
+  // wavefront per token, whose maximum needs no barrier)
+  const int64_t nvr = K / (xmode == 1 ? 8 : 4);
+  const int xw = (xmode != 0 && T <= 4 && cdiv(nvr, dec_group((int)T, 256)) <= kDecMaxVec) ? 4 : 8;
   int lg = 0;                                  // log2 of the threads per token
-  while ((1 << lg) < dec_group((int)T)) ++lg;
+  while ((1 << lg) < dec_group((int)T, 64 * xw)) ++lg;
   const DecodeArgs a{x, sx, eps, (const uint8_t*)packed, (int)row_pitch(K, N, M), sw,
                      (int)sw_inc, (int)T, (int)O, (int)K, R, ntiles / blocks, ntiles % blocks, lg,
-                     y, acc};
+                     xw, y, acc};
   if (index_form(N, M))
     return y_bf16 ? dispatch_x<true, true>(xmode, a, blocks, s)
                   : dispatch_x<true, false>(xmode, a, blocks, s);
