@@ -21,10 +21,10 @@
 //    is shared by 64 XW / T' threads, T' = T rounded up to a power of two; with
 //    one wavefront per token its maximum needs no barrier), into int8 rows in
 //    LDS -- the same arithmetic as the stand-alone quantizer, so the codes are
-//    identical -- or, when xq is given, copied by LDS-DMA. For T <= 4, XW = 4
-//    and the other four wavefronts issue the weight copies: a wave's loads
-//    complete in order, so the quantizing waves then wait for x alone and
-//    quantize while the weights are in flight;
+//    identical -- or, when xq is given, copied by LDS-DMA. For T <= 8 (when a
+//    row fits), XW = 4 and the other four wavefronts issue the weight copies:
+//    a wave's loads complete in order, so the quantizing waves then wait for x
+//    alone and quantize while the weights are in flight;
 //  - the waves then split the K-steps of each tile (MFMA A operand = 8 bytes of
 //    packed W per lane and K-step, the operand layout of the prefill kernel;
 //    B = the int8 rows, columns t >= T read row T-1 and are never stored),
@@ -98,8 +98,9 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// XM: 0 = xq given, 1 = bf16 x, 2 = fp32 x.
-template <bool SP, int XM, bool YBF16>
+// XM: 0 = xq given, 1 = bf16 x, 2 = fp32 x. NV: most activation vectors of
+// one thread (the loads and codes are unrolled NV times; few is faster).
+template <bool SP, int XM, bool YBF16, int NV>
 __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int T = a.T, O = a.O, K = a.K;
@@ -139,12 +140,13 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   const int tt = min(tid >> lg, T - 1), col = tid & (G - 1);   // token and first vector
   const bool tok = (tid >> lg) < T;                      // thread has a token
   const int nvt = (nvr + G - 1) >> lg;                   // vectors per thread (uniform)
-  uint4 v[kDecMaxVec];
+  static_assert(NV <= kDecMaxVec, "activation registers");
+  uint4 v[NV];
   if constexpr (XM != 0) {
     if (xwave) {
       const uint4* const row = (const uint4*)a.x + (int64_t)tt * nvr;
 #pragma unroll
-      for (int i = 0; i < kDecMaxVec; ++i)
+      for (int i = 0; i < NV; ++i)
         if (i < nvt) v[i] = row[min(col + G * i, nvr - 1)];   // clamped duplicates are harmless
     }
   }
@@ -181,14 +183,16 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
     // wave), then over the token's waves through LDS
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < kDecMaxVec; ++i)
+    for (int i = 0; i < NV; ++i)
       if (xwave && i < nvt) m = max(m, absmax_vec<BF>(v[i]));
     m = row_max_dpp(m);
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x142, 0xA, 0xF, false));
     if (G >= 64) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x143, 0xC, 0xF, false));
     const uint32_t m_lo = __builtin_amdgcn_readlane(m, 31), m_hi = __builtin_amdgcn_readlane(m, 63);
-    uint32_t mt = m_hi;                                  // G == 64: one wave per token
-    if (G != 64) {                                       // (uniform over the workgroup)
+    // a wavefront that holds whole tokens (G = 64: one; G = 32: one per half)
+    // has their maxima in lanes 63 and 31: no barrier
+    uint32_t mt = (G == 32 && lane < 32) ? m_lo : m_hi;
+    if (G > 64) {                                        // (uniform over the workgroup)
       if (lane == 0 && xwave) {
         pmax[2 * wave] = G >= 64 ? m_hi : m_lo;
         pmax[2 * wave + 1] = m_hi;
@@ -202,22 +206,16 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
         pm[4 * k] = q4.x; pm[4 * k + 1] = q4.y; pm[4 * k + 2] = q4.z; pm[4 * k + 3] = q4.w;
       }
       mt = 0;
-      if (G > 64) {
-        const int w0 = tt << (lg - 6), w1 = (tt + 1) << (lg - 6);   // the token's waves
+      const int w0 = tt << (lg - 6), w1 = (tt + 1) << (lg - 6);   // the token's waves
 #pragma unroll
-        for (int w = 0; w < kDecWaves; ++w)
-          if (w >= w0 && w < w1) mt = max(mt, pm[2 * w]);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-          if (k == tt) mt = pm[k];
-      }
+      for (int w = 0; w < kDecWaves; ++w)
+        if (w >= w0 && w < w1) mt = max(mt, pm[2 * w]);
     }
     const ActScale sc = act_scale(mt, a.eps);
     if (col == 0 && tok && xwave) sxs[tt] = sc.s;
     int8_t* const xrow = xs + tt * XP;
 #pragma unroll
-    for (int i = 0; i < kDecMaxVec; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int c = col + G * i;
       if (xwave && i < nvt && c < nvr && tok) {
         const uint2 q = act_codes_vec<BF>(v[i], sc.q);
@@ -293,9 +291,9 @@ int dec_blocks(int64_t O) {
   return (int)(nb < ntiles ? nb : ntiles);
 }
 
-template <bool SP, int XM, bool YBF16>
+template <bool SP, int XM, bool YBF16, int NV>
 hipError_t run_decode(const DecodeArgs& a, int blocks, hipStream_t s) {
-  auto kern = k_decode<SP, XM, YBF16>;
+  auto kern = k_decode<SP, XM, YBF16, NV>;
   const int lds = dec_lds(a.T, a.K, a.R);
   if (lds > 65536) {
     static int set = 0;   // the attribute is per kernel; raised as needed
@@ -311,10 +309,16 @@ hipError_t run_decode(const DecodeArgs& a, int blocks, hipStream_t s) {
 }
 
 template <bool SP, bool YBF16>
-hipError_t dispatch_x(int xmode, const DecodeArgs& a, int blocks, hipStream_t s) {
-  if (xmode == 0) return run_decode<SP, 0, YBF16>(a, blocks, s);
-  if (xmode == 1) return run_decode<SP, 1, YBF16>(a, blocks, s);
-  return run_decode<SP, 2, YBF16>(a, blocks, s);
+hipError_t dispatch_x(int xmode, int nv, const DecodeArgs& a, int blocks, hipStream_t s) {
+  if (xmode == 0) return run_decode<SP, 0, YBF16, 1>(a, blocks, s);
+  if (xmode == 1) {
+    if (nv <= 4) return run_decode<SP, 1, YBF16, 4>(a, blocks, s);
+    if (nv <= 8) return run_decode<SP, 1, YBF16, 8>(a, blocks, s);
+    return run_decode<SP, 1, YBF16, kDecMaxVec>(a, blocks, s);
+  }
+  if (nv <= 4) return run_decode<SP, 2, YBF16, 4>(a, blocks, s);
+  if (nv <= 8) return run_decode<SP, 2, YBF16, 8>(a, blocks, s);
+  return run_decode<SP, 2, YBF16, kDecMaxVec>(a, blocks, s);
 }
 
 }  // namespace
@@ -336,21 +340,21 @@ hipError_t launch_decode(const void* x, int xmode, const float* sx, float eps, c
   const int blocks = dec_blocks(O);
   const int R = (int)cdiv(cdiv(O, 16), blocks);
   const int ntiles = (int)cdiv(O, 16);
-  // four quantizing wavefronts when a token gets at least one of them (T <= 4)
-  // and its vectors fit their registers; else all eight (T = 5..8: one
-  // wavefront per token, whose maximum needs no barrier)
+  // four quantizing wavefronts when a token gets at least half of one of them
+  // (T <= 8) and its vectors fit their registers; else all eight
   const int64_t nvr = K / (xmode == 1 ? 8 : 4);
-  const int xw = (xmode != 0 && T <= 4 && cdiv(nvr, dec_group((int)T, 256)) <= kDecMaxVec) ? 4 : 8;
+  const int xw = (xmode != 0 && T <= 8 && cdiv(nvr, dec_group((int)T, 256)) <= kDecMaxVec) ? 4 : 8;
   int lg = 0;                                  // log2 of the threads per token
   while ((1 << lg) < dec_group((int)T, 64 * xw)) ++lg;
   const DecodeArgs a{x, sx, eps, (const uint8_t*)packed, (int)row_pitch(K, N, M), sw,
                      (int)sw_inc, (int)T, (int)O, (int)K, R, ntiles / blocks, ntiles % blocks, lg,
                      xw, y, acc};
+  const int nv = xmode == 0 ? 0 : (int)cdiv(nvr, (int64_t)1 << lg);   // vectors per thread
   if (index_form(N, M))
-    return y_bf16 ? dispatch_x<true, true>(xmode, a, blocks, s)
-                  : dispatch_x<true, false>(xmode, a, blocks, s);
-  return y_bf16 ? dispatch_x<false, true>(xmode, a, blocks, s)
-                : dispatch_x<false, false>(xmode, a, blocks, s);
+    return y_bf16 ? dispatch_x<true, true>(xmode, nv, a, blocks, s)
+                  : dispatch_x<true, false>(xmode, nv, a, blocks, s);
+  return y_bf16 ? dispatch_x<false, true>(xmode, nv, a, blocks, s)
+                : dispatch_x<false, false>(xmode, nv, a, blocks, s);
 }
 
 }  // namespace sbl
