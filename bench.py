@@ -530,7 +530,7 @@ def main():
         calibrate_copy()
         return
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU (no multi-GPU path); --gpus must be 1",
                           "n_gpus": a.gpus}))
         sys.exit(2)
     torch.cuda.init()

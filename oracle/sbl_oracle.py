@@ -444,7 +444,7 @@ def unpack(packed: np.ndarray, O: int, K: int, N: int, M: int):
 def mask_words(mask: np.ndarray) -> np.ndarray:
     """The library's bit layout of a keep-mask: uint32 [O, C] with
     C = ceil(K/128)*4 words per row; bit e of word c is the mask of column
-    k = 32c + e (0 for k >= K). (A storage layout of this build, not a
+    k = 32c + e (0 for k >= K). (A storage layout of the library, not a
     definition of the pages.)"""
     mask = np.asarray(mask, dtype=np.uint8)
     O, K = mask.shape
