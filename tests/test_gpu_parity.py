@@ -394,7 +394,8 @@ def test_absmean_outliers_in_some_blocks(S, dt):
         r = S.sbl_quant_mask_weight(dev(W), 6, 8)
         gs = host(r["gamma_sw"])
         assert f32_bits(gs[0]) == f32_bits(g_ref) and f32_bits(gs[1]) == f32_bits(sw_ref)
-    for order in ((clean, dirty, wide), (dirty, clean), (clean, clean, wide, clean)):
+    for order in ((clean, dirty, wide), (dirty, clean), (clean, clean, wide, clean),
+                  (clean, dirty, clean, wide, dirty, clean, wide, clean)):   # the largest batch
         outs = S.sbl_quant_mask_weight_batch([{"w": dev(W)} for W in order], 6, 8)
         for W, r in zip(order, outs):
             g_ref, sw_ref = o.absmean(W)
