@@ -438,6 +438,25 @@ __device__ __forceinline__ uint32_t drop_low_keep_bits8(const uint32_t* a) {
   return 0xFFu & ~(b1 | b2);
 }
 
+// Keep bits of a group of 8 when N = 2: the two highest in keep priority (a
+// larger |w| first, equal magnitudes the lower index) -- the set the rank
+// rule above keeps -- by one scan in index order that tracks the best and
+// second-best slot (6 operations per slot instead of 3 per pair).
+__device__ __forceinline__ uint32_t keep_top2_bits8(const uint32_t* a) {
+  const bool c = a[1] > a[0];                 // slot 1 above slot 0
+  uint32_t v1 = c ? a[1] : a[0], b1 = c ? 2u : 1u;
+  uint32_t v2 = c ? a[0] : a[1], b2 = c ? 1u : 2u;
+#pragma unroll
+  for (int j = 2; j < 8; ++j) {
+    const bool c1 = a[j] > v1, c2 = a[j] > v2;
+    v2 = c1 ? v1 : (c2 ? a[j] : v2);
+    b2 = c1 ? b1 : (c2 ? (1u << j) : b2);
+    v1 = c1 ? a[j] : v1;
+    b1 = c1 ? (1u << j) : b1;
+  }
+  return b1 | b2;
+}
+
 // The two slots an index-form group of 4 selects: its kept slots (bits 0..3
 // of kb), completed by the lowest free slots while fewer than two are set.
 __device__ __forceinline__ uint32_t select2(uint32_t kb) {
@@ -531,6 +550,7 @@ __global__ __launch_bounds__(kAbsThreads) void k_absmean_partial_kept(
       if constexpr (SEL == 1) kb = drop_low_keep_bits8<1>(a + g * M);
       else if constexpr (SEL == 2) kb = drop_low_keep_bits8<2>(a + g * M);
       else if constexpr (SEL == 3) kb = 0xFFu;
+      else if constexpr (SEL == 4) kb = keep_top2_bits8(a + g * M);
       else kb = topn_keep_bits<M>(a + g * M, N);
       keep |= kb << (g * M);
     }
@@ -569,7 +589,7 @@ static_assert(kAbsPerTensor % 64 == 0, "compact records: whole loads per lane");
 
 // SEL: how the mask is found -- 0: rank rule (any N); for M = 8 also
 // 1: drop the lowest slot (N = 7), 2: drop the two lowest (N = 6), 3: keep
-// all (N = 8).
+// all (N = 8), 4: keep the two highest (N = 2).
 
 template <bool BF16, int M, bool IDX, int SEL>
 __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int N,
@@ -750,6 +770,7 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
       if constexpr (SEL == 1) kb = drop_low_keep_bits8<1>(a + g * M);
       else if constexpr (SEL == 2) kb = drop_low_keep_bits8<2>(a + g * M);
       else if constexpr (SEL == 3) kb = 0xFFu;
+      else if constexpr (SEL == 4) kb = keep_top2_bits8(a + g * M);
       else kb = topn_keep_bits<M>(a + g * M, N);
       keep |= kb << (g * M);
     }
@@ -910,6 +931,7 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
     else if (N == 8) SBL_KEPT(BV, 8, 3);                              \
     else if (N == 7) SBL_KEPT(BV, 8, 1);                              \
     else if (N == 6) SBL_KEPT(BV, 8, 2);                              \
+    else if (N == 2) SBL_KEPT(BV, 8, 4);                              \
     else SBL_KEPT(BV, 8, 0)
     if (bf16) { SBL_KEPT_NM(true); } else { SBL_KEPT_NM(false); }
 #undef SBL_KEPT_NM
@@ -930,11 +952,11 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
   else if (N == 6) SBL_QMP(BV, 8, false, 2); \
   else SBL_QMP(BV, 8, false, 0)
   if (bf16) {
-    if (index_form(N, M)) { if (M == 4) SBL_QMP(true, 4, true, 0); else SBL_QMP(true, 8, true, 0); }
+    if (index_form(N, M)) { if (M == 4) SBL_QMP(true, 4, true, 0); else SBL_QMP(true, 8, true, 4); }
     else if (M == 4) SBL_QMP(true, 4, false, 0);
     else SBL_QMP8(true);
   } else {
-    if (index_form(N, M)) { if (M == 4) SBL_QMP(false, 4, true, 0); else SBL_QMP(false, 8, true, 0); }
+    if (index_form(N, M)) { if (M == 4) SBL_QMP(false, 4, true, 0); else SBL_QMP(false, 8, true, 4); }
     else if (M == 4) SBL_QMP(false, 4, false, 0);
     else SBL_QMP8(false);
   }

@@ -254,7 +254,7 @@ def test_mask_from_ternary_variant_parity(S, N, M, dt):
     assert differs
 
 
-@pytest.mark.parametrize("N,M", [(6, 8), (2, 4), (7, 8), (8, 8), (3, 8), (1, 4)])
+@pytest.mark.parametrize("N,M", [(6, 8), (2, 4), (7, 8), (8, 8), (3, 8), (1, 4), (2, 8)])
 @pytest.mark.parametrize("dt", ["fp32", "bf16"])
 def test_mask_then_quant_variant_parity(S, N, M, dt):
     """The composition-order ablation (gamma over the kept weights): gamma and
