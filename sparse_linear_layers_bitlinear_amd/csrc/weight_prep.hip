@@ -438,23 +438,62 @@ __device__ __forceinline__ uint32_t drop_low_keep_bits8(const uint32_t* a) {
   return 0xFFu & ~(b1 | b2);
 }
 
-// Keep bits of a group of 8 when N = 2: the two highest in keep priority (a
-// larger |w| first, equal magnitudes the lower index) -- the set the rank
-// rule above keeps -- by one scan in index order that tracks the best and
-// second-best slot (6 operations per slot instead of 3 per pair).
-__device__ __forceinline__ uint32_t keep_top2_bits8(const uint32_t* a) {
-  const bool c = a[1] > a[0];                 // slot 1 above slot 0
-  uint32_t v1 = c ? a[1] : a[0], b1 = c ? 2u : 1u;
-  uint32_t v2 = c ? a[0] : a[1], b2 = c ? 1u : 2u;
+// Keep bits of a group of 8 from a short sorted list instead of all ranks:
+// keep_topk_bits8<K> keeps the K highest (N = K), drop_lowk_keep_bits8<D>
+// drops the D lowest (N = 8 - D). Keep priority as in the rank rule: a larger
+// |w| first, equal magnitudes the lower index. One scan in index order
+// inserts each slot into a list of K (or D) (magnitude, slot) entries that
+// starts from sentinels: a later slot enters the kept list only if strictly
+// larger than an entry, the dropped list if not larger. About 3K operations
+// per slot and few registers, against 3 per pair for the rank rule.
+template <int K>
+__device__ __forceinline__ uint32_t keep_topk_bits8(const uint32_t* a) {
+  int v[K];                                   // |w| < 2^31: every slot beats -1
+  uint32_t b[K];
 #pragma unroll
-  for (int j = 2; j < 8; ++j) {
-    const bool c1 = a[j] > v1, c2 = a[j] > v2;
-    v2 = c1 ? v1 : (c2 ? a[j] : v2);
-    b2 = c1 ? b1 : (c2 ? (1u << j) : b2);
-    v1 = c1 ? a[j] : v1;
-    b1 = c1 ? (1u << j) : b1;
+  for (int k = 0; k < K; ++k) { v[k] = -1; b[k] = 0; }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int x = (int)a[j];
+    bool c[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) c[k] = x > v[k];
+#pragma unroll
+    for (int k = K - 1; k >= 1; --k) {
+      v[k] = c[k - 1] ? v[k - 1] : (c[k] ? x : v[k]);
+      b[k] = c[k - 1] ? b[k - 1] : (c[k] ? (1u << j) : b[k]);
+    }
+    v[0] = c[0] ? x : v[0];
+    b[0] = c[0] ? (1u << j) : b[0];
   }
-  return b1 | b2;
+  uint32_t keep = 0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) keep |= b[k];
+  return keep;
+}
+template <int D>
+__device__ __forceinline__ uint32_t drop_lowk_keep_bits8(const uint32_t* a) {
+  uint32_t v[D], b[D];                        // every |w| is at most the sentinel
+#pragma unroll
+  for (int k = 0; k < D; ++k) { v[k] = 0xFFFFFFFFu; b[k] = 0; }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t x = a[j];
+    bool c[D];
+#pragma unroll
+    for (int k = 0; k < D; ++k) c[k] = x <= v[k];
+#pragma unroll
+    for (int k = D - 1; k >= 1; --k) {
+      v[k] = c[k - 1] ? v[k - 1] : (c[k] ? x : v[k]);
+      b[k] = c[k - 1] ? b[k - 1] : (c[k] ? (1u << j) : b[k]);
+    }
+    v[0] = c[0] ? x : v[0];
+    b[0] = c[0] ? (1u << j) : b[0];
+  }
+  uint32_t drop = 0;
+#pragma unroll
+  for (int k = 0; k < D; ++k) drop |= b[k];
+  return 0xFFu & ~drop;
 }
 
 // The two slots an index-form group of 4 selects: its kept slots (bits 0..3
@@ -550,7 +589,10 @@ __global__ __launch_bounds__(kAbsThreads) void k_absmean_partial_kept(
       if constexpr (SEL == 1) kb = drop_low_keep_bits8<1>(a + g * M);
       else if constexpr (SEL == 2) kb = drop_low_keep_bits8<2>(a + g * M);
       else if constexpr (SEL == 3) kb = 0xFFu;
-      else if constexpr (SEL == 4) kb = keep_top2_bits8(a + g * M);
+      else if constexpr (SEL == 4) kb = keep_topk_bits8<2>(a + g * M);
+      else if constexpr (SEL == 5) kb = keep_topk_bits8<3>(a + g * M);
+      else if constexpr (SEL == 6) kb = drop_lowk_keep_bits8<3>(a + g * M);
+      else if constexpr (SEL == 7) kb = keep_topk_bits8<4>(a + g * M);
       else kb = topn_keep_bits<M>(a + g * M, N);
       keep |= kb << (g * M);
     }
@@ -589,7 +631,8 @@ static_assert(kAbsPerTensor % 64 == 0, "compact records: whole loads per lane");
 
 // SEL: how the mask is found -- 0: rank rule (any N); for M = 8 also
 // 1: drop the lowest slot (N = 7), 2: drop the two lowest (N = 6), 3: keep
-// all (N = 8), 4: keep the two highest (N = 2).
+// all (N = 8), 4: keep the two highest (N = 2), 5: the three highest (N = 3),
+// 6: drop the three lowest (N = 5), 7: keep the four highest (N = 4).
 
 template <bool BF16, int M, bool IDX, int SEL>
 __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int N,
@@ -770,7 +813,10 @@ __global__ __launch_bounds__(kQmpThreads) void k_qmp(const PrepBatchK batch, int
       if constexpr (SEL == 1) kb = drop_low_keep_bits8<1>(a + g * M);
       else if constexpr (SEL == 2) kb = drop_low_keep_bits8<2>(a + g * M);
       else if constexpr (SEL == 3) kb = 0xFFu;
-      else if constexpr (SEL == 4) kb = keep_top2_bits8(a + g * M);
+      else if constexpr (SEL == 4) kb = keep_topk_bits8<2>(a + g * M);
+      else if constexpr (SEL == 5) kb = keep_topk_bits8<3>(a + g * M);
+      else if constexpr (SEL == 6) kb = drop_lowk_keep_bits8<3>(a + g * M);
+      else if constexpr (SEL == 7) kb = keep_topk_bits8<4>(a + g * M);
       else kb = topn_keep_bits<M>(a + g * M, N);
       keep |= kb << (g * M);
     }
@@ -932,6 +978,9 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
     else if (N == 7) SBL_KEPT(BV, 8, 1);                              \
     else if (N == 6) SBL_KEPT(BV, 8, 2);                              \
     else if (N == 2) SBL_KEPT(BV, 8, 4);                              \
+    else if (N == 3) SBL_KEPT(BV, 8, 5);                              \
+    else if (N == 5) SBL_KEPT(BV, 8, 6);                              \
+    else if (N == 4) SBL_KEPT(BV, 8, 7);                              \
     else SBL_KEPT(BV, 8, 0)
     if (bf16) { SBL_KEPT_NM(true); } else { SBL_KEPT_NM(false); }
 #undef SBL_KEPT_NM
@@ -950,6 +999,9 @@ hipError_t launch_quant_mask_weight(const PrepTensor* items, int count, bool bf1
   if (N == 8) SBL_QMP(BV, 8, false, 3);     \
   else if (N == 7) SBL_QMP(BV, 8, false, 1); \
   else if (N == 6) SBL_QMP(BV, 8, false, 2); \
+  else if (N == 5) SBL_QMP(BV, 8, false, 6); \
+  else if (N == 3) SBL_QMP(BV, 8, false, 5); \
+  else if (N == 4) SBL_QMP(BV, 8, false, 7); \
   else SBL_QMP(BV, 8, false, 0)
   if (bf16) {
     if (index_form(N, M)) { if (M == 4) SBL_QMP(true, 4, true, 0); else SBL_QMP(true, 8, true, 4); }
