@@ -603,7 +603,7 @@ def _x_host(x, xdt):
     return bf16_round(x) if xdt == "bf16" else x
 
 
-@pytest.mark.parametrize("T", [1, 3, 8, 16])
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 16])
 @pytest.mark.parametrize("xdt", ["bf16", "fp32"])
 @pytest.mark.parametrize("N,M,O,K", [(2, 4, 200, 2560), (6, 8, 37, 1000), (2, 4, 64, 6912),
                                      (6, 8, 130, 8192), (2, 4, 48, 264), (1, 4, 16, 128),
