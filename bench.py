@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="qwen05b_ffn",
+    p.add_argument("--workload", default="qwen3b_sweep",
                    choices=["qwen05b_ffn", "qwen15b_ffn", "qwen3b_sweep", "bitnet_decode", "tiny"])
     p.add_argument("--nm", default=None, help="override N:M, e.g. 2:8")
     p.add_argument("--decode-T", type=int, default=8)
@@ -190,7 +190,7 @@ class PrefillStep:
                     self.dy[xn], self.xt[xn], dw=self.dw[xn], keep_bits=self.keep.get(xn))))
         return out
 
-    cold_weights = False   # inputs of every call were just written by the step: cache-hot
+    cold_weights = True    # each replay starts from a flushed last-level cache
 
     def run(self):
         """One step: act quant of the FFN input, one batched preparation of every
@@ -341,18 +341,32 @@ def capture(fn):
     return graph
 
 
+FLUSH_BYTES = 1 << 30     # > the 256 MB last-level cache (MALL) and the L2s
+
+
+def flush_buffer():
+    return torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+
+
 def time_steps(step, steps, warmup, eager):
+    """Device ms per step: HIP events on the launch stream around each step;
+    before each step (outside the events) a 1 GiB write evicts every cache
+    level, so each step reads its inputs and weights from HBM."""
     run = step.run if eager else capture(step.run).replay
+    flush = flush_buffer()
     for _ in range(warmup):
+        flush.fill_(1.0)
         run()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        flush.fill_(1.0)
+        a.record()
         run()
-    end.record()
+        b.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    return sum(a.elapsed_time(b) for a, b in evs) / steps
 
 
 def per_call_times(step, reps):
@@ -365,8 +379,7 @@ def per_call_times(step, reps):
     so that the weights come from HBM, as they do inside the step."""
     calls = step.calls()
     names = list(dict.fromkeys(n for n, _ in calls))
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0") if step.cold_weights \
-        else None
+    flush = flush_buffer() if step.cold_weights else None
     out, per_step = {}, {}
     for name in names:
         fs = [f for n, f in calls if n == name]
@@ -423,7 +436,7 @@ def cpu_baseline(wl_name, N, M, seconds, decode_T=None, backward=False):
                   f"recomputed{', forward + backward' if backward else ''}), repeated")
     times = []
     t_end = time.time() + seconds
-    while time.time() < t_end or len(times) < 2:
+    while time.time() < t_end or len(times) < 1:
         t0 = time.perf_counter()
         one()
         times.append(time.perf_counter() - t0)
@@ -446,8 +459,8 @@ def _cpu_model():
 
 
 TRAFFIC_FILES = [os.path.join(ROOT, "profiles", f)
-                 for f in ("traffic_qwen05b_ffn.txt", "traffic_bitnet_decode_t8.txt",
-                           "traffic_qwen15b_ffn_train.txt")]
+                 for f in ("traffic_qwen3b_sweep.txt", "traffic_qwen05b_ffn.txt",
+                           "traffic_bitnet_decode_t8.txt", "traffic_qwen15b_ffn_train.txt")]
 def measured_traffic(workload, kernel_call):
     """HBM bytes per launch of the dominant call from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary (scaled by the same counters on a plain

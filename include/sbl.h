@@ -104,15 +104,15 @@ sbl_status sbl_quant_act(const void* x, sbl_dtype xdt, int64_t T, int64_t K, int
  * activations are normalized -- RMSNorm in BitNet -- then quantized); BitNet
  * b1.58 2B4T summary, section 3.2 (subln normalization, no bias terms).
  * The pages fix no arithmetic for the norm; per row t this call computes
- *   sq_k = fp32(x_k * x_k), S = their fp64 sum in a fixed order (lane l of a
- *     64-lane group sums the 16-byte vectors l, l+64, ... in element order;
- *     the 64 partial sums are combined by an xor butterfly, offsets 32..1),
+ *   sq_k = fp32(x_k * x_k), S = their exact sum rounded once to the nearest
+ *     fp64 (independent of the order of the terms),
  *   r = fp32(1 / sqrt(S / K + eps_n)) in fp64,
  *   z_k = fp32(fp32(x_k * r) * gain[k])  (gain NULL: z_k = fp32(x_k * r)),
  * and then exactly sbl_quant_act on z (xq and sx as there; sx refers to z).
  * gain: optional device float [K] (16-byte aligned). eps_n > 0, normal.
  * Rows must be 16-byte aligned (ldx * element size % 16 == 0) and K a
- * multiple of 8 (bf16) or 4 (fp32), else SBL_ERR_SHAPE.
+ * multiple of 8 (bf16) or 4 (fp32), else SBL_ERR_SHAPE. |x| < 2^64 (finite
+ * squares), else the result is unspecified.
  */
 sbl_status sbl_rmsnorm_quant_act(const void* x, sbl_dtype xdt, const float* gain, int64_t T,
                                  int64_t K, int64_t ldx, float eps_n, float eps_a, int8_t* xq,
@@ -248,7 +248,10 @@ sbl_status sbl_unpack(const void* packed, int64_t O, int64_t K, int N, int M, in
  * y: device [T,O] of ydt (written); acc: optional device int32 [T,O].
  * 2:4 weights run on the gfx950 sparse MFMA (smfmac); other N:M on dense
  * int8 MFMA; small T uses a bandwidth-oriented variant. Same results.
- * T = 0 or O = 0: nothing is enqueued.
+ * T = 0 or O = 0: nothing is enqueued. Extent limits (SBL_ERR_SHAPE beyond,
+ * checked before anything else is looked at): T < 2^31, O < 2^31, and each
+ * operand below 2^31 -- T*K (xq bytes), O*pitch (packed bytes), T*O (y and
+ * acc elements); the kernels address them with 32-bit offsets.
  */
 sbl_status sbl_gemm(const int8_t* xq, const float* sx, const void* packed, const float* sw,
                     int64_t sw_inc, int64_t T, int64_t O, int64_t K, int N, int M, void* y,
@@ -267,6 +270,7 @@ sbl_status sbl_linear_fwd_workspace(int64_t T, int64_t O, int64_t K, int N, int 
  * of wdt) and prepacked (device packed buffer, with sw_prepacked / sw_inc as
  * in sbl_gemm) must be non-NULL. y: device [T,O] of ydt.
  * ws: at least sbl_linear_fwd_workspace bytes (scratch).
+ * Extent limits as sbl_gemm (SBL_ERR_SHAPE beyond).
  */
 sbl_status sbl_linear_fwd(const void* x, sbl_dtype xdt, const void* w_master, sbl_dtype wdt,
                           const void* prepacked, const float* sw_prepacked, int64_t sw_inc,

@@ -19,7 +19,8 @@ value decides an integer (the int8 activation code, the ternary code) the
 decision is taken in IEEE fp32 -- the precision the kernels compute in -- so
 both sides take it identically. The absmean sum is exact (correctly rounded
 to fp64). The dequantized output is computed in fp64 from the exact int32
-accumulator.
+accumulator; the bf16 output is the bf16 rounding of the same product
+taken in the reading's fixed fp32 order (``dequant_f32``).
 
 Pins (what checks this file against something other than itself) live in
 tests/test_oracle_pins.py: brute-force integer GEMM, exhaustive mask
@@ -39,10 +40,10 @@ import numpy as np
 
 __all__ = [
     "quant_act", "absmean", "nm_mask", "ternary_codes", "apply_mask",
-    "quant_mask_weight", "gemm_int", "gemm_int_bruteforce", "dequant",
+    "quant_mask_weight", "gemm_int", "gemm_int_bruteforce", "dequant", "dequant_f32",
     "to_bf16", "linear_fwd", "packed_row_bytes", "packed_bytes", "pack",
     "unpack", "INDEX_FORM", "mask_words", "mask_flips", "group_threshold",
-    "rms_scale", "rmsnorm_quant_act", "dropped_max",
+    "rms_scale", "sum_squares", "rmsnorm_quant_act", "dropped_max",
     "act_dequant_bf16", "linear_bwd_dx", "linear_bwd_dw",
 ]
 
@@ -221,6 +222,17 @@ def dequant(acc: np.ndarray, sx: np.ndarray, sw) -> np.ndarray:
     sw = np.broadcast_to(np.asarray(sw, dtype=np.float64), (acc.shape[1],))
     return (acc.astype(np.float64) * np.asarray(sx, dtype=np.float64)[:, None]
             * sw[None, :])
+
+
+def dequant_f32(acc: np.ndarray, sx: np.ndarray, sw) -> np.ndarray:
+    """y[t, o] = fp32(fp32(fp32(acc) * sx[t]) * sw[o]): the same product as
+    ``dequant`` taken in IEEE fp32, left to right, each step rounded to
+    nearest (the reading of the dequant arithmetic: one fixed fp32 order, no
+    fused multiply-add). fp32(acc) is exact (|acc| < 2^24). Returns float32;
+    ``to_bf16`` of it is the bf16 output."""
+    sw = np.broadcast_to(np.asarray(sw, dtype=F32), (acc.shape[1],))
+    a = np.asarray(acc).astype(F32)
+    return ((a * np.asarray(sx, dtype=F32)[:, None]).astype(F32) * sw[None, :]).astype(F32)
 
 
 def to_bf16(y: np.ndarray) -> np.ndarray:
@@ -499,40 +511,36 @@ def group_threshold(w: np.ndarray, N: int, M: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Q_a(Norm(x)): RMS normalization before the activation quantizer
 # ---------------------------------------------------------------------------
-def rms_scale(x: np.ndarray, eps_n: float, vec: int) -> np.ndarray:
-    """Per-row r = fp32(1 / sqrt(S / K + eps_n)).
+def rms_scale(x: np.ndarray, eps_n: float) -> np.ndarray:
+    """Per-row r = fp32(1 / sqrt(S / K + eps_n)), S = sum_k fp32(x_k * x_k).
 
     [SB] Algorithm 1 walk-through: x~ = Q_a(Norm(x)), Norm likely RMSNorm;
     [B2T] section 3.2: subln normalization without bias terms. The pages fix
-    no arithmetic; reading (the kernel's): sq_k = fp32(x_k * x_k); S is their
-    fp64 sum in this order -- lane l of 64 sums the vectors l, l+64, ... of
-    `vec` consecutive elements, element by element; the 64 lane sums are
-    combined by an xor butterfly (offsets 32, 16, ..., 1); then fp64 division,
-    square root and reciprocal, rounded once to fp32.
-    x: [T, K] float32 with K % vec == 0. Returns float32 [T]."""
+    no arithmetic; reading: the squares are fp32 products; S is their exact
+    sum rounded once to fp64 (math.fsum, so no summation order is implied);
+    then fp64 division by K, addition of eps_n, square root and reciprocal,
+    rounded once to fp32. x: [T, K] float32 with finite squares. Returns
+    float32 [T]."""
     x = np.asarray(x, dtype=F32)
-    T, K = x.shape
-    assert K % vec == 0
-    sq = (x * x).astype(F32).astype(np.float64)         # fp32 products, exact in fp64
-    nvec = K // vec
-    U = -(-nvec // 64)
-    padded = np.zeros((T, U * 64, vec), np.float64)     # +0.0 padding adds nothing
-    padded[:, :nvec] = sq.reshape(T, nvec, vec)
-    per_lane = padded.reshape(T, U, 64, vec).transpose(0, 2, 1, 3).reshape(T, 64, U * vec)
-    S = np.cumsum(per_lane, axis=2)[:, :, -1]           # sequential per lane
-    lanes = np.arange(64)
-    for off in (32, 16, 8, 4, 2, 1):
-        S = S + S[:, lanes ^ off]
-    S = S[:, 0]
+    K = x.shape[1]
+    S = sum_squares(x)
     r = 1.0 / np.sqrt(S / float(K) + float(np.float32(eps_n)))
     return r.astype(F32)
 
 
-def rmsnorm_quant_act(x: np.ndarray, gain, eps_n: float, eps_a: float, vec: int):
+def sum_squares(x: np.ndarray) -> np.ndarray:
+    """Per row, S = sum_k fp32(x_k * x_k), the exact sum rounded once to
+    fp64 (math.fsum). Returns float64 [T]."""
+    x = np.asarray(x, dtype=F32)
+    sq = (x * x).astype(F32).astype(np.float64)         # fp32 products, exact in fp64
+    return np.array([math.fsum(sq[t]) for t in range(x.shape[0])], dtype=np.float64)
+
+
+def rmsnorm_quant_act(x: np.ndarray, gain, eps_n: float, eps_a: float):
     """z = fp32(fp32(x * r) * gain) per element (gain None: fp32(x * r)),
     then quant_act(z). Returns (xq int8 [T, K], sx float32 [T])."""
     x = np.asarray(x, dtype=F32)
-    r = rms_scale(x, eps_n, vec)
+    r = rms_scale(x, eps_n)
     z = (x * r[:, None]).astype(F32)
     if gain is not None:
         z = (z * np.asarray(gain, dtype=F32)[None, :]).astype(F32)

@@ -25,7 +25,7 @@
 // lane 4j + q pointing at row base + j, column 4q, lane i gets column i of
 // rows base..base+3.
 #include "sbl_internal.h"
-#include "device_util.cuh"
+#include "device_util.h"
 
 #include <algorithm>
 #include <type_traits>

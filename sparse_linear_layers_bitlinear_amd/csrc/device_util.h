@@ -129,10 +129,10 @@ __device__ __forceinline__ uint2 act_codes_vec(const uint4& d, float q) {
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Raw buffer resource over [base, base + 4 GiB): loads take a per-lane 32-bit
-// offset plus a wave-uniform scalar offset, so address arithmetic costs no
-// VALU. Offsets are always in bounds by construction (no reliance on the
-// hardware range check).
+// Raw buffer resource over [base, base + 2 GiB - 1): loads take a per-lane
+// 32-bit offset plus a wave-uniform scalar offset, so address arithmetic
+// costs no VALU. Offsets are always in bounds by construction (callers keep
+// every buffer below 2^31 bytes; no reliance on the hardware range check).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF,
                                            0x00020000);

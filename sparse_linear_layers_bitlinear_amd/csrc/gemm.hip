@@ -27,7 +27,7 @@
 // Staged rows have pitches of 80 / 144 bytes so that the 16-byte fragment
 // reads of 16 consecutive rows fall in distinct banks.
 #include "sbl_internal.h"
-#include "device_util.cuh"
+#include "device_util.h"
 
 #include <cmath>
 #include <cstdlib>
@@ -1018,7 +1018,7 @@ template <int WO, int KS, int FI, int FJ, int NA, bool SP, bool KA16, bool YBF16
 static hipError_t launch_ra(const Args& a, hipStream_t s) {
   using C = RaCfg<WO, KS, FI, FJ, NA>;
   // 16-byte xq segments and 32-bit buffer offsets
-  if (!KA16 || a.T * a.K >= (int64_t(1) << 31))
+  if (!KA16 || a.T * a.K >= (int64_t(1) << 31) || a.O * a.pitch >= (int64_t(1) << 31))
     return launch_cfg<128, 128, 2, 2, SP, KA16, YBF16>(a, s);
   auto kern = k_gemm_ra<WO, KS, FI, FJ, NA, SP, YBF16>;
   if (C::LDS > 65536) {

@@ -31,7 +31,7 @@
 //    add their int32 partial sums into LDS (ds_add, exact), and the
 //    workgroup dequantizes y = fp32(fp32(acc * s_x) * s_w).
 #include "sbl_internal.h"
-#include "device_util.cuh"
+#include "device_util.h"
 
 #include <cstdlib>
 

@@ -12,7 +12,8 @@
 // re-read their tail from L2. HBM traffic is the algorithmic 3 bytes/element
 // (bf16) + 4 bytes/token.
 #include "sbl_internal.h"
-#include "device_util.cuh"
+#include "device_util.h"
+#include "exact_sum.h"
 
 namespace sbl {
 
@@ -98,16 +99,21 @@ __global__ __launch_bounds__(256) void k_quant_act_scalar(const void* __restrict
 // Sparse-BitNet summary, section 3.4 (Algorithm 1 walk-through: the input is
 // normalized, RMSNorm in the BitNet architecture, then quantized); BitNet
 // b1.58 2B4T summary, section 3.2 (subln normalization, no bias terms).
-// The pages fix no arithmetic; this kernel defines it, per row:
-//   sq_k = fp32(x_k * x_k); lane l of the row's wavefront owns the 16-byte
-//   vectors l, l + 64, ... and adds their sq_k in fp64, vector by vector in
-//   element order; the 64 lane sums are combined by an xor butterfly
-//   (offsets 32, 16, ..., 1), so every lane holds the same S;
+// The pages fix no arithmetic; this kernel computes, per row:
+//   sq_k = fp32(x_k * x_k),
+//   S = sum_k sq_k, exactly, rounded once to the nearest fp64 -- the result
+//       does not depend on the order of the terms (see exact_sum.h),
 //   r = fp32(1 / sqrt(S / K + eps_n))   (fp64 division, square root, division)
 //   z_k = fp32(fp32(x_k * r) * g_k)     (without g: z_k = fp32(x_k * r))
 // and then exactly the quantizer above on z. x is read once (plus g, which
 // stays in L2) and only the int8 codes are written: the HBM round trip of a
 // separate normalized tensor is gone.
+//
+// The exact sum: every lane marks the 32-binade windows its squares fall in;
+// for each window present in the row (a wave-uniform loop, usually two or
+// three windows) every lane adds its squares of that window as integers into
+// a 96-bit register accumulator, the wave sums the accumulators exactly, and
+// the row's 16 window bins are turned into the fp64 S.
 // ---------------------------------------------------------------------------
 template <bool BF16>
 __device__ __forceinline__ void unpack_f32(const uint4& d, float* f) {
@@ -145,21 +151,59 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant_act(const void* __restric
     const int64_t i = lane + 64 * u;
     d[u] = i < nvec ? row[i] : make_uint4(0, 0, 0, 0);   // zeros add +0 to S
   }
-  double S = 0.0;
-  auto add_sq = [&](const uint4& v) {
+  // square of element e of a vector, as a sign-free fp32 bit pattern
+  auto sq_bits = [&](const uint4& v, int e) -> uint32_t {
     float f[V];
     unpack_f32<BF16>(v, f);
+    const float p = f[e] * f[e];
+    return __float_as_uint(p);
+  };
+  // windows holding a nonzero square (per lane, then over the wave)
+  uint32_t tags = 0;
+  auto mark = [&](const uint4& v) {
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      const float p = f[e] * f[e];
-      S += (double)p;
+      uint32_t tg;
+      uint64_t tv;
+      exact_term(sq_bits(v, e), tg, tv);
+      tags |= (tv != 0 ? 1u : 0u) << tg;
     }
   };
 #pragma unroll
-  for (int u = 0; u < kActCache; ++u) add_sq(d[u]);
-  for (int64_t i = lane + 64 * kActCache; i < nvec; i += 64) add_sq(row[i]);
+  for (int u = 0; u < kActCache; ++u) mark(d[u]);
+  for (int64_t i = lane + 64 * kActCache; i < nvec; i += 64) mark(row[i]);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) S = S + __shfl_xor(S, off, 64);
+  for (int off = 32; off >= 1; off >>= 1) tags |= (uint32_t)__shfl_xor((int)tags, off, 64);
+  tags = __builtin_amdgcn_readfirstlane(tags);
+  unsigned long long bins[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) bins[j] = 0;
+  while (tags) {                                         // (wave-uniform)
+    const uint32_t tw = 31u - __clz(tags);
+    tags &= ~(1u << tw);
+    uint32_t a0 = 0, a1 = 0, a2 = 0;
+    auto add = [&](const uint4& v) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        uint32_t tg;
+        uint64_t tv;
+        exact_term(sq_bits(v, e), tg, tv);
+        add96(a0, a1, a2, tg == tw ? tv : 0ull);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < kActCache; ++u) add(d[u]);
+    for (int64_t i = lane + 64 * kActCache; i < nvec; i += 64) add(row[i]);
+    const unsigned long long lo = wave_sum_u64(a0);
+    const unsigned long long hi = wave_sum_u64((unsigned long long)a1 | ((unsigned long long)a2 << 32));
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j == (int)tw) {
+        bins[2 * j] = lo;
+        bins[2 * j + 1] = hi;
+      }
+  }
+  const double S = exact_bins_to_f64(bins);
   const float r = (float)(1.0 / sqrt(S / (double)K + (double)eps_n));
 
   // z of vector i (V values)

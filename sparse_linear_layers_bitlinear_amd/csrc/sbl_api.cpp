@@ -42,6 +42,7 @@ using namespace sbl;
 namespace {
 
 constexpr int64_t kMaxK = int64_t(1) << 24;
+constexpr int64_t kLim31 = int64_t(1) << 31;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool dtype_ok(int d) { return d == SBL_BF16 || d == SBL_FP32; }
@@ -58,7 +59,16 @@ sbl_status hip_status(hipError_t e, const char* what) {
 sbl_status check_wshape(int64_t O, int64_t K, int N, int M) {
   if (!nm_ok(N, M)) return SBL_ERR_NM;
   if (O < 0 || K < 1 || K > kMaxK || K % M != 0) return SBL_ERR_SHAPE;
-  if (O > (int64_t(1) << 31)) return SBL_ERR_SHAPE;
+  if (O >= kLim31) return SBL_ERR_SHAPE;
+  return SBL_OK;
+}
+
+// Sizes one GEMM call can address: the kernels index every operand with
+// 32-bit offsets (xq [T,K] bytes, packed [O, pitch] bytes, y / acc [T,O]
+// elements), so each must stay below 2^31.
+sbl_status check_gemm_extent(int64_t T, int64_t O, int64_t K, int N, int M) {
+  if (T < 0 || T >= kLim31 || O >= kLim31) return SBL_ERR_SHAPE;
+  if (T * K >= kLim31 || O * row_pitch(K, N, M) >= kLim31 || T * O >= kLim31) return SBL_ERR_SHAPE;
   return SBL_OK;
 }
 
@@ -248,6 +258,8 @@ sbl_status sbl_gemm(const int8_t* xq, const float* sx, const void* packed, const
   sbl_status st = check_wshape(O, K, N, M);
   if (st != SBL_OK) return st;
   if (T < 0 || (sw_inc != 0 && sw_inc != 1)) return SBL_ERR_SHAPE;
+  st = check_gemm_extent(T, O, K, N, M);
+  if (st != SBL_OK) return st;
   if (T == 0 || O == 0) return SBL_OK;
   if (!xq || !sx || !packed || !sw || !y) return SBL_ERR_NULL;
   if (!aligned16(xq) || !aligned16(sx) || !aligned16(packed) || !aligned16(y) ||
@@ -276,6 +288,8 @@ sbl_status sbl_linear_fwd(const void* x, sbl_dtype xdt, const void* w_master, sb
   sbl_status st = check_wshape(O, K, N, M);
   if (st != SBL_OK) return st;
   if (T < 0) return SBL_ERR_SHAPE;
+  st = check_gemm_extent(T, O, K, N, M);
+  if (st != SBL_OK) return st;
   const bool pre = prepacked != nullptr;
   if (pre == (w_master != nullptr)) return SBL_ERR_NULL;  // exactly one weight source
   if (pre && sw_inc != 0 && sw_inc != 1) return SBL_ERR_SHAPE;

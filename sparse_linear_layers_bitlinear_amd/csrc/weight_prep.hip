@@ -19,7 +19,8 @@
 //                      loads and ranks it: top-N-of-M mask; then
 //                      code = sign(w) * (|w| >= t), packing.
 #include "sbl_internal.h"
-#include "device_util.cuh"
+#include "device_util.h"
+#include "exact_sum.h"
 
 namespace sbl {
 
@@ -33,13 +34,6 @@ namespace sbl {
 // magnitudes span far fewer than 32 binades). Bins hold (low 32 bits, rest)
 // pairs so that u64 LDS atomics cannot overflow for n < 2^31.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void add96(uint32_t& a0, uint32_t& a1, uint32_t& a2, uint64_t v) {
-  uint64_t lo = (uint64_t)a0 + (uint32_t)v;
-  uint64_t mid = (uint64_t)a1 + (uint32_t)(v >> 32) + (lo >> 32);
-  a0 = (uint32_t)lo;
-  a1 = (uint32_t)mid;
-  a2 += (uint32_t)(mid >> 32);
-}
 
 // Register accumulator of one window. Window 3 holds every |w| in
 // [2^-31, 2) (e' in [96, 127]), where practically all weights lie; any other
@@ -49,15 +43,6 @@ struct AbsSlot {
   uint32_t tag = kAbsWindow, a0 = 0, a1 = 0, a2 = 0;
 };
 
-// Term of |w| (bits u with the sign cleared): window tag and the 64-bit
-// integer m << (e' & 31), where m is the significand with the hidden bit for
-// normals (u - ((e' - 1) << 23) with e' = max(e, 1)). Zero gives v = 0.
-__device__ __forceinline__ void abs_term(uint32_t u, uint32_t& tag, uint64_t& v) {
-  const uint32_t ee = max(u >> 23, 1u);
-  const uint32_t m = u - ((ee - 1u) << 23);
-  tag = ee >> 5;
-  v = (uint64_t)m << (ee & 31u);
-}
 
 // Accumulate one |w| (any sign bit): terms of the slot's window go to the
 // 96-bit register accumulator with no branch (zeros add nothing, whatever
@@ -65,7 +50,7 @@ __device__ __forceinline__ void abs_term(uint32_t u, uint32_t& tag, uint64_t& v)
 __device__ __forceinline__ void abs_accumulate(AbsSlot& st, unsigned long long* bins, uint32_t u) {
   uint32_t tag;
   uint64_t v;
-  abs_term(u & 0x7FFFFFFFu, tag, v);
+  exact_term(u & 0x7FFFFFFFu, tag, v);
   const bool here = tag == st.tag || v == 0;
   const uint64_t vh = here ? v : 0;
   add96(st.a0, st.a1, st.a2, vh);
@@ -123,7 +108,7 @@ __device__ __forceinline__ PrepItemK prep_item(const PrepBatchK& b, int i) {
 __device__ __forceinline__ void abs_accumulate_other(unsigned long long* bins, uint32_t u) {
   uint32_t tag;
   uint64_t v;
-  abs_term(u & 0x7FFFFFFFu, tag, v);
+  exact_term(u & 0x7FFFFFFFu, tag, v);
   if (tag != kAbsWindow && v != 0) {
     atomicAdd(&bins[2 * tag], (unsigned long long)(uint32_t)v);
     atomicAdd(&bins[2 * tag + 1], (unsigned long long)(v >> 32));
@@ -302,52 +287,7 @@ __device__ float roundclip_threshold(float sw) {
 // The bins are exact integers: bin 2w holds low parts and bin 2w+1 high parts
 // of window w (weight 2^(32 w - 150)).
 __device__ PrepScalars scalars_from_bins(const unsigned long long* bins, int64_t n, float eps) {
-  // exact sum in units of 2^-150 as 32-bit limbs (registers only: constant indices)
-  constexpr int NL = 12;
-  uint32_t L[NL];
-  {
-    unsigned long long w[NL + 1];
-#pragma unroll
-    for (int i = 0; i <= NL; ++i) w[i] = 0;
-#pragma unroll
-    for (int tag = 0; tag < 8; ++tag) {
-      const unsigned long long lo = bins[2 * tag], hi = bins[2 * tag + 1];
-      w[tag] += lo & 0xFFFFFFFFull;
-      w[tag + 1] += (lo >> 32) + (hi & 0xFFFFFFFFull);
-      w[tag + 2] += hi >> 32;
-    }
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      w[i + 1] += w[i] >> 32;
-      L[i] = (uint32_t)w[i];
-    }
-  }
-  int top = -1;
-#pragma unroll
-  for (int i = 0; i < NL; ++i)
-    if (L[i]) top = i;
-  double S = 0.0;
-  if (top >= 0) {
-    // 96-bit window of the three highest limbs, plus a sticky bit for the rest
-    uint32_t h = 0, m = 0, l = 0;
-    bool below = false;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      if (i == top) h = L[i];
-      if (i == top - 1) m = L[i];
-      if (i == top - 2) l = L[i];
-      if (i < top - 2 && L[i]) below = true;
-    }
-    const int c = __clz(h);                               // h != 0
-    unsigned __int128 V = ((unsigned __int128)h << 64) | ((unsigned __int128)m << 32) | l;
-    V <<= c;                                              // bit 95 set
-    unsigned long long mant = (unsigned long long)(V >> 43) & ((1ull << 53) - 1);
-    const bool rb = (V >> 42) & 1;
-    const bool sticky = below || ((V & (((unsigned __int128)1 << 42) - 1)) != 0);
-    if (rb && (sticky || (mant & 1ull))) ++mant;          // nearest, ties to even
-    // value = V_window * 2^(32*(top-2)) * 2^-150, V_window = mant * 2^(43 - c)
-    S = ldexp((double)mant, 43 - c + 32 * (top - 2) - 150);
-  }
+  const double S = exact_bins_to_f64(bins);
   const double q = S / (double)n;
   PrepScalars r;
   r.gamma = (float)q;

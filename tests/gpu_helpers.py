@@ -43,19 +43,16 @@ def assert_f32_close(y_gpu, y_ref64, rtol=1e-3):
     assert float(rel.max(initial=0.0)) <= rtol, f"max rel err {rel.max()}"
 
 
-def _ordered(bits):
-    b = bits.astype(np.int32)
-    return np.where(b >= 0x8000, 0x8000 - b, b)
-
-
-def assert_bf16_close(y_gpu_f32, y_ref64, max_ulp=1):
-    """bf16 output: at most max_ulp bf16 steps from the correctly rounded value."""
-    ref = o.to_bf16(y_ref64)
-    gb = (np.asarray(y_gpu_f32, np.float32).view(np.uint32) >> 16).astype(np.uint32)
-    rb = (ref.view(np.uint32) >> 16).astype(np.uint32)
-    d = np.abs(_ordered(gb) - _ordered(rb))
-    assert int(d.max(initial=0)) <= max_ulp, f"max bf16 ulp distance {d.max()}"
-    return float((d == 0).mean()) if d.size else 1.0
+def assert_bf16_exact(y_gpu_f32, acc, sx, sw):
+    """bf16 output: bit-identical to the bf16 rounding (nearest even) of
+    fp32(fp32(acc * sx[t]) * sw[o]) -- the dequant product in the reading's
+    fixed fp32 order, from the oracle's exact int32 accumulator."""
+    ref = o.to_bf16(o.dequant_f32(acc, sx, sw).astype(np.float64))
+    got = np.asarray(y_gpu_f32, np.float32)
+    assert got.shape == ref.shape
+    bad = got.view(np.uint32) != ref.view(np.uint32)
+    assert not bad.any(), (f"{int(bad.sum())} of {bad.size} bf16 outputs differ, first at "
+                           f"{np.argwhere(bad)[0].tolist()}")
 
 
 def f32_bits(a):

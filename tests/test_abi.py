@@ -108,6 +108,15 @@ def test_gemm_and_linear_validation(S):
     assert L.sbl_gemm(*g(T=0)) == 0           # empty: nothing enqueued
     assert L.sbl_gemm(*g(O=0)) == 0
     assert L.sbl_gemm(*g(K=(1 << 24) + 8)) == 2
+    # every operand must stay below 2^31 bytes / elements (32-bit offsets):
+    # xq [T,K], packed [O, pitch], y [T,O]; T and O below 2^31
+    assert L.sbl_gemm(*g(T=1 << 31)) == 2
+    assert L.sbl_gemm(*g(O=1 << 31)) == 2
+    assert L.sbl_gemm(*g(T=1 << 21, K=1 << 10)) == 2                       # T K = 2^31
+    pitch = o.packed_row_bytes(1 << 14, 6, 8)
+    assert L.sbl_gemm(*g(T=4, O=-(-(1 << 31) // pitch), K=1 << 14)) == 2  # O pitch >= 2^31
+    assert L.sbl_gemm(*g(T=1 << 16, O=1 << 15, K=64)) == 2                  # T O = 2^31
+    assert L.sbl_gemm(*g(T=1 << 31, O=0)) == 2                              # checked before empty
     lf = lambda w=FAKE, pre=None, ws=FAKE, wsb=1 << 30, eps=1e-5, T=4: (
         FAKE, 0, w, 1, pre, FAKE, 0, T, 8, 64, 6, 8, eps, 1e-5, FAKE, 0, ws, wsb, None)
     assert L.sbl_linear_fwd(*lf(w=FAKE, pre=FAKE)) == 1      # both weight sources
@@ -115,6 +124,8 @@ def test_gemm_and_linear_validation(S):
     assert L.sbl_linear_fwd(*lf(wsb=8)) == 6
     assert L.sbl_linear_fwd(*lf(eps=0.0)) == 8
     assert L.sbl_linear_fwd(*lf(T=0)) == 0
+    assert L.sbl_linear_fwd(*lf(T=1 << 31)) == 2
+    assert L.sbl_linear_fwd(*lf(T=1 << 25)) == 2                             # T K = 2^31
     n = ctypes.c_size_t()
     assert L.sbl_linear_fwd_workspace(16, 128, 256, 6, 8, 0, ctypes.byref(n)) == 0
     assert n.value >= 16 * 256 + o.packed_bytes(128, 256, 6, 8)

@@ -368,6 +368,31 @@ def test_to_bf16_is_nearest_even():
     assert np.all(((bu[tie] >> 16) & 1) == 0)         # ties -> even
 
 
+def test_dequant_f32_rounds_each_step():
+    """dequant_f32 against exact rational arithmetic: each product of two
+    fp32 values is exact in Fraction, and np.float32(float(.)) of it is the
+    nearest fp32 (the fp64 conversion is exact: 48 significant bits), so
+    fp32(fp32(acc * sx) * sw) is fixed independently of numpy's float32
+    multiply; it stays within two fp32 roundings of the fp64 ``dequant``."""
+    from fractions import Fraction
+    rng = np.random.default_rng(12)
+    acc = rng.integers(-(127 * 8192), 127 * 8192, size=(6, 7)).astype(np.int32)
+    acc[0, 0] = 0
+    sx = rng.uniform(1e-4, 1.0, 6).astype(np.float32)
+    sw = rng.uniform(1e-3, 0.1, 7).astype(np.float32)
+    y = o.dequant_f32(acc, sx, sw)
+    assert y.dtype == np.float32
+    for t in range(6):
+        for j in range(7):
+            p1 = np.float32(float(Fraction(int(acc[t, j])) * Fraction(float(sx[t]))))
+            p2 = np.float32(float(Fraction(float(p1)) * Fraction(float(sw[j]))))
+            assert y[t, j] == p2
+    ref = o.dequant(acc, sx, sw)
+    assert np.all(np.abs(y - ref) <= 2.0 ** -23 * np.abs(ref))
+    # scalar sw broadcasts like a per-row vector of equal values
+    assert np.array_equal(o.dequant_f32(acc, sx, sw[2]), o.dequant_f32(acc, sx, np.full(7, sw[2])))
+
+
 # ------------------------------------------------------------ packed format --
 @pytest.mark.parametrize("M", [4, 8])
 def test_pack_roundtrip_all_nm(M):
@@ -468,25 +493,46 @@ def test_mask_words_hand_layout():
 
 
 # ------------------------------------------------------- Q_a(Norm(x)) ------
-def test_rms_scale_against_exact_sum():
-    """r against the exactly rounded sum of squares (math.fsum): the fixed
-    summation order costs at most a few fp64 ulps, invisible after the fp32
-    rounding except at rare ties; every term, K and eps placement pinned."""
+def test_sum_squares_exact_rational():
+    """S against exact rational arithmetic (fractions.Fraction, converted to
+    fp64 with correct rounding), on rows whose squares span many binades --
+    including sums a running fp64 total gets wrong (2^60 + 256 ones) and
+    squares that are fp32 denormals -- and invariant under any permutation."""
+    from fractions import Fraction
     rng = np.random.default_rng(11)
-    for (T, K, vec) in [(3, 64, 8), (5, 1000, 4), (2, 9000, 8)]:
-        x = rng.standard_normal((T, K)).astype(np.float32) * np.float32(3.0)
-        eps = 1e-6
-        r = o.rms_scale(x, eps, vec)
-        for t in range(T):
-            S = math.fsum(float(np.float32(v) * np.float32(v)) for v in x[t])
-            exact = 1.0 / math.sqrt(S / K + float(np.float32(eps)))
-            assert abs(float(r[t]) - exact) <= 1e-6 * exact
+    rows = [rng.standard_normal(1000).astype(np.float32) * np.float32(3.0),
+            np.concatenate([[np.float32(2.0 ** 30)], np.ones(256, np.float32)]),
+            (rng.standard_normal(600) * np.exp2(rng.integers(-70, 60, 600))).astype(np.float32),
+            np.array([2.0 ** -70, 2.0 ** -75, 3.0 * 2.0 ** -80, 0.0, -0.0], np.float32),
+            np.zeros(16, np.float32)]
+    for row in rows:
+        S = o.sum_squares(row[None, :])[0]
+        sq = (row * row).astype(np.float32)
+        exact = sum((Fraction(float(v)) for v in sq), Fraction(0))
+        assert S == float(exact)
+        perm = row[rng.permutation(row.size)]
+        assert o.sum_squares(perm[None, :])[0] == S
+    # a running fp64 total loses every +1 next to 2^60: the exact sum does not
+    assert o.sum_squares(rows[1][None, :])[0] == 2.0 ** 60 + 256.0
+
+
+def test_rms_scale_closed_form():
+    """r = fp32(1 / sqrt(S / K + eps)) with S exact: rows of c (r = 1/|c| up
+    to eps) and the hand value of a row with two nonzero entries."""
+    for c in (1.0, 0.5, 3.0, 2.0 ** 20):
+        x = np.full((1, 64), c, np.float32)
+        r = o.rms_scale(x, 1e-30)
+        assert r[0] == np.float32(1.0 / c)
+    x = np.zeros((1, 8), np.float32)
+    x[0, :2] = [3.0, 4.0]
+    r = o.rms_scale(x, 1e-6)
+    assert r[0] == np.float32(1.0 / math.sqrt(25.0 / 8 + float(np.float32(1e-6))))
 
 
 def test_rmsnorm_quant_act_hand_example_and_unit_rms():
     x = np.zeros((1, 8), np.float32)
     x[0, :2] = [3.0, 4.0]                     # S = 25, mean 25/8
-    xq, sx = o.rmsnorm_quant_act(x, None, 1e-6, 1e-5, 8)
+    xq, sx = o.rmsnorm_quant_act(x, None, 1e-6, 1e-5)
     r = np.float32(1.0 / math.sqrt(25.0 / 8 + float(np.float32(1e-6))))
     z = (x * r).astype(np.float32)
     xq2, sx2 = o.quant_act(z)
@@ -494,7 +540,7 @@ def test_rmsnorm_quant_act_hand_example_and_unit_rms():
     assert xq[0, 1] == 127 and xq[0, 0] == round(127 * 3 / 4)
     rng = np.random.default_rng(2)
     x = rng.standard_normal((4, 512)).astype(np.float32)
-    r = o.rms_scale(x, 1e-12, 8)
+    r = o.rms_scale(x, 1e-12)
     z = x * r[:, None]
     assert np.allclose(np.mean(z.astype(np.float64) ** 2, axis=1), 1.0, rtol=1e-5)
 
@@ -506,6 +552,6 @@ def test_rmsnorm_quant_act_power_of_two_invariance():
     x = rng.standard_normal((6, 256)).astype(np.float32)
     g = (1 + 0.1 * rng.standard_normal(256)).astype(np.float32)
     for gain in (None, g):
-        a = o.rmsnorm_quant_act(x, gain, float(np.float32(1e-5)), 1e-5, 8)
-        b = o.rmsnorm_quant_act(2 * x, gain, 4 * float(np.float32(1e-5)), 1e-5, 8)
+        a = o.rmsnorm_quant_act(x, gain, float(np.float32(1e-5)), 1e-5)
+        b = o.rmsnorm_quant_act(2 * x, gain, 4 * float(np.float32(1e-5)), 1e-5)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
