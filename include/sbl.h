@@ -146,6 +146,27 @@ sbl_status sbl_quant_mask_weight(const void* w, sbl_dtype wdt, int64_t O, int64_
                                  hipStream_t stream);
 
 /*
+ * sbl_quant_mask_weight without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Arguments, validation, kernels and
+ * results are those of sbl_quant_mask_weight; the workspace is a fixed
+ * 64 KiB array in device memory that the library holds on every GPU it runs
+ * on until the process ends (the call needs 40 KiB for any shape, so no
+ * size is refused for want of scratch; SBL_ERR_WORKSPACE would report it).
+ * The call allocates and frees nothing. Its first call on a device looks up
+ * that device's copy of the array (SBL_ERR_HIP if the lookup fails).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (on different streams, or from several host threads onto
+ * streams that run concurrently) race and give undefined results; calls
+ * ordered on one stream are safe. The array's contents need no clearing:
+ * every byte the kernels read there was written earlier in the same call.
+ */
+sbl_status sbl_quant_mask_weight_noalloc(const void* w, sbl_dtype wdt, int64_t O, int64_t K,
+                                         int N, int M, float eps_w, int8_t* w_eff,
+                                         uint8_t* mask, void* packed, float* gamma_sw,
+                                         float* sw_rows, hipStream_t stream);
+
+/*
  * One weight tensor of sbl_quant_mask_weight_batch. Every pointer is a
  * device pointer with the meaning, layout and optionality of the argument of
  * the same name of sbl_quant_mask_weight; O and K likewise.

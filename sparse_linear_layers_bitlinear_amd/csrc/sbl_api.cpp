@@ -99,6 +99,22 @@ LinearWs linear_ws_layout(int64_t T, int64_t O, int64_t K, int N, int M, bool pr
 
 }  // namespace
 
+namespace sbl {
+sbl_status check_quant_mask_weight(const void* w, int wdt, int64_t O, int64_t K, int N, int M,
+                                   float eps_w, const void* w_eff, const void* mask,
+                                   const void* packed, const void* gamma_sw, const void* sw_rows) {
+  if (!dtype_ok(wdt)) return SBL_ERR_DTYPE;
+  sbl_status st = check_wshape(O, K, N, M);
+  if (st != SBL_OK) return st;
+  if (O < 1 || O * K >= (int64_t(1) << 31)) return SBL_ERR_SHAPE;
+  if (!eps_ok(eps_w)) return SBL_ERR_VALUE;
+  if (!w || !gamma_sw) return SBL_ERR_NULL;
+  for (const void* p : {w, w_eff, mask, packed, gamma_sw, sw_rows})
+    if (p && !aligned16(p)) return SBL_ERR_ALIGN;
+  return SBL_OK;
+}
+}  // namespace sbl
+
 extern "C" {
 
 const char* sbl_status_string(int s) {
@@ -158,17 +174,12 @@ sbl_status sbl_quant_mask_weight(const void* w, sbl_dtype wdt, int64_t O, int64_
                                  float eps_w, int8_t* w_eff, uint8_t* mask, void* packed,
                                  float* gamma_sw, float* sw_rows, void* ws, size_t ws_bytes,
                                  hipStream_t stream) {
-  if (!dtype_ok(wdt)) return SBL_ERR_DTYPE;
-  sbl_status st = check_wshape(O, K, N, M);
+  sbl_status st = sbl::check_quant_mask_weight(w, wdt, O, K, N, M, eps_w, w_eff, mask, packed,
+                                               gamma_sw, sw_rows);
   if (st != SBL_OK) return st;
-  if (O < 1 || O * K >= (int64_t(1) << 31)) return SBL_ERR_SHAPE;
-  if (!eps_ok(eps_w)) return SBL_ERR_VALUE;
-  if (!w || !gamma_sw) return SBL_ERR_NULL;
   if (!ws) return SBL_ERR_WORKSPACE;
   if (ws_bytes < prep_workspace_bytes()) return SBL_ERR_WORKSPACE;
-  for (const void* p : {w, (const void*)w_eff, (const void*)mask, (const void*)packed,
-                        (const void*)gamma_sw, (const void*)sw_rows, (const void*)ws})
-    if (p && !aligned16(p)) return SBL_ERR_ALIGN;
+  if (!aligned16(ws)) return SBL_ERR_ALIGN;
   const PrepTensor t{w, O, K, w_eff, mask, packed, gamma_sw, sw_rows};
   return hip_status(launch_quant_mask_weight(&t, 1, wdt == SBL_BF16, N, M, eps_w, ws, stream),
                     "quant_mask_weight");

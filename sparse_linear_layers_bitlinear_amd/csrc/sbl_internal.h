@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "sbl.h"
 #include <stddef.h>
 
 namespace sbl {
@@ -62,6 +64,12 @@ struct DeviceInfo {
   int cus = 256;
 };
 const DeviceInfo& device_info();  // cached per device
+
+// Host validation of sbl_quant_mask_weight's arguments apart from the
+// workspace.
+sbl_status check_quant_mask_weight(const void* w, int wdt, int64_t O, int64_t K, int N, int M,
+                                   float eps_w, const void* w_eff, const void* mask,
+                                   const void* packed, const void* gamma_sw, const void* sw_rows);
 
 // ---- launchers (return hipGetLastError() of the launch) -------------------
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t T, int64_t K, int64_t ldx,

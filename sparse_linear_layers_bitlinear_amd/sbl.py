@@ -58,6 +58,7 @@ def _load():
         "sbl_quant_mask_weight": ([P, I, I64, I64, I, I, F, P, P, P, P, P, P, S, P], I),
         "sbl_quant_mask_weight_batch_workspace": ([I, ctypes.POINTER(S)], I),
         "sbl_quant_mask_weight_batch": ([ctypes.POINTER(WeightPrep), I, I, I, I, F, P, S, P], I),
+        "sbl_quant_mask_weight_noalloc": ([P, I, I64, I64, I, I, F, P, P, P, P, P, P], I),
         "sbl_packed_bytes": ([I64, I64, I, I, ctypes.POINTER(S)], I),
         "sbl_pack": ([P, P, I64, I64, I, I, P, P], I),
         "sbl_unpack": ([P, I64, I64, I, I, P, P, P], I),
@@ -167,6 +168,29 @@ def sbl_quant_mask_weight(w: torch.Tensor, N: int, M: int, eps_w: float = 1e-5,
         _ptr(w), _dt(w.dtype), O, K, N, M, eps_w, _ptr(out["w_eff"]), _ptr(out["mask"]),
         _ptr(packed), _ptr(out["gamma_sw"]), _ptr(sw_rows), _ptr(ws), ws.numel(),
         _stream(dev)))
+    return out
+
+
+def sbl_quant_mask_weight_noalloc(w: torch.Tensor, N: int, M: int, eps_w: float = 1e-5,
+                                  packed=None, want_packed=True, want_w_eff=False,
+                                  want_mask=False, want_sw_rows=False, sw_rows=None):
+    """As sbl_quant_mask_weight, with the library's fixed device scratch array
+    as the workspace (the call itself allocates nothing)."""
+    assert w.dim() == 2 and w.is_contiguous()
+    O, K = w.shape
+    dev = w.device
+    out = {"gamma_sw": torch.empty(2, dtype=torch.float32, device=dev)}
+    if packed is None and want_packed:
+        packed = torch.empty(sbl_packed_bytes(O, K, N, M), dtype=torch.uint8, device=dev)
+    out["packed"] = packed
+    out["w_eff"] = torch.empty((O, K), dtype=torch.int8, device=dev) if want_w_eff else None
+    out["mask"] = torch.empty((O, K), dtype=torch.uint8, device=dev) if want_mask else None
+    if sw_rows is None and want_sw_rows:
+        sw_rows = torch.empty(O, dtype=torch.float32, device=dev)
+    out["sw_rows"] = sw_rows
+    _check("sbl_quant_mask_weight_noalloc", _lib.sbl_quant_mask_weight_noalloc(
+        _ptr(w), _dt(w.dtype), O, K, N, M, eps_w, _ptr(out["w_eff"]), _ptr(out["mask"]),
+        _ptr(packed), _ptr(out["gamma_sw"]), _ptr(sw_rows), _stream(dev)))
     return out
 
 

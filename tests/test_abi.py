@@ -134,6 +134,23 @@ def test_gemm_and_linear_validation(S):
     assert n2.value < n.value
 
 
+def test_noalloc_prep_validation(S):
+    """The allocation-free preparation validates like the workspace entry
+    point, before it looks at any device (no GPU needed for these)."""
+    L = S.lib
+    a = lambda wdt=1, O=8, K=64, N=6, M=8, eps=1e-5, w=FAKE, g=FAKE: (
+        w, wdt, O, K, N, M, eps, None, None, None, g, None, None)
+    assert L.sbl_quant_mask_weight_noalloc(*a(wdt=5)) == 4
+    assert L.sbl_quant_mask_weight_noalloc(*a(K=60)) == 2
+    assert L.sbl_quant_mask_weight_noalloc(*a(O=0)) == 2
+    assert L.sbl_quant_mask_weight_noalloc(*a(O=1 << 20, K=1 << 11)) == 2    # O K = 2^31
+    assert L.sbl_quant_mask_weight_noalloc(*a(N=0)) == 3
+    assert L.sbl_quant_mask_weight_noalloc(*a(eps=0.0)) == 8
+    assert L.sbl_quant_mask_weight_noalloc(*a(w=None)) == 1
+    assert L.sbl_quant_mask_weight_noalloc(*a(g=None)) == 1
+    assert L.sbl_quant_mask_weight_noalloc(*a(w=MIS)) == 5
+
+
 def test_pack_validation(S):
     L = S.lib
     assert L.sbl_pack(FAKE, FAKE, 4, 12, 6, 8, FAKE, None) == 2
