@@ -344,24 +344,38 @@ def capture(fn):
 FLUSH_BYTES = 1 << 30     # > the 256 MB last-level cache (MALL) and the L2s
 
 
+class CacheFlush:
+    """Evicts every cache level by reading 1 GiB (a sum over a buffer written
+    once at set-up). A read leaves only clean lines behind: a 1 GiB write
+    would leave the last-level cache full of dirty lines whose write-back
+    lands in the next kernel's time (measured: +57 us on the 3B step's first
+    kernel), which is the flush's cost, not the kernel's."""
+
+    def __init__(self):
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+
+    def __call__(self):
+        self.sink = self.buf.sum()
+
+
 def flush_buffer():
-    return torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    return CacheFlush()
 
 
 def time_steps(step, steps, warmup, eager):
     """Device ms per step: HIP events on the launch stream around each step;
-    before each step (outside the events) a 1 GiB write evicts every cache
+    before each step (outside the events) a 1 GiB read evicts every cache
     level, so each step reads its inputs and weights from HBM."""
     run = step.run if eager else capture(step.run).replay
     flush = flush_buffer()
     for _ in range(warmup):
-        flush.fill_(1.0)
+        flush()
         run()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     for a, b in evs:
-        flush.fill_(1.0)
+        flush()
         a.record()
         run()
         b.record()
@@ -374,9 +388,8 @@ def per_call_times(step, reps):
     library's stream around graph replays of that call alone: for each name, a
     graph of all of the step's launches of that name in step order (decode:
     one launch per layer, distinct weights), repeated so that a replay holds
-    at least 8 launches. Where the step streams weights larger than the
-    last-level cache, a 1 GiB write precedes every replay (outside the events)
-    so that the weights come from HBM, as they do inside the step."""
+    at least 8 launches. A 1 GiB read precedes every replay (outside the
+    events), so the replay's first launch finds no input in any cache."""
     calls = step.calls()
     names = list(dict.fromkeys(n for n, _ in calls))
     flush = flush_buffer() if step.cold_weights else None
@@ -391,7 +404,7 @@ def per_call_times(step, reps):
         ms = []
         for _ in range(reps):
             if flush is not None:
-                flush.fill_(1.0)
+                flush()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             graph.replay()
