@@ -12,8 +12,12 @@
 // workgroup the instructions a wavefront executes once (not in a loop) are
 // what the latency is made of. So every phase is either a handful of
 // instructions or a short loop:
-//  - the 16-row tiles of W are split evenly over at most one workgroup of 8
-//    wavefronts per compute unit; a workgroup copies all of its packed W
+//  - the tokens are split into groups and the 16-row tiles of W evenly into
+//    slices, one workgroup of 8 wavefronts per (group, slice) and at most one
+//    per compute unit; each workgroup quantizes only its group's rows (that
+//    VALU work grows with tokens x K, so long rows take small groups when
+//    there are few tiles) and the groups of one slice share its W through
+//    their XCD's L2. A workgroup copies all of its packed W
 //    straight into LDS with 16-byte LDS-DMA loads (one instruction moves 1 KB:
 //    16 rows x two K-steps), issued at the start so the whole weight stream is
 //    in flight at once;
@@ -52,14 +56,15 @@ struct DecodeArgs {
   const float* sw;        // weight scale(s), element o at o * sw_inc
   int sw_inc;
   int T, O, K, R;         // R: most tiles of one workgroup
-  int tq, trem;           // tiles per workgroup: tq, one more for the first trem
+  int tq, trem;           // tiles per slice: tq, one more for the first trem
+  int S, tg;              // row-tile slices; tokens per workgroup (token group)
   int lg;                 // log2 of the threads per token (dec_group)
   int xw;                 // wavefronts that quantize x (4 or 8; the rest copy W)
   void* y;                // [T, O] bf16 or fp32
   int32_t* acc;           // optional [T, O] int32
 };
 
-// LDS: W [R][np][1 KB] | xs [T][xpitch] int8 | sxs [16] f32 | pmax [16] u32 (per half-wave) |
+// LDS: W [R][np][1 KB] | xs [tg][xpitch] int8 | sxs [16] f32 | pmax [16] u32 (per half-wave) |
 //      red [R][64][4] i32     (np = pairs of K-steps)
 __host__ __device__ inline int dec_np(int K) { return ((K + 127) / 128 + 1) / 2; }
 __host__ __device__ inline int dec_xpitch(int K) { return 128 * ((K + 127) / 128) + 16; }
@@ -103,23 +108,28 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
 template <bool SP, int XM, bool YBF16, int NV>
 __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int T = a.T, O = a.O, K = a.K;
+  const int O = a.O, K = a.K;
   const int ns = (K + 127) >> 7, np = (ns + 1) >> 1;   // K-steps, pairs of K-steps
   const int XP = dec_xpitch(K);
   uint8_t* const wsm = smem;
   int8_t* const xs = (int8_t*)(smem + dec_off_x(K, a.R));
-  float* const sxs = (float*)(smem + dec_off_sx(T, K, a.R));
+  float* const sxs = (float*)(smem + dec_off_sx(a.tg, K, a.R));
   uint32_t* const pmax = (uint32_t*)(sxs + 16);
   int* const red = (int*)(pmax + 16);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, r16 = lane & 15;
-  // this workgroup's tiles [tb, tb + ntb) of the (O + 15) / 16 (even split,
-  // quotient and remainder from the host: no division here)
+  // workgroup b = (token group) * S + (slice): the slice's 16-row tiles
+  // [tb, tb + ntb) of the (O + 15) / 16 (even split, quotient and remainder
+  // from the host) for the group's tokens [t0, t0 + T). With S a multiple of
+  // 8 the token groups of one slice run on one XCD and share its W in L2.
   const int bx = blockIdx.x;
-  const int tb = bx * a.tq + min(bx, a.trem);
-  const int ntb = a.tq + (bx < a.trem ? 1 : 0);
+  const int grp = bx / a.S, slice = bx - grp * a.S;
+  const int t0 = grp * a.tg;
+  const int T = min(a.tg, a.T - t0);                     // this workgroup's tokens
+  const int tb = slice * a.tq + min(slice, a.trem);
+  const int ntb = a.tq + (slice < a.trem ? 1 : 0);
   // the weight scales of this thread's first output item (loaded now, so the
   // epilogue does not wait for them)
   float swp[4];
@@ -144,7 +154,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   uint4 v[NV];
   if constexpr (XM != 0) {
     if (xwave) {
-      const uint4* const row = (const uint4*)a.x + (int64_t)tt * nvr;
+      const uint4* const row = (const uint4*)a.x + (int64_t)(t0 + tt) * nvr;
 #pragma unroll
       for (int i = 0; i < NV; ++i)
         if (i < nvt) v[i] = row[min(col + G * i, nvr - 1)];   // clamped duplicates are harmless
@@ -174,9 +184,9 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
     for (int j = wave; j < T * nq; j += kDecWaves) {
       const int t = j / nq, q = j - t * nq;
       if (1024 * q + 16 * lane < K)
-        dma16(xq + (int64_t)t * K + 1024 * q + 16 * lane, (uint8_t*)xs + t * XP + 1024 * q);
+        dma16(xq + (int64_t)(t0 + t) * K + 1024 * q + 16 * lane, (uint8_t*)xs + t * XP + 1024 * q);
     }
-    if (tid < T) sxs[tid] = a.sx[tid];
+    if (tid < T) sxs[tid] = a.sx[t0 + tid];
   } else {
     // per-token max over the token's G threads: within each wave by DPP (lane
     // 31 holds the max of lanes 0-31, lane 63 that of 32-63 or of the whole
@@ -275,26 +285,57 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
     const int t = i & 15, o = (tb + (i >> 6)) * 16 + 4 * ((i >> 4) & 3);
     if (i != tid) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) swp[r] = a.sw[(int64_t)min(o + r, O - 1) * a.sw_inc];
+      for (int k = 0; k < 4; ++k) swp[k] = a.sw[(int64_t)min(o + k, O - 1) * a.sw_inc];
     }
     if (t < T && o < O)
-      store_tile_sw<YBF16>(a.y, a.acc, *(const v4i*)(red + 4 * i), t, o, O, sxs[t], swp);
+      store_tile_sw<YBF16>(a.y, a.acc, *(const v4i*)(red + 4 * i), t0 + t, o, O, sxs[t], swp);
   }
 }
 
-// workgroups: at most one per compute unit and one per tile
-int dec_blocks(int64_t O) {
-  const char* ev = std::getenv("SBL_DECODE_BLOCKS");   // tuning override
+// Launch plan: the T tokens are split into groups of tg (the last may be
+// shorter) and the 16-row tiles into S slices; one workgroup per (group,
+// slice), at most one per compute unit. Every workgroup quantizes its
+// group's rows itself (a whole row's maximum sets a token's scale), at about
+// four VALU instructions per element; groups keep tg * K to kDecXElems when
+// the extra groups' copies of W still leave every compute unit with at most
+// about two tiles per group (the groups of a slice read W from the same
+// XCD's L2, so it comes from HBM once).
+constexpr int kDecXElems = 16384;
+struct DecPlan {
+  int tg, ng, S, R, tq, trem, blocks;
+};
+DecPlan dec_plan(int64_t T, int64_t O, int64_t K, int xmode) {
+  DecPlan p{};
   const int64_t ntiles = cdiv(O, 16);
-  int64_t nb = ev ? std::atoi(ev) : 0;
-  if (nb < 1) nb = device_info().cus;
-  return (int)(nb < ntiles ? nb : ntiles);
+  const int cus = device_info().cus;
+  int64_t tg = T;
+  const char* et = std::getenv("SBL_DECODE_TG");      // tuning override
+  if (et && std::atoi(et) >= 1) tg = std::min<int64_t>(T, std::atoi(et));
+  else if (xmode != 0)
+    while (tg > 1 && tg * K > kDecXElems && cdiv(T, (tg + 1) / 2) * ntiles <= 2 * cus)
+      tg = (tg + 1) / 2;
+  p.tg = (int)tg;
+  p.ng = (int)cdiv(T, tg);
+  const char* ev = std::getenv("SBL_DECODE_BLOCKS");  // tuning override: slices
+  int64_t S = ev ? std::atoi(ev) : 0;
+  if (S < 1) {
+    S = cus / p.ng;
+    if (S >= 8) S = S / 8 * 8;                        // token groups of a slice on one XCD
+    if (S < 1) S = 1;
+  }
+  if (S > ntiles) S = ntiles;
+  p.S = (int)S;
+  p.R = (int)cdiv(ntiles, S);
+  p.tq = (int)(ntiles / S);
+  p.trem = (int)(ntiles % S);
+  p.blocks = p.S * p.ng;
+  return p;
 }
 
 template <bool SP, int XM, bool YBF16, int NV>
 hipError_t run_decode(const DecodeArgs& a, int blocks, hipStream_t s) {
   auto kern = k_decode<SP, XM, YBF16, NV>;
-  const int lds = dec_lds(a.T, a.K, a.R);
+  const int lds = dec_lds(a.tg, a.K, a.R);
   if (lds > 65536) {
     static int set = 0;   // the attribute is per kernel; raised as needed
     if (lds > set) {
@@ -327,27 +368,26 @@ bool decode_fits(int64_t T, int64_t O, int64_t K, int N, int M, int xmode) {
   if (T < 1 || T > 16 || O < 1 || K < 1 || K % 16 != 0) return false;
   if (O * row_pitch(K, N, M) >= (int64_t(1) << 31)) return false;
   // activation vectors per thread
+  const DecPlan p = dec_plan(T, O, K, xmode);
   const int64_t nvr = K / (xmode == 0 ? 16 : xmode == 1 ? 8 : 4);
-  if (xmode != 0 && cdiv(nvr, dec_group((int)T)) > kDecMaxVec) return false;
-  const int64_t R = cdiv(cdiv(O, 16), dec_blocks(O));
-  return dec_lds((int)T, (int)K, (int)R) <= kDecMaxLds;
+  if (xmode != 0 && cdiv(nvr, dec_group(p.tg)) > kDecMaxVec) return false;
+  return dec_lds(p.tg, (int)K, p.R) <= kDecMaxLds;
 }
 
 hipError_t launch_decode(const void* x, int xmode, const float* sx, float eps, const void* packed,
                          const float* sw, int64_t sw_inc, int64_t T, int64_t O, int64_t K, int N,
                          int M, void* y, bool y_bf16, int32_t* acc, hipStream_t s) {
   if (!decode_fits(T, O, K, N, M, xmode)) return hipErrorInvalidValue;
-  const int blocks = dec_blocks(O);
-  const int R = (int)cdiv(cdiv(O, 16), blocks);
-  const int ntiles = (int)cdiv(O, 16);
+  const DecPlan p = dec_plan(T, O, K, xmode);
+  const int blocks = p.blocks;
   // four quantizing wavefronts when a token gets at least half of one of them
-  // (T <= 8) and its vectors fit their registers; else all eight
+  // (tg <= 8) and its vectors fit their registers; else all eight
   const int64_t nvr = K / (xmode == 1 ? 8 : 4);
-  const int xw = (xmode != 0 && T <= 8 && cdiv(nvr, dec_group((int)T, 256)) <= kDecMaxVec) ? 4 : 8;
+  const int xw = (xmode != 0 && p.tg <= 8 && cdiv(nvr, dec_group(p.tg, 256)) <= kDecMaxVec) ? 4 : 8;
   int lg = 0;                                  // log2 of the threads per token
-  while ((1 << lg) < dec_group((int)T, 64 * xw)) ++lg;
+  while ((1 << lg) < dec_group(p.tg, 64 * xw)) ++lg;
   const DecodeArgs a{x, sx, eps, (const uint8_t*)packed, (int)row_pitch(K, N, M), sw,
-                     (int)sw_inc, (int)T, (int)O, (int)K, R, ntiles / blocks, ntiles % blocks, lg,
+                     (int)sw_inc, (int)T, (int)O, (int)K, p.R, p.tq, p.trem, p.S, p.tg, lg,
                      xw, y, acc};
   const int nv = xmode == 0 ? 0 : (int)cdiv(nvr, (int64_t)1 << lg);   // vectors per thread
   if (index_form(N, M))

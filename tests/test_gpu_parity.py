@@ -688,6 +688,32 @@ def test_decode_tiles_per_workgroup(S, R, monkeypatch):
         assert_bf16_exact(host(yb), ref["acc"], ref["sx"], ref["sw"])
 
 
+@pytest.mark.parametrize("tg", [1, 2, 3, 5])
+def test_decode_token_groups(S, tg, monkeypatch):
+    """Token groups of the decode GEMV forced (the last group ragged), with
+    forced slice counts too: every group quantizes its own rows and stores its
+    own outputs."""
+    monkeypatch.setenv("SBL_DECODE_TG", str(tg))
+    for (T, O, K, N, M, slices) in [(16, 333, 1024, 6, 8, 0), (7, 1000, 2560, 2, 4, 0),
+                                    (8, 130, 6912, 2, 4, 3), (5, 64, 512, 4, 8, 0)]:
+        if slices:
+            monkeypatch.setenv("SBL_DECODE_BLOCKS", str(slices))
+        else:
+            monkeypatch.delenv("SBL_DECODE_BLOCKS", raising=False)
+        log_case("decode token groups", tg, T, O, K, N, M, slices)
+        W, x = make_linear_inputs(T, O, K, seed=tg * 17 + O)
+        r = S.sbl_quant_mask_weight(to_dev(W), N, M, want_sw_rows=True)
+        ref = o.linear_fwd(bf16_round(x), W, N, M)
+        yb = S.sbl_linear_fwd(bf16_tensor(x), N, M, prepacked=r["packed"], sw=r["sw_rows"], O=O,
+                              out_dtype=torch.bfloat16)
+        assert_bf16_exact(host(yb), ref["acc"], ref["sx"], ref["sw"])
+        xq, sx = S.sbl_quant_act(bf16_tensor(x))
+        y2, acc = S.sbl_gemm(xq, sx, r["packed"], r["sw_rows"], O, N, M,
+                             out_dtype=torch.float32, want_acc=True)
+        assert np.array_equal(host(acc), ref["acc"])
+        assert_f32_close(host(y2), ref["y"])
+
+
 @pytest.mark.parametrize("T", [1, 4, 8])
 def test_decode_bench_launches(S, T):
     """The calls the decode benchmark times, as it makes them: per projection
