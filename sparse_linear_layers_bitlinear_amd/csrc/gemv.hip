@@ -103,6 +103,82 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* lds) {
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
+// Workgroup barrier that waits only for the wave's LDS operations. A
+// workgroup-scope fence (so __syncthreads()) also waits for every outstanding
+// global load -- here the weight copies still in flight into LDS. The
+// wavefront-scope fences keep the compiler from moving memory operations
+// across the barrier and emit no wait; the explicit lgkmcnt(0) completes the
+// wave's LDS writes before it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);                   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The MMA phase of one wavefront when the workgroup has two or more tiles:
+// K-steps s = wave + 8 (c0 + i), i < KU, of every tile, for chunks c0 = 0,
+// KU, ... of its nsw K-steps. A K-step's activation fragments are the same
+// for every tile, so they are read from LDS once per chunk, and each tile's W
+// fragments are read while the tile before it is computed. Reads past the
+// wave's last K-step repeat it (in bounds; never computed). The int32 sums go
+// to the tile's LDS accumulator (red + 256 r; this lane's 4 at rl) by ds_add.
+template <bool SP, int KU>
+__device__ __forceinline__ void mma_tiles(const uint8_t* wsm, const int8_t* xr, int aoff, int wave,
+                                          int nsw, int np, int ntb, int g, int* rl) {
+  for (int c0 = 0; c0 < nsw; c0 += KU) {
+    const int nc = min(KU, nsw - c0);
+    int woff[KU];
+    v4i xa[KU], xb[KU];
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+      const int s = wave + kDecWaves * (c0 + min(i, nc - 1));
+      woff[i] = (s >> 1) * 1024 + 512 * (s & 1) + aoff;
+      const int kb = 128 * s;
+      xa[i] = *(const v4i*)(xr + kb + (SP ? 16 : 32) * g);
+      xb[i] = *(const v4i*)(xr + kb + (SP ? 64 + 16 * g : 32 * g + 16));
+    }
+    uint2 wa[KU], wb[KU];
+    // tile r from cur (read earlier) while tile r + 1 is read into nxt; two
+    // tiles per trip, so the buffers swap roles without register copies
+    auto tile = [&](int r, const uint2 (&cur)[KU], uint2 (&nxt)[KU]) {
+      if (r + 1 < ntb) {
+        const uint8_t* const wr = wsm + (r + 1) * np * 1024;
+#pragma unroll
+        for (int i = 0; i < KU; ++i) nxt[i] = *(const uint2*)(wr + woff[i]);
+      }
+      v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < KU; ++i) {
+        if (i < nc) {                                    // (uniform)
+          v4i& acc = (i & 1) ? acc1 : acc0;
+          if constexpr (SP)
+            acc = __builtin_amdgcn_smfmac_i32_16x16x128_i8(
+                expand4(cur[i].x),
+                v8i{xa[i][0], xa[i][1], xa[i][2], xa[i][3], xb[i][0], xb[i][1], xb[i][2], xb[i][3]},
+                acc, (int)cur[i].y, 0, 0);
+          else {
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand4(cur[i].x), xa[i], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand4(cur[i].y), xb[i], acc, 0, 0, 0);
+          }
+        }
+      }
+      acc0 += acc1;
+      int* const rp = rl + r * 256;
+      atomicAdd(rp + 0, acc0[0]);
+      atomicAdd(rp + 1, acc0[1]);
+      atomicAdd(rp + 2, acc0[2]);
+      atomicAdd(rp + 3, acc0[3]);
+    };
+#pragma unroll
+    for (int i = 0; i < KU; ++i) wa[i] = *(const uint2*)(wsm + woff[i]);
+    for (int r = 0; r < ntb; r += 2) {
+      tile(r, wa, wb);
+      if (r + 1 < ntb) tile(r + 1, wb, wa);
+    }
+  }
+}
+
 // XM: 0 = xq given, 1 = bf16 x, 2 = fp32 x. NV: most activation vectors of
 // one thread (the loads and codes are unrolled NV times; few is faster).
 template <bool SP, int XM, bool YBF16, int NV>
@@ -192,9 +268,25 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
     // 31 holds the max of lanes 0-31, lane 63 that of 32-63 or of the whole
     // wave), then over the token's waves through LDS
     uint32_t m = 0;
+    if constexpr (BF) {
+      // bf16 pairs with the signs cleared, as packed u16 (magnitudes order as
+      // integers): packed maxima, then the larger half, as an fp32 pattern
+      typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+      auto mag = [](uint32_t w) { return __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu); };
+      u16x2 pm = {0, 0};
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (xwave && i < nvt) m = max(m, absmax_vec<BF>(v[i]));
+      for (int i = 0; i < NV; ++i)
+        if (xwave && i < nvt)
+          pm = __builtin_elementwise_max(
+              pm, __builtin_elementwise_max(
+                      __builtin_elementwise_max(mag(v[i].x), mag(v[i].y)),
+                      __builtin_elementwise_max(mag(v[i].z), mag(v[i].w))));
+      m = (uint32_t)max(pm.x, pm.y) << 16;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (xwave && i < nvt) m = max(m, absmax_vec<BF>(v[i]));
+    }
     m = row_max_dpp(m);
     m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x142, 0xA, 0xF, false));
     if (G >= 64) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x143, 0xC, 0xF, false));
@@ -207,19 +299,23 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
         pmax[2 * wave] = G >= 64 ? m_hi : m_lo;
         pmax[2 * wave + 1] = m_hi;
       }
-      __syncthreads();
-      // all 16 partial maxima at once (constant indices: no dependent reads)
-      uint32_t pm[16];
+      lds_barrier();
+      if (xwave) {
+        // all 16 partial maxima at once (constant indices: no dependent reads;
+        // only in the quantizing waves: a compiled LDS read after the W
+        // copies waits for all of them)
+        uint32_t pm[16];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint4 q4 = *(const uint4*)(pmax + 4 * k);
-        pm[4 * k] = q4.x; pm[4 * k + 1] = q4.y; pm[4 * k + 2] = q4.z; pm[4 * k + 3] = q4.w;
+        for (int k = 0; k < 4; ++k) {
+          const uint4 q4 = *(const uint4*)(pmax + 4 * k);
+          pm[4 * k] = q4.x; pm[4 * k + 1] = q4.y; pm[4 * k + 2] = q4.z; pm[4 * k + 3] = q4.w;
+        }
+        mt = 0;
+        const int w0 = tt << (lg - 6), w1 = (tt + 1) << (lg - 6);   // the token's waves
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w)
+          if (w >= w0 && w < w1) mt = max(mt, pm[2 * w]);
       }
-      mt = 0;
-      const int w0 = tt << (lg - 6), w1 = (tt + 1) << (lg - 6);   // the token's waves
-#pragma unroll
-      for (int w = 0; w < kDecWaves; ++w)
-        if (w >= w0 && w < w1) mt = max(mt, pm[2 * w]);
     }
     const ActScale sc = act_scale(mt, a.eps);
     if (col == 0 && tok && xwave) sxs[tt] = sc.s;
@@ -261,21 +357,31 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(expand4(w.y), b1, acc, 0, 0, 0);
     }
   };
-  for (int r = 0; r < ntb; ++r) {
-    v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-    int s = wave;
-    for (; s + kDecWaves < ns; s += 2 * kDecWaves) {
-      unit(r, s, acc0);
-      unit(r, s + kDecWaves, acc1);
-    }
-    if (s < ns) unit(r, s, acc0);
-    acc0 += acc1;
-    if (wave < ns) {
-      int* const rp = red + r * 256 + lane * 4;
-      atomicAdd(rp + 0, acc0[0]);
-      atomicAdd(rp + 1, acc0[1]);
-      atomicAdd(rp + 2, acc0[2]);
-      atomicAdd(rp + 3, acc0[3]);
+  // the wave's K-steps (uniform); several tiles with at most 4 K-steps per
+  // wave (K <= 4096): activation fragments read once, W one tile ahead (with
+  // more K-steps the reads issued up front cost more than the reuse saves)
+  const int nsw = wave < ns ? (ns - 1 - wave) / kDecWaves + 1 : 0;
+  if (ntb >= 2 && nsw <= 4) {
+    int* const rl = red + lane * 4;
+    if (nsw <= 2) mma_tiles<SP, 2>(wsm, xr, aoff, wave, nsw, np, ntb, g, rl);
+    else mma_tiles<SP, 4>(wsm, xr, aoff, wave, nsw, np, ntb, g, rl);
+  } else {
+    for (int r = 0; r < ntb; ++r) {
+      v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+      int s = wave;
+      for (; s + kDecWaves < ns; s += 2 * kDecWaves) {
+        unit(r, s, acc0);
+        unit(r, s + kDecWaves, acc1);
+      }
+      if (s < ns) unit(r, s, acc0);
+      acc0 += acc1;
+      if (wave < ns) {
+        int* const rp = red + r * 256 + lane * 4;
+        atomicAdd(rp + 0, acc0[0]);
+        atomicAdd(rp + 1, acc0[1]);
+        atomicAdd(rp + 2, acc0[2]);
+        atomicAdd(rp + 3, acc0[3]);
+      }
     }
   }
   __syncthreads();
@@ -294,26 +400,21 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
 
 // Launch plan: the T tokens are split into groups of tg (the last may be
 // shorter) and the 16-row tiles into S slices; one workgroup per (group,
-// slice), at most one per compute unit. Every workgroup quantizes its
-// group's rows itself (a whole row's maximum sets a token's scale), at about
-// four VALU instructions per element; groups keep tg * K to kDecXElems when
-// the extra groups' copies of W still leave every compute unit with at most
-// about two tiles per group (the groups of a slice read W from the same
-// XCD's L2, so it comes from HBM once).
-constexpr int kDecXElems = 16384;
+// slice), at most one per compute unit, the groups of a slice on one XCD so
+// that W comes from HBM once and from that XCD's L2 for the others. Every
+// workgroup quantizes its group's rows itself (a whole row's maximum sets a
+// token's scale), work that grows with tg * K, while more groups leave fewer
+// slices, so more tiles -- R * np KB of W to copy and multiply -- per
+// workgroup. The plan takes the tg among T, T/2, T/4, ... (rounded up) with
+// the least tg * K + kDecElemsPerKB * R * np whose LDS and per-thread
+// activation vectors fit: measured on 2560- and 6912-wide rows, about 600
+// activation elements per workgroup cost as much as one more KB of W.
+constexpr int kDecElemsPerKB = 600;
 struct DecPlan {
   int tg, ng, S, R, tq, trem, blocks;
 };
-DecPlan dec_plan(int64_t T, int64_t O, int64_t K, int xmode) {
+DecPlan dec_plan_tg(int64_t T, int64_t ntiles, int cus, int64_t tg) {
   DecPlan p{};
-  const int64_t ntiles = cdiv(O, 16);
-  const int cus = device_info().cus;
-  int64_t tg = T;
-  const char* et = std::getenv("SBL_DECODE_TG");      // tuning override
-  if (et && std::atoi(et) >= 1) tg = std::min<int64_t>(T, std::atoi(et));
-  else if (xmode != 0)
-    while (tg > 1 && tg * K > kDecXElems && cdiv(T, (tg + 1) / 2) * ntiles <= 2 * cus)
-      tg = (tg + 1) / 2;
   p.tg = (int)tg;
   p.ng = (int)cdiv(T, tg);
   const char* ev = std::getenv("SBL_DECODE_BLOCKS");  // tuning override: slices
@@ -330,6 +431,33 @@ DecPlan dec_plan(int64_t T, int64_t O, int64_t K, int xmode) {
   p.trem = (int)(ntiles % S);
   p.blocks = p.S * p.ng;
   return p;
+}
+bool dec_plan_fits(const DecPlan& p, int64_t K, int xmode) {
+  const int64_t nvr = K / (xmode == 0 ? 16 : xmode == 1 ? 8 : 4);   // vectors per row
+  if (xmode != 0 && cdiv(nvr, dec_group(p.tg)) > kDecMaxVec) return false;
+  return dec_lds(p.tg, (int)K, p.R) <= kDecMaxLds;
+}
+DecPlan dec_plan(int64_t T, int64_t O, int64_t K, int xmode) {
+  const int64_t ntiles = cdiv(O, 16);
+  const int cus = device_info().cus;
+  const char* et = std::getenv("SBL_DECODE_TG");      // tuning override
+  if (et && std::atoi(et) >= 1) return dec_plan_tg(T, ntiles, cus, std::min<int64_t>(T, std::atoi(et)));
+  DecPlan best = dec_plan_tg(T, ntiles, cus, T);
+  if (xmode == 0) return best;                        // (xq given: nothing to quantize)
+  bool have = dec_plan_fits(best, K, xmode);
+  int64_t best_cost = T * K + (int64_t)kDecElemsPerKB * best.R * dec_np((int)K);
+  for (int64_t tg = T; tg > 1;) {
+    tg = (tg + 1) / 2;
+    const DecPlan p = dec_plan_tg(T, ntiles, cus, tg);
+    if (!dec_plan_fits(p, K, xmode)) continue;
+    const int64_t cost = tg * K + (int64_t)kDecElemsPerKB * p.R * dec_np((int)K);
+    if (!have || cost < best_cost) {
+      best = p;
+      best_cost = cost;
+      have = true;
+    }
+  }
+  return best;
 }
 
 template <bool SP, int XM, bool YBF16, int NV>
@@ -367,11 +495,8 @@ hipError_t dispatch_x(int xmode, int nv, const DecodeArgs& a, int blocks, hipStr
 bool decode_fits(int64_t T, int64_t O, int64_t K, int N, int M, int xmode) {
   if (T < 1 || T > 16 || O < 1 || K < 1 || K % 16 != 0) return false;
   if (O * row_pitch(K, N, M) >= (int64_t(1) << 31)) return false;
-  // activation vectors per thread
-  const DecPlan p = dec_plan(T, O, K, xmode);
-  const int64_t nvr = K / (xmode == 0 ? 16 : xmode == 1 ? 8 : 4);
-  if (xmode != 0 && cdiv(nvr, dec_group(p.tg)) > kDecMaxVec) return false;
-  return dec_lds(p.tg, (int)K, p.R) <= kDecMaxLds;
+  if (K > (1 << 20)) return false;                    // (LDS holds far less)
+  return dec_plan_fits(dec_plan(T, O, K, xmode), K, xmode);
 }
 
 hipError_t launch_decode(const void* x, int xmode, const float* sx, float eps, const void* packed,
