@@ -376,19 +376,22 @@ __global__ __launch_bounds__(kThreads, (WMB * WNB > 16) ? 1 : 2) void k_bwd(cons
 // dW with direct global-to-LDS loads. Staging through registers (load, wait,
 // write LDS) costs about as much as the products themselves here; the LDS DMA
 // (global_load_lds, 16 bytes per lane) lands the operands without the waves'
-// instructions, so the ring can run kDmaStages steps ahead.
-//   Tile 128x128 (2 x 2 waves of 64x64), steps of 32 rows of T.
-//   LDS: kDmaStages slots of {dY tile, x~ tile}, each 32 rows x 256 bytes, no
-//   padding (one DMA instruction fills 4 whole rows); bank conflicts of the
-//   transposed reads are avoided by XOR-swizzling the 16-byte chunks of a
-//   row: chunk c of row r sits at c ^ (2 (r mod 8)).
+// instructions, so the ring can run several steps ahead.
+//   Tile BM x 128 (2 x 2 waves of (BM / 2) x 64), steps of 32 rows of T:
+//   BM = 128 with four ring stages, or BM = 256 with three (each wave's
+//   transposed fragment reads then feed twice the products: the kernel is
+//   bound by LDS traffic per product, not by HBM).
+//   LDS: stages of {BM / 128 dY sub-tiles, x~ tile}, each 32 rows x 256
+//   bytes, no padding (one DMA instruction fills 4 whole rows); bank conflicts
+//   of the transposed reads are avoided by XOR-swizzling the 16-byte chunks
+//   of a row: chunk c of row r sits at c ^ (2 (r mod 8)).
 //   Rows past the tile edges are loaded from clamped (valid) addresses: they
 //   only reach outputs that are not written. Rows past T in the last step
 //   would reach real outputs, so that step's x~ rows past T are zeroed in
 //   LDS after their loads land.
 // ---------------------------------------------------------------------------
-constexpr int kDmaBR = 32, kDmaStages = 4;
-constexpr int kDmaSlotElems = 2 * kDmaBR * 128;            // dY tile + x~ tile
+constexpr int kDmaBR = 32;
+constexpr int kDmaSub = kDmaBR * 128;                      // one 32 x 128 sub-tile
 
 __device__ __forceinline__ int swz(int r, int c) { return c ^ (2 * (r & 7)); }
 
@@ -397,9 +400,10 @@ __device__ __forceinline__ void dma16(const void* g, uint16_t* lds) {
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// Wait until at most N DMAs of this wave are outstanding (and all its LDS
-// operations are done), then barrier. The empty asm statements keep the
-// compiler from moving memory accesses across.
+// Wait until at most n DMAs of this wave are outstanding (and all its LDS
+// operations are done), then barrier. n is a compile-time constant at every
+// call (the waits are instruction immediates). The empty asm statements keep
+// the compiler from moving memory accesses across.
 template <int N>
 __device__ __forceinline__ void dma_wait_barrier() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
@@ -417,35 +421,50 @@ __device__ __forceinline__ bf16x8 frag_swz(const uint16_t* tile, int col0, int s
   return join(lds_tr(tile + r0 * 128 + 8 * swz(r0, c) + e), lds_tr(tile + r1 * 128 + 8 * swz(r1, c) + e));
 }
 
-// The four ring slots are separate LDS objects, each named at compile time
-// (the loop is unrolled by four): the compiler then knows that a read of one
-// slot does not depend on the DMAs still landing in the others, and does not
-// drain them before every read.
-__shared__ __align__(16) uint16_t dma_slot0[kDmaSlotElems];
-__shared__ __align__(16) uint16_t dma_slot1[kDmaSlotElems];
-__shared__ __align__(16) uint16_t dma_slot2[kDmaSlotElems];
-__shared__ __align__(16) uint16_t dma_slot3[kDmaSlotElems];
-static_assert(kDmaStages == 4, "one named slot per stage");
+// The ring slots are separate LDS objects, each named at compile time (the
+// loop is unrolled by the stage count): the compiler then knows that a read
+// of one slot does not depend on the DMAs still landing in the others, and
+// does not drain them before every read. 128-row tiles: four slots of two
+// sub-tiles; 256-row tiles: three slots of three.
+__shared__ __align__(16) uint16_t dma_slot0[2 * kDmaSub];
+__shared__ __align__(16) uint16_t dma_slot1[2 * kDmaSub];
+__shared__ __align__(16) uint16_t dma_slot2[2 * kDmaSub];
+__shared__ __align__(16) uint16_t dma_slot3[2 * kDmaSub];
+__shared__ __align__(16) uint16_t dma_wslot0[3 * kDmaSub];
+__shared__ __align__(16) uint16_t dma_wslot1[3 * kDmaSub];
+__shared__ __align__(16) uint16_t dma_wslot2[3 * kDmaSub];
 
-template <int I>
+template <int BM, int I>
 __device__ __forceinline__ uint16_t* dma_slot() {
-  if constexpr (I == 0) return dma_slot0;
-  else if constexpr (I == 1) return dma_slot1;
-  else if constexpr (I == 2) return dma_slot2;
-  else return dma_slot3;
+  if constexpr (BM == 256) {
+    if constexpr (I == 0) return dma_wslot0;
+    else if constexpr (I == 1) return dma_wslot1;
+    else return dma_wslot2;
+  } else {
+    if constexpr (I == 0) return dma_slot0;
+    else if constexpr (I == 1) return dma_slot1;
+    else if constexpr (I == 2) return dma_slot2;
+    else return dma_slot3;
+  }
 }
 
+template <int BM>
 __global__ __launch_bounds__(kThreads, 2) void k_bwd_dw_dma(const BwdArgs a) {
+  static_assert(BM == 128 || BM == 256, "tile rows");
+  constexpr int NS = BM == 256 ? 3 : 4;                    // ring stages
+  constexpr int NH = BM / 128;                             // dY sub-tiles per stage
+  constexpr int WM = BM / 2, NI = WM / 16;                 // wave rows, row strips
+  constexpr int D = 2 * NH + 2;                            // DMAs per wave and step
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   int tm, tn;
   tile_of(xcd_tile(blockIdx.x, a.ntm * a.ntn), a.ntm, a.ntn, a.gm, tm, tn);
-  const int m0 = tm * 128, n0 = tn * 128;
+  const int m0 = tm * BM, n0 = tn * 128;
   const int T = a.T, steps = (T + kDmaBR - 1) / kDmaBR;
   const uint16_t* __restrict__ xt = (const uint16_t*)a.b;
 
-  // DMA i of the wave fills rows 4 (2 wave + i) .. + 3 of a tile; lane l
+  // DMA i of the wave fills rows 4 (2 wave + i) .. + 3 of a sub-tile; lane l
   // takes row + l / 16, physical chunk l % 16 (logical chunk swz of it)
   auto issue = [&](uint16_t* slot, int st) {
 #pragma unroll
@@ -453,68 +472,80 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dw_dma(const BwdArgs a) {
       const int r = 4 * (2 * wave + i) + (lane >> 4);
       const int c = swz(r, lane & 15);
       const int t = min(st * kDmaBR + r, T - 1);
-      const int o = min(m0 + 8 * c, a.O - 8), k = min(n0 + 8 * c, a.K - 8);
-      dma16(a.dy + (int64_t)t * a.ldy + o, slot + 4 * (2 * wave + i) * 128);
-      dma16(xt + (int64_t)t * a.ldb + k, slot + kDmaBR * 128 + 4 * (2 * wave + i) * 128);
+      const int k = min(n0 + 8 * c, a.K - 8);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int o = min(m0 + 128 * h + 8 * c, a.O - 8);
+        dma16(a.dy + (int64_t)t * a.ldy + o, slot + h * kDmaSub + 4 * (2 * wave + i) * 128);
+      }
+      dma16(xt + (int64_t)t * a.ldb + k, slot + NH * kDmaSub + 4 * (2 * wave + i) * 128);
     }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[NI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // step st (st % 4 == I): wait for its slot, refill the slot of step st - 1
-  // with step st + 3, compute
+  // step st (st % NS == I): wait for its slot, refill the slot of step st - 1
+  // with step st + NS - 1, compute
   auto body = [&](auto I_, int st) {
     constexpr int I = decltype(I_)::value;
     if (st >= steps) return;
-    // at most the DMAs of the later issued steps (4 per step and wave) may
+    // at most the DMAs of the later issued steps (D per step and wave) may
     // still be outstanding
-    const int later = min(kDmaStages - 2, steps - 1 - st);
-    if (later >= 2) dma_wait_barrier<8>();
-    else if (later == 1) dma_wait_barrier<4>();
+    const int later = min(NS - 2, steps - 1 - st);
+    if (later >= 2) dma_wait_barrier<2 * D>();
+    else if (later == 1) dma_wait_barrier<D>();
     else dma_wait_barrier<0>();
-    if (st + kDmaStages - 1 < steps) issue(dma_slot<(I + kDmaStages - 1) % kDmaStages>(), st + kDmaStages - 1);
-    uint16_t* slot = dma_slot<I>();
+    if (st + NS - 1 < steps) issue(dma_slot<BM, (I + NS - 1) % NS>(), st + NS - 1);
+    uint16_t* slot = dma_slot<BM, I>();
     const int valid = T - st * kDmaBR;
     if (valid < kDmaBR) {                                    // last step: zero x~ rows >= T
-      uint16_t* xs = slot + kDmaBR * 128;
+      uint16_t* xs = slot + NH * kDmaSub;
       for (int v = threadIdx.x; v < (kDmaBR - valid) * 16; v += kThreads)
         *(uint4*)(xs + (valid + v / 16) * 128 + 8 * (v % 16)) = make_uint4(0, 0, 0, 0);
       __syncthreads();
     }
-    bf16x8 fa[4], fb[4];
+    // wave rows: sub-tile wm, all 128 columns (BM 256), or sub-tile 0,
+    // columns 64 wm .. (BM 128)
+    const uint16_t* ya = slot + (NH == 2 ? wm : 0) * kDmaSub;
+    const int ycol = NH == 2 ? 0 : 64 * wm;
+    bf16x8 fa[NI], fb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = frag_swz(slot, wm * 64, i, lane);
+    for (int i = 0; i < NI; ++i) fa[i] = frag_swz(ya, ycol, i, lane);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[j] = frag_swz(slot + kDmaBR * 128, wn * 64, j, lane);
+    for (int j = 0; j < 4; ++j) fb[j] = frag_swz(slot + NH * kDmaSub, wn * 64, j, lane);
     // issue priority raised for the matrix-core block (of two waves on a SIMD
     // the one with MFMAs ready goes first; 7-8% on the 1.5B dW products)
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     __builtin_amdgcn_s_setprio(0);
   };
 
-  if (steps > 0) issue(dma_slot<0>(), 0);
-  if (steps > 1) issue(dma_slot<1>(), 1);
-  if (steps > 2) issue(dma_slot<2>(), 2);
-  for (int st = 0; st < steps; st += 4) {
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) {
+    if (p < steps) {
+      if constexpr (NS == 3) issue(p == 0 ? dma_slot<BM, 0>() : dma_slot<BM, 1>(), p);
+      else issue(p == 0 ? dma_slot<BM, 0>() : p == 1 ? dma_slot<BM, 1>() : dma_slot<BM, 2>(), p);
+    }
+  }
+  for (int st = 0; st < steps; st += NS) {
     body(std::integral_constant<int, 0>{}, st);
     body(std::integral_constant<int, 1>{}, st + 1);
     body(std::integral_constant<int, 2>{}, st + 2);
-    body(std::integral_constant<int, 3>{}, st + 3);
+    if constexpr (NS == 4) body(std::integral_constant<int, 3>{}, st + 3);
   }
 
-  const int rbase = m0 + wm * 64 + 4 * (lane >> 4);
+  const int rbase = m0 + wm * WM + 4 * (lane >> 4);
   const int cbase = n0 + wn * 64 + (lane & 15);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -527,6 +558,184 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dw_dma(const BwdArgs a) {
         else ((float*)a.out)[off] = v;
       }
 }
+
+
+// ---------------------------------------------------------------------------
+// dX of a single weight tensor with dY landed by LDS DMA. Tile BM x 128 of
+// [T, K] (2 x 2 waves of (BM / 2) x 64), steps of 32 rows of O (one MFMA
+// depth) in a ring of NS slots: BM = 128 with four, BM = 256 with three.
+//   A (dY [t][o], the reduction index o contiguous): BM rows x 64 bytes per
+//   step, 16 rows per DMA instruction (4 lanes per row); the 16-byte chunk c
+//   of row r sits at c ^ ((r >> 1) & 3), so a fragment read (16 rows, one
+//   chunk each) touches every bank pair once.
+//   B (W_eff [o][k] in bf16, decoded from the packed rows): the codes of step
+//   st + NS - 1 are loaded before that step's DMAs are issued and decoded
+//   into its slot after the current step's products, so waiting for them
+//   never waits for a DMA; rows o >= O decode to zeros.
+//   Rows t >= T load row T - 1 and reach no stored output; columns o >= O of
+//   the last step load valid data that meets those zero rows.
+// ---------------------------------------------------------------------------
+constexpr int kDxPB = 128 + kPadRM;                        // decoded W row pitch (elements)
+
+template <int BM>
+constexpr int dx_slot_elems() { return BM * 32 + 32 * kDxPB; }
+
+__shared__ __align__(16) uint16_t dx_slot0[dx_slot_elems<128>()];
+__shared__ __align__(16) uint16_t dx_slot1[dx_slot_elems<128>()];
+__shared__ __align__(16) uint16_t dx_slot2[dx_slot_elems<128>()];
+__shared__ __align__(16) uint16_t dx_slot3[dx_slot_elems<128>()];
+__shared__ __align__(16) uint16_t dx_wslot0[dx_slot_elems<256>()];
+__shared__ __align__(16) uint16_t dx_wslot1[dx_slot_elems<256>()];
+__shared__ __align__(16) uint16_t dx_wslot2[dx_slot_elems<256>()];
+
+template <int BM, int I>
+__device__ __forceinline__ uint16_t* dx_slot() {
+  if constexpr (BM == 256) {
+    if constexpr (I == 0) return dx_wslot0;
+    else if constexpr (I == 1) return dx_wslot1;
+    else return dx_wslot2;
+  } else {
+    if constexpr (I == 0) return dx_slot0;
+    else if constexpr (I == 1) return dx_slot1;
+    else if constexpr (I == 2) return dx_slot2;
+    else return dx_slot3;
+  }
+}
+
+template <int BM, bool IDX>
+__global__ __launch_bounds__(kThreads, 2) void k_bwd_dx_dma(const BwdArgs a) {
+  static_assert(BM == 128 || BM == 256, "tile rows");
+  constexpr int NS = BM == 256 ? 3 : 4;                    // ring stages
+  constexpr int WM = BM / 2, NI = WM / 16;                 // wave rows, row strips
+  constexpr int DA = BM / 64;                              // A DMAs per wave and step
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  int tm, tn;
+  tile_of(xcd_tile(blockIdx.x, a.ntm * a.ntn), a.ntm, a.ntn, a.gm, tm, tn);
+  const int m0 = tm * BM, n0 = tn * 128;
+  const int O = a.O, steps = (O + 31) / 32;
+  const uint8_t* __restrict__ packed = (const uint8_t*)a.b;
+
+  // A: DMA q = DA wave + i fills rows 16 q .. 16 q + 15 of the step's tile
+  auto issue = [&](uint16_t* slot, int st) {
+#pragma unroll
+    for (int i = 0; i < DA; ++i) {
+      const int q = DA * wave + i;
+      const int r = 16 * q + (lane >> 2), pc = lane & 3;
+      const int c = pc ^ ((r >> 1) & 3);
+      const int t = min(m0 + r, a.T - 1);
+      const int o = min(32 * st + 8 * c, O - 8);
+      dma16(a.dy + (int64_t)t * a.ldy + o, slot + 16 * q * 32);
+    }
+  };
+  // B: thread v takes row v / 8 of the step and 16 columns n0 + 16 (v % 8)
+  const int brow = threadIdx.x >> 3, bcol = 16 * (threadIdx.x & 7);
+  const int kk = n0 + bcol;
+  auto load_codes = [&](int st) -> uint2 {
+    const int o = 32 * st + brow;
+    const uint8_t* row = packed + (int64_t)o * a.ldb;
+    if constexpr (IDX) {
+      const bool ok = o < O && (kk & ~31) < a.K;           // chunk kk / 32 exists
+      return ok ? *(const uint2*)(row + 8 * (kk >> 5)) : make_uint2(0u, 0u);
+    } else {
+      const bool ok = o < O && kk < a.K;                   // word kk / 16 lies in the code area
+      return make_uint2(ok ? *(const uint32_t*)(row + 4 * (kk >> 4)) : 0u, 0u);
+    }
+  };
+  auto write_b = [&](uint16_t* slot, uint2 w) {
+    uint4 lo, hi;
+    if constexpr (IDX) decode_index16(w.x, w.y, (kk >> 4) & 1, lo, hi);
+    else decode_dense16(w.x, lo, hi);
+    uint16_t* B = slot + BM * 32 + brow * kDxPB + bcol;
+    *(uint4*)B = lo;
+    *(uint4*)(B + 8) = hi;
+  };
+
+  f32x4 acc[NI][4];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto body = [&](auto I_, int st) {
+    constexpr int I = decltype(I_)::value;
+    if (st >= steps) return;
+    // at most the A DMAs of the later issued steps may still be outstanding
+    // (the codes loaded in earlier steps were consumed there)
+    const int later = min(NS - 2, steps - 1 - st);
+    if (later >= 2) dma_wait_barrier<2 * DA>();
+    else if (later == 1) dma_wait_barrier<DA>();
+    else dma_wait_barrier<0>();
+    const bool refill = st + NS - 1 < steps;
+    uint2 w = make_uint2(0u, 0u);
+    if (refill) {
+      w = load_codes(st + NS - 1);
+      issue(dx_slot<BM, (I + NS - 1) % NS>(), st + NS - 1);
+    }
+    const uint16_t* A = dx_slot<BM, I>();
+    const uint16_t* B = A + BM * 32;
+    bf16x8 fa[NI], fb[4];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = wm * WM + 16 * i + (lane & 15), g = lane >> 4;
+      fa[i] = __builtin_bit_cast(bf16x8, *(const uint4*)(A + r * 32 + 8 * (g ^ ((r >> 1) & 3))));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[j] = frag_rm<false>(B + wn * 64, kDxPB, 0, j, lane);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+    if (refill) write_b(dx_slot<BM, (I + NS - 1) % NS>(), w);
+  };
+
+  // prologue: steps 0 .. NS - 2 (their B decoded now; the first barrier
+  // publishes them)
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) {
+    if (p < steps) {
+      const uint2 w = load_codes(p);
+      uint16_t* slot = p == 0 ? dx_slot<BM, 0>() : p == 1 ? dx_slot<BM, 1>() : dx_slot<BM, 2>();
+      issue(slot, p);
+      write_b(slot, w);
+    }
+  }
+  for (int st = 0; st < steps; st += NS) {
+    body(std::integral_constant<int, 0>{}, st);
+    body(std::integral_constant<int, 1>{}, st + 1);
+    body(std::integral_constant<int, 2>{}, st + 2);
+    if constexpr (NS == 4) body(std::integral_constant<int, 3>{}, st + 3);
+  }
+
+  const float sw = a.sw_rows[0];
+  const int rbase = m0 + wm * WM + 4 * (lane >> 4);
+  const int cbase = n0 + wn * 64 + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = rbase + 16 * i + e, col = cbase + 16 * j;
+        if (row >= a.T || col >= a.K) continue;
+        float v = sw * acc[i][j][e];
+        const int64_t off = (int64_t)row * a.ldo + col;
+        if (a.out_bf16) {
+          uint16_t* o = (uint16_t*)a.out + off;
+          if (a.accumulate) v += bf16_bits_to_f32(*o);
+          *o = (uint16_t)f32_to_bf16_bits(v);
+        } else {
+          float* o = (float*)a.out + off;
+          if (a.accumulate) v += *o;
+          *o = v;
+        }
+      }
+}
+
 
 // x~ = bf16_rne(fp32(q) * sx[t]); 8 codes per thread (K % 8 == 0).
 __global__ __launch_bounds__(256) void k_act_dequant(const int8_t* __restrict__ xq,
@@ -651,6 +860,30 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t ldy, const void* packed, co
   a.out_bf16 = dx_bf16; a.accumulate = accumulate;
   if (cfg < 0) cfg = pick_cfg(T, K);
   const bool idx = index_form(N, M);
+  // The LDS-DMA kernel with 256-row tiles where it measured faster: at
+  // least two tiles per CU and a reduction of 2048 rows or more (Qwen2.5-3B
+  // up 445 -> 360 us, down 514 -> 480); with fewer tiles or shorter
+  // reductions (the 0.5B and 1.5B projections) the register-staged 128x128
+  // kernel is faster. SBL_BWD_DX_DMA=1 forces it (SBL_BWD_DX_WIDE=0 / 1
+  // picks the tile rows), SBL_BWD_DMA=0 disables it (tuning and tests).
+  const char* ev = std::getenv("SBL_BWD_DMA");
+  const char* ed = std::getenv("SBL_BWD_DX_DMA");
+  const bool dma = ed ? ed[0] == '1'
+                      : cdiv(T, 256) * cdiv(K, 128) >= 2 * (int64_t)device_info().cus && O >= 2048;
+  if (nseg == 1 && cfg == 0 && dma && !(ev && ev[0] == '0')) {
+    const char* ew = std::getenv("SBL_BWD_DX_WIDE");
+    const bool wide = ew ? ew[0] == '1' : true;
+    set_order(a, wide ? 256 : 128, 128, true);
+    const dim3 grid((unsigned)(a.ntm * a.ntn)), block(kThreads);
+    if (wide) {
+      if (idx) hipLaunchKernelGGL((k_bwd_dx_dma<256, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((k_bwd_dx_dma<256, false>), grid, block, 0, s, a);
+    } else {
+      if (idx) hipLaunchKernelGGL((k_bwd_dx_dma<128, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((k_bwd_dx_dma<128, false>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+  }
   if (nseg > 1)
     return idx ? launch_mode<kModeDxIndex, true>(a, cfg, s) : launch_mode<kModeDxDense, true>(a, cfg, s);
   return idx ? launch_mode<kModeDxIndex, false>(a, cfg, s) : launch_mode<kModeDxDense, false>(a, cfg, s);
@@ -669,8 +902,18 @@ hipError_t launch_bwd_dw(const uint16_t* dy, int64_t ldy, const uint16_t* xt, in
   if (cfg < 0) cfg = pick_cfg(O, K);
   const char* ev = std::getenv("SBL_BWD_DMA");   // tuning: 0 keeps the register-staged kernel
   if (cfg == 0 && !(ev && ev[0] == '0')) {
-    set_order(a, 128, 128, false);
-    hipLaunchKernelGGL(k_bwd_dw_dma, dim3((unsigned)(a.ntm * a.ntn)), dim3(kThreads), 0, s, a);
+    // 256-row tiles when they still give every CU at least one (measured
+    // 1.02-1.29x faster on the Qwen2.5 0.5B-3B projections that qualify;
+    // 0.78x on the 0.5B down projection's 152 tiles, which does not)
+    const char* ew = std::getenv("SBL_BWD_DW_WIDE");   // tuning: 0 / 1 forces the tile rows
+    const bool wide = ew ? ew[0] == '1' : cdiv(O, 256) * cdiv(K, 128) >= (int64_t)device_info().cus;
+    if (wide) {
+      set_order(a, 256, 128, false);
+      hipLaunchKernelGGL(k_bwd_dw_dma<256>, dim3((unsigned)(a.ntm * a.ntn)), dim3(kThreads), 0, s, a);
+    } else {
+      set_order(a, 128, 128, false);
+      hipLaunchKernelGGL(k_bwd_dw_dma<128>, dim3((unsigned)(a.ntm * a.ntn)), dim3(kThreads), 0, s, a);
+    }
     return hipGetLastError();
   }
   return launch_mode<kModeDw, false>(a, cfg, s);

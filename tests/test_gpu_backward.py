@@ -100,9 +100,27 @@ def test_bwd_dx_parity(S, N, M, out_bf16):
 @pytest.mark.parametrize("N,M", [(6, 8), (2, 4)])
 def test_bwd_dx_every_tile_config(S, cfg, N, M, monkeypatch):
     monkeypatch.setenv("SBL_BWD_TILE", str(cfg))
+    monkeypatch.setenv("SBL_BWD_DMA", "0")                 # the register-staged kernel
     for T, O, K in [(200, 264, 392), (70, 520, 136)]:
         log_case("bwd_dx tile", cfg, N, M, T, O, K)
         _dx_case(S, T, O, K, N, M, False, seed=cfg + T)
+
+
+@pytest.mark.parametrize("wide", ["0", "1"])
+@pytest.mark.parametrize("N,M", [(6, 8), (2, 4), (2, 8)])
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_bwd_dx_dma_kernel(S, wide, N, M, out_bf16, monkeypatch):
+    """The single-tensor dX kernels with dY landed by LDS DMA, 128x128 and
+    256x128 tiles: T tails (one row, past a tile), O tails (a last step of 8
+    rows, steps past one round of the three- and four-stage rings), K tails
+    (partial tile columns), and accumulation into dx."""
+    monkeypatch.setenv("SBL_BWD_TILE", "0")
+    monkeypatch.setenv("SBL_BWD_DX_DMA", "1")
+    monkeypatch.setenv("SBL_BWD_DX_WIDE", wide)
+    for T, O, K, acc in [(1, 8, 16, False), (33, 136, 264, False), (150, 264, 392, True),
+                         (300, 392, 520, False), (257, 520, 136, False), (97, 40, 16, True)]:
+        log_case("bwd_dx dma", wide, N, M, out_bf16, T, O, K, acc)
+        _dx_case(S, T, O, K, N, M, out_bf16, seed=T + O + K + N, accumulate=acc)
 
 
 @pytest.mark.parametrize("N,M", [(6, 8), (2, 4)])
@@ -146,16 +164,20 @@ def test_bwd_dw_every_tile_config(S, cfg, monkeypatch):
         _dw_case(S, T, O, K, False, seed=cfg + T)
 
 
+@pytest.mark.parametrize("wide", ["0", "1"])
 @pytest.mark.parametrize("out_bf16", [False, True])
-def test_bwd_dw_dma_kernel(S, out_bf16, monkeypatch):
-    """The 128x128 dW kernel with direct-to-LDS loads: T tails of every size
-    class (one row, one past a step, many steps), tiles smaller than O and K
-    (clamped edge loads), several tile-order groups."""
+def test_bwd_dw_dma_kernel(S, out_bf16, wide, monkeypatch):
+    """The dW kernels with direct-to-LDS loads, 128x128 and 256x128 tiles:
+    T tails of every size class (one row, one past a step, many steps, past
+    one round of the three- and four-stage rings), tiles smaller than O and
+    K (clamped edge loads), several tile-order groups."""
     monkeypatch.setenv("SBL_BWD_TILE", "0")
+    monkeypatch.setenv("SBL_BWD_DW_WIDE", wide)
     for T, O, K, grp in [(1, 8, 8, 1), (33, 136, 264, 1), (150, 264, 392, 3), (97, 8, 16, 1),
-                         (300, 392, 520, 2), (256, 128, 128, 1)]:
+                         (300, 392, 520, 2), (256, 128, 128, 1), (65, 520, 136, 1),
+                         (160, 776, 264, 2)]:
         monkeypatch.setenv("SBL_BWD_GROUP", str(grp))
-        log_case("bwd_dw dma", out_bf16, T, O, K, grp)
+        log_case("bwd_dw dma", out_bf16, wide, T, O, K, grp)
         _dw_case(S, T, O, K, out_bf16, seed=T + O + K)
 
 
@@ -246,3 +268,23 @@ def test_bwd_full_size_sampled(S):
     ref = o.linear_bwd_dw(dy2[:, orow], oxt)
     abs_sum = o.linear_bwd_dw(np.abs(dy2[:, orow]), np.abs(oxt))
     assert_grad_close(host(dw)[orow], ref, abs_sum, wl.T, False)
+
+
+def test_bwd_dx_dma_full_size_sampled(S):
+    """dX of a Qwen2.5-3B-shaped up projection (T = 8192 tokens, 11008 x
+    2048 weights, 6:8), the shape class that takes the LDS-DMA dX kernel
+    with 256-row tiles, in the launch configuration chosen for it; checked on
+    sampled rows."""
+    T, O, K, N, M = 8192, 11008, 2048, 6, 8
+    rng = np.random.default_rng(17)
+    W, _ = make_linear_inputs(1, O, K, seed=17)
+    log_case("bwd full dx dma", T, O, K)
+    p = S.sbl_quant_mask_weight(to_dev(W), N, M, want_sw_rows=True)
+    dy = _dy(rng, T, O)
+    dx = S.sbl_linear_bwd_dx(bf16_tensor(dy), p["packed"], p["sw_rows"], K, N, M,
+                             out_dtype=torch.float32)
+    w_eff, _, _, sw = o.quant_mask_weight(W, N, M)
+    rows = rng.choice(T, 48, replace=False)
+    ref = o.linear_bwd_dx(dy[rows], w_eff, sw)
+    abs_sum = o.linear_bwd_dx(np.abs(dy[rows]), np.abs(w_eff), sw)
+    assert_grad_close(host(dx)[rows], ref, abs_sum, O, False)
