@@ -799,8 +799,10 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
 #pragma unroll
       for (int t = 0; t < U; ++t) {
         const int s = sb + it + t;
-        aload(s + NA - 1, ar[(t + NA - 1) % NA]);      // into the slot of step s-1
+        // (xq first: waiting for it before its LDS store then leaves the W
+        // loads behind it in flight)
         if constexpr (NBS == 1) bload(s + 1, rb[0]);
+        aload(s + NA - 1, ar[(t + NA - 1) % NA]);      // into the slot of step s-1
         if (s < se) compute(t & 1, ar[t % NA], ar[(t + 1) % NA]);
         if constexpr (NBS == 1) {
           bstore(s + 1, (t + 1) & 1, rb[0]);
@@ -809,7 +811,9 @@ void k_gemm_ra(const int8_t* __restrict__ xq, const float* __restrict__ sx,
           bstore(s + 1, (t + 1) & 1, rb[(t + 1) & 1]);
           bload(s + 3, rb[(t + 1) & 1]);
         }
-        __syncthreads();
+        // LDS-only barrier: the global loads of later steps stay in flight
+        // (__syncthreads() would wait for all of them)
+        dma_barrier<63>();
       }
     }
 
