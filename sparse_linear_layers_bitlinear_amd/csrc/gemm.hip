@@ -983,7 +983,8 @@ enum TileCfg { kT256x256 = 0, kT256x128 = 1, kT128x256 = 2, kT128x128 = 3, kT256
                kR512x64w8 = 23,    // WO 8, KS 1, FI 4, FJ 4
                kR256x80 = 24,      // WO 4, KS 1, FI 4, FJ 5
                kR256x96 = 25,      // WO 4, KS 1, FI 4, FJ 6 (NA 2)
-               kNumCfg = 26 };
+               kR512x128w8 = 26,   // WO 8, KS 1, FI 4, FJ 8 (NA 2)
+               kNumCfg = 27 };
 
 struct Args {
   const int8_t* xq; const float* sx; const uint8_t* packed; int64_t pitch; const float* sw;
@@ -1067,6 +1068,7 @@ static hipError_t launch_sel(int cfg, const Args& a, hipStream_t s) {
     case kR512x64w8: return launch_ra<8, 1, 4, 4, 4, SP, KA16, YBF16>(a, s);
     case kR256x80: return launch_ra<4, 1, 4, 5, 4, SP, KA16, YBF16>(a, s);
     case kR256x96: return launch_ra<4, 1, 4, 6, 2, SP, KA16, YBF16>(a, s);
+    case kR512x128w8: return launch_ra<8, 1, 4, 8, 2, SP, KA16, YBF16>(a, s);
     case kT64x128: return launch_cfg<64, 128, 2, 2, SP, KA16, YBF16>(a, s);
     case kDma128x256: return launch_dma<128, 256, 2, 4, SP, YBF16, SP ? 3 : 4>(a, s);
     case kDma256x128: return launch_dma<256, 128, 4, 2, SP, YBF16, SP ? 4 : 5>(a, s);
@@ -1105,6 +1107,10 @@ static int choose_cfg(int64_t T, int64_t O, int64_t K, bool sp) {
   const int64_t t64 = cdiv(O, 256) * cdiv(T, 64);
   const int64_t t128 = cdiv(O, 256) * cdiv(T, 128);
   if (t64 < cus) return kR128x64k2;
+  // long rows with a 512x128 tile for every CU: one 8-wave workgroup per CU
+  // stages each xq tile once for eight waves instead of four (Qwen2.5-3B down
+  // projections, K = 11008: 2:4 123 -> 117 us, 2:8 116 -> 112, 6:8 equal)
+  if (K >= 4096 && cdiv(O, 512) * cdiv(T, 128) >= cus) return kR512x128w8;
   if (sp) {
     if (K < 4096) return kR256x96;
     return t128 >= 2 * cus ? kR256x128 : kR512x64w8;

@@ -494,6 +494,11 @@ def _gemm_case(S, T, O, K, N, M, ydt, seed, sw_per_row):
         assert_f32_close(host(y), y_ref)
     else:
         assert_bf16_exact(host(y), acc_ref, sx, sw if sw_per_row else sw[0])
+        # without the int32 output the prefill kernel stages the bf16 tile in
+        # LDS and writes whole row segments: a separate epilogue
+        y2 = S.sbl_gemm(to_dev(xq), to_dev(sx), to_dev(packed.reshape(-1)), to_dev(sw), O, N, M,
+                        out_dtype=ydt)
+        assert_bf16_exact(host(y2), acc_ref, sx, sw if sw_per_row else sw[0])
 
 
 @pytest.mark.parametrize("N,M", [(6, 8), (2, 4), (2, 8), (1, 4), (8, 8), (4, 8), (3, 8), (7, 8)])
@@ -576,6 +581,9 @@ def _full_projection(S, W, x, N, M, rows_t, rows_o, sw_full=None):
     acc_g = host(acc)[np.ix_(rows_t, rows_o)]
     assert np.array_equal(acc_g, acc_s)
     assert_bf16_exact(host(y)[np.ix_(rows_t, rows_o)], acc_s, sx_s, sw)
+    # bf16 y alone (the staged epilogue the benchmark times)
+    y2 = S.sbl_gemm(xq, sx, r["packed"], r["gamma_sw"][1:], O, N, M, out_dtype=torch.bfloat16)
+    assert_bf16_exact(host(y2)[np.ix_(rows_t, rows_o)], acc_s, sx_s, sw)
 
 
 def _sample(n, k, seed):
@@ -604,6 +612,50 @@ def test_full_size_qwen3b_sweep(S):
             log_case("full size qwen3b", lin.name, f"{N}:{M}", wl.T, lin.O, lin.K)
             _full_projection(S, W[lin.name], X[lin.x_name], N, M,
                              _sample(wl.T, 32, N), _sample(lin.O, 96, N + 1))
+
+
+@pytest.mark.parametrize("wl,nm", [("qwen05b_ffn", None), ("qwen15b_ffn", None),
+                                   ("qwen3b_sweep", (6, 8)), ("qwen3b_sweep", (2, 4)),
+                                   ("qwen3b_sweep", (2, 8))])
+def test_prefill_bench_launches(S, wl, nm):
+    """The GEMM calls the prefill benchmark times, as it makes them: per input
+    one sbl_gemm over the group's tensors concatenated along O (gate|up) with
+    per-row sw written by each tensor's preparation, int8 x from
+    sbl_quant_act, bf16 y into a preallocated buffer, no int32 output. Sampled
+    rows and columns of each segment against the oracle, bit for bit."""
+    w = WORKLOADS[wl]
+    N, M = nm if nm else (w.N, w.M)
+    W, X = make_workload(wl)
+    groups = {}
+    for lin in w.linears:
+        groups.setdefault(lin.x_name, []).append(lin)
+    for xn, lins in groups.items():
+        K = dict(w.x_specs)[xn]
+        O = sum(l.O for l in lins)
+        log_case("prefill bench launch", wl, f"{N}:{M}", "+".join(l.name for l in lins), w.T, O, K)
+        packed = torch.empty(S.sbl_packed_bytes(O, K, N, M), dtype=torch.uint8, device="cuda:0")
+        swr = torch.empty(O, dtype=torch.float32, device="cuda:0")
+        op, oo = 0, 0
+        for l in lins:
+            nb = S.sbl_packed_bytes(l.O, l.K, N, M)
+            S.sbl_quant_mask_weight(to_dev(W[l.name]), N, M, packed=packed[op:op + nb],
+                                    sw_rows=swr[oo:oo + l.O])
+            op += nb
+            oo += l.O
+        x = X[xn]
+        xq, sx = S.sbl_quant_act(bf16_tensor(x))
+        y = torch.empty((w.T, O), dtype=torch.bfloat16, device="cuda:0")
+        S.sbl_gemm(xq, sx, packed, swr, O, N, M, y=y)
+        yh = host(y)
+        rows_t = _sample(w.T, 24, O)
+        xq_s, sx_s = o.quant_act(x[rows_t])
+        oo = 0
+        for i, l in enumerate(lins):
+            rows_o = _sample(l.O, 64, i + 3)
+            w_eff_s, _, _, sw = oracle_rows(W[l.name], N, M, rows_o)
+            acc_s = o.gemm_int(xq_s, w_eff_s)
+            assert_bf16_exact(yh[np.ix_(rows_t, oo + rows_o)], acc_s, sx_s, sw)
+            oo += l.O
 
 
 @pytest.mark.parametrize("T", [1, 4, 8])
@@ -760,7 +812,7 @@ def test_decode_large_k_falls_back(S):
     assert_f32_close(host(y), o.linear_fwd(bf16_round(x), W, N, M)["y"])
 
 
-@pytest.mark.parametrize("cfg", list(range(26)))
+@pytest.mark.parametrize("cfg", list(range(27)))
 def test_gemm_every_tile_config(S, cfg, monkeypatch):
     """Each workgroup-tile configuration of the GEMM, forced, on ragged shapes."""
     monkeypatch.setenv("SBL_GEMM_TILE", str(cfg))
