@@ -65,7 +65,7 @@ struct DecodeArgs {
 };
 
 // LDS: W [R][np][1 KB] | xs [tg][xpitch] int8 | sxs [16] f32 | pmax [16] u32 (per half-wave) |
-//      red [R][64][4] i32     (np = pairs of K-steps)
+//      red [R][4][64] i32     (np = pairs of K-steps; value k of lane l at 64 k + l)
 __host__ __device__ inline int dec_np(int K) { return ((K + 127) / 128 + 1) / 2; }
 __host__ __device__ inline int dec_xpitch(int K) { return 128 * ((K + 127) / 128) + 16; }
 __host__ __device__ inline int dec_off_x(int K, int R) { return R * dec_np(K) * 1024; }
@@ -122,7 +122,8 @@ __device__ __forceinline__ void lds_barrier() {
 // for every tile, so they are read from LDS once per chunk, and each tile's W
 // fragments are read while the tile before it is computed. Reads past the
 // wave's last K-step repeat it (in bounds; never computed). The int32 sums go
-// to the tile's LDS accumulator (red + 256 r; this lane's 4 at rl) by ds_add.
+// to the tile's LDS accumulator (red + 256 r; this lane's k-th at rl + 64 k) by
+// ds_add.
 template <bool SP, int KU>
 __device__ __forceinline__ void mma_tiles(const uint8_t* wsm, const int8_t* xr, int aoff, int wave,
                                           int nsw, int np, int ntb, int g, int* rl) {
@@ -166,9 +167,9 @@ __device__ __forceinline__ void mma_tiles(const uint8_t* wsm, const int8_t* xr, 
       acc0 += acc1;
       int* const rp = rl + r * 256;
       atomicAdd(rp + 0, acc0[0]);
-      atomicAdd(rp + 1, acc0[1]);
-      atomicAdd(rp + 2, acc0[2]);
-      atomicAdd(rp + 3, acc0[3]);
+      atomicAdd(rp + 64, acc0[1]);
+      atomicAdd(rp + 128, acc0[2]);
+      atomicAdd(rp + 192, acc0[3]);
     };
 #pragma unroll
     for (int i = 0; i < KU; ++i) wa[i] = *(const uint2*)(wsm + woff[i]);
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
   // more K-steps the reads issued up front cost more than the reuse saves)
   const int nsw = wave < ns ? (ns - 1 - wave) / kDecWaves + 1 : 0;
   if (ntb >= 2 && nsw <= 4) {
-    int* const rl = red + lane * 4;
+    int* const rl = red + lane;
     if (nsw <= 2) mma_tiles<SP, 2>(wsm, xr, aoff, wave, nsw, np, ntb, g, rl);
     else mma_tiles<SP, 4>(wsm, xr, aoff, wave, nsw, np, ntb, g, rl);
   } else {
@@ -376,17 +377,23 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
       if (s < ns) unit(r, s, acc0);
       acc0 += acc1;
       if (wave < ns) {
-        int* const rp = red + r * 256 + lane * 4;
+        // (k-major: the 64 lanes of one add hit 64 consecutive words, no
+        // bank conflicts; lane-major quads put 8 lanes on each bank)
+        int* const rp = red + r * 256 + lane;
         atomicAdd(rp + 0, acc0[0]);
-        atomicAdd(rp + 1, acc0[1]);
-        atomicAdd(rp + 2, acc0[2]);
-        atomicAdd(rp + 3, acc0[3]);
+        atomicAdd(rp + 64, acc0[1]);
+        atomicAdd(rp + 128, acc0[2]);
+        atomicAdd(rp + 192, acc0[3]);
       }
     }
   }
   __syncthreads();
 
   // lane l of tile r: outputs o = 16 (tb + r) + 4 (l / 16) + 0..3 of token l % 16
+  auto rsum = [&](int i) {
+    const int* const p = red + (i >> 6) * 256 + (i & 63);
+    return v4i{p[0], p[64], p[128], p[192]};
+  };
   for (int i = tid; i < ntb * 64; i += kDecThreads) {
     const int t = i & 15, o = (tb + (i >> 6)) * 16 + 4 * ((i >> 4) & 3);
     if (i != tid) {
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecodeArgs a) {
       for (int k = 0; k < 4; ++k) swp[k] = a.sw[(int64_t)min(o + k, O - 1) * a.sw_inc];
     }
     if (t < T && o < O)
-      store_tile_sw<YBF16>(a.y, a.acc, *(const v4i*)(red + 4 * i), t0 + t, o, O, sxs[t], swp);
+      store_tile_sw<YBF16>(a.y, a.acc, rsum(i), t0 + t, o, O, sxs[t], swp);
   }
 }
 
