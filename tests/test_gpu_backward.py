@@ -288,3 +288,62 @@ def test_bwd_dx_dma_full_size_sampled(S):
     ref = o.linear_bwd_dx(dy[rows], w_eff, sw)
     abs_sum = o.linear_bwd_dx(np.abs(dy[rows]), np.abs(w_eff), sw)
     assert_grad_close(host(dx)[rows], ref, abs_sum, O, False)
+
+
+@pytest.mark.parametrize("wl_name", ["qwen05b_ffn", "qwen15b_ffn"])
+def test_bwd_bench_launches(S, wl_name):
+    """The backward calls the training-step benchmark times, as it makes them:
+    per input, x~ from sbl_act_dequant, one sbl_linear_bwd_dx over the group's
+    tensors concatenated along O (gate|up: two segments with their own sw)
+    into a preallocated bf16 dx, and one sbl_linear_bwd_dw of the group's dY
+    against x~ into a preallocated fp32 dW. Sampled rows against the oracle,
+    the segments' products summed in fp64."""
+    wl = WORKLOADS[wl_name]
+    N, M, T = wl.N, wl.M, wl.T
+    W, X = make_workload(wl_name)
+    rng = np.random.default_rng(23)
+    dev = torch.device("cuda:0")
+    groups = {}
+    for lin in wl.linears:
+        groups.setdefault(lin.x_name, []).append(lin)
+    for xn, lins in groups.items():
+        K = dict(wl.x_specs)[xn]
+        O = sum(l.O for l in lins)
+        log_case("bwd bench launch", wl_name, "+".join(l.name for l in lins), T, O, K)
+        packed = torch.empty(S.sbl_packed_bytes(O, K, N, M), dtype=torch.uint8, device=dev)
+        swr = torch.empty(O, dtype=torch.float32, device=dev)
+        op, oo = 0, 0
+        for l in lins:
+            nb = S.sbl_packed_bytes(l.O, l.K, N, M)
+            S.sbl_quant_mask_weight(to_dev(W[l.name]), N, M, packed=packed[op:op + nb],
+                                    sw_rows=swr[oo:oo + l.O])
+            op += nb
+            oo += l.O
+        x = X[xn]
+        xq, sx = S.sbl_quant_act(bf16_tensor(x))
+        xt = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+        S.sbl_act_dequant(xq, sx, xt=xt)
+        dy = _dy(rng, T, O)
+        dx = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+        dw = torch.empty((O, K), dtype=torch.float32, device=dev)
+        S.sbl_linear_bwd_dx(bf16_tensor(dy), packed, swr, K, N, M, seg_rows=[l.O for l in lins],
+                            dx=dx)
+        S.sbl_linear_bwd_dw(bf16_tensor(dy), xt, dw=dw)
+        oq, osx = o.quant_act(x)
+        oxt = o.act_dequant_bf16(oq, osx)
+        assert np.array_equal(f32_bits(host(xt)), f32_bits(oxt))
+        rows = rng.choice(T, 32, replace=False)
+        ref = np.zeros((len(rows), K))
+        abs_sum = np.zeros((len(rows), K))
+        oo = 0
+        for l in lins:
+            w_eff, _, _, sw = o.quant_mask_weight(W[l.name], N, M)
+            d = dy[rows][:, oo:oo + l.O]
+            ref += o.linear_bwd_dx(d, w_eff, sw)
+            abs_sum += o.linear_bwd_dx(np.abs(d), np.abs(w_eff), sw)
+            oo += l.O
+        assert_grad_close(host(dx)[rows], ref, abs_sum, O, True)
+        orow = rng.choice(O, 48, replace=False)
+        ref = o.linear_bwd_dw(dy[:, orow], oxt)
+        abs_sum = o.linear_bwd_dw(np.abs(dy[:, orow]), np.abs(oxt))
+        assert_grad_close(host(dw)[orow], ref, abs_sum, T, False)
