@@ -513,6 +513,27 @@ def calibrate_copy():
                       "bytes_written_per_copy": n, "copies": 3}))
 
 
+def copy_bandwidth():
+    """HBM bandwidth a plain device copy reaches on this GPU (GB/s, read + written
+    bytes): a 1 GiB device-to-device copy, one warm-up then five timed copies
+    between HIP events on the current stream. The practical ceiling the
+    HBM-bound calls are also compared with."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    rate = 2.0 * n * 5 / (s.elapsed_time(e) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return rate
+
+
 def traffic_tag(a, N, M):
     """Workload key of the committed counter summaries."""
     if a.workload == "bitnet_decode":
@@ -523,9 +544,10 @@ def traffic_tag(a, N, M):
             + (" gated" if a.mask_gated_grad and a.backward else ""))
 
 
-def per_call_rates(step, per_call):
+def per_call_rates(step, per_call, copy_gbs=None):
     """Device time of one launch of each call and its rate against the call's
-    own roofline (HBM GB/s or effective TOPS)."""
+    own roofline (HBM GB/s or effective TOPS); HBM-bound calls also against
+    the measured device-copy bandwidth."""
     out = {}
     for k, ms in per_call.items():
         bound, units, _ = step.call_info(k)
@@ -533,6 +555,8 @@ def per_call_rates(step, per_call):
         if bound == "hbm":
             out[k] = {"us": round(ms * 1e3, 2), "GB/s": round(rate / 1e9, 1),
                       "frac": round(rate / 1e9 / PEAK_HBM_GBS, 4)}
+            if copy_gbs:
+                out[k]["frac_of_copy"] = round(rate / 1e9 / copy_gbs, 4)
         elif bound == "mfma_bf16":
             out[k] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(rate / 1e12, 1),
                       "frac": round(rate / 1e12 / PEAK_BF16_DENSE_TFLOPS, 4)}
@@ -588,6 +612,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    copy_gbs = copy_bandwidth()
+    if roof["bound"] == "hbm":
+        roof["frac_of_copy"] = round(roof["achieved"] / copy_gbs, 4)
     roof["traffic"] = measured_traffic(traffic_tag(a, N, M), dom)
     roof["kernel"] = dom
     roof["avg_ms"] = round(per_call[dom], 5)
@@ -621,9 +648,10 @@ def main():
                   else "int8xternary->int32 (bf16 in/out)"), "data": "synthetic",
         "config": config, "roofline": roof,
         "breakdown_ms": {k: round(share[k], 5) for k in share},
-        "per_call": per_call_rates(step, per_call),
+        "per_call": per_call_rates(step, per_call, copy_gbs),
         "breakdown_note": "per-step device ms of each call, from graph replays of that call alone",
         "timing": "eager launches" if a.eager else "HIP graph replay",
+        "copy_GBs": round(copy_gbs, 1),
     }
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(a.workload, N, M, a.cpu_seconds, a.decode_T,
