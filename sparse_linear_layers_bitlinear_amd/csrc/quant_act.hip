@@ -17,7 +17,7 @@
 
 namespace sbl {
 
-constexpr int kActRowsPerBlock = 4;  // 4 wavefronts, one row each
+constexpr int kActRowsPerBlock = 4;
 
 // codes of one 16-byte input vector: 8 bytes (bf16) or 4 bytes (fp32)
 template <bool BF16>
@@ -109,11 +109,23 @@ __global__ __launch_bounds__(256) void k_quant_act_scalar(const void* __restrict
 // stays in L2) and only the int8 codes are written: the HBM round trip of a
 // separate normalized tensor is gone.
 //
-// The exact sum: every lane marks the 32-binade windows its squares fall in;
-// for each window present in the row (a wave-uniform loop, usually two or
-// three windows) every lane adds its squares of that window as integers into
-// a 96-bit register accumulator, the wave sums the accumulators exactly, and
-// the row's 16 window bins are turned into the fp64 S.
+// The exact sum, fast case: a square of a bf16 value has at most 16
+// significant bits (fp32 input: 24), so the squares whose exponents lie in a
+// window of W binades are integer multiples of the window's lowest unit, and
+// a sum of at most K of them stays below K * 2^(W - 1 + SB) of that unit.
+// With W = 54 - SB - ceil(log2 K) every partial sum is an integer below 2^53
+// units: fp64 accumulation of the window's squares is exact in any order.
+// A first pass finds the largest square; if every nonzero square is normal
+// and lies in the two windows below the largest, each window is summed in
+// fp64 (per lane, then over the wave) and the two exact sums are added once:
+// one IEEE addition, so S is the exact sum rounded once to the nearest fp64.
+// Other rows (squares spread over more binades, subnormal squares, overflow)
+// take the general sum: every lane marks the 32-binade windows its squares
+// fall in; for each window present in the row (a wave-uniform loop) every
+// lane adds its squares of that window as integers into a 96-bit register
+// accumulator, the wave sums the accumulators exactly, and the row's 16
+// window bins are turned into the fp64 S. That path re-reads the row from
+// L2 so that it holds few registers.
 // ---------------------------------------------------------------------------
 template <bool BF16>
 __device__ __forceinline__ void unpack_f32(const uint4& d, float* f) {
@@ -130,48 +142,46 @@ __device__ __forceinline__ void unpack_f32(const uint4& d, float* f) {
   }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(256) void k_rmsnorm_quant_act(const void* __restrict__ xv,
-                                                           const float* __restrict__ gain,
-                                                           int64_t T, int64_t K, int64_t ldx,
-                                                           float eps_n, float eps,
-                                                           int8_t* __restrict__ xq,
-                                                           float* __restrict__ sx) {
-  constexpr int V = BF16 ? 8 : 4;
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kActRowsPerBlock + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int64_t nvec = K / V;
-  const uint4* row = (const uint4*)((const char*)xv + t * ldx * (BF16 ? 2 : 4));
-  int8_t* qrow = xq + t * K;
+// The fused kernel keeps 8 vectors per lane in registers (with 16 its four
+// passes need more than 256 registers) and re-reads the rest of a row from L2
+// in batches of kRmsBatch loads issued together.
+constexpr int kRmsCache = 8;
+constexpr int kRmsBatch = 8;
 
-  uint4 d[kActCache];
+// fp64 sum over the wave (any order: the callers' terms sum exactly)
+__device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
-  for (int u = 0; u < kActCache; ++u) {
-    const int64_t i = lane + 64 * u;
-    d[u] = i < nvec ? row[i] : make_uint4(0, 0, 0, 0);   // zeros add +0 to S
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+    v = v < o ? v : o;
   }
-  // square of element e of a vector, as a sign-free fp32 bit pattern
-  auto sq_bits = [&](const uint4& v, int e) -> uint32_t {
-    float f[V];
-    unpack_f32<BF16>(v, f);
-    const float p = f[e] * f[e];
-    return __float_as_uint(p);
-  };
-  // windows holding a nonzero square (per lane, then over the wave)
+  return v;
+}
+
+// the general exact sum of fp32(x * x) over a row (see above)
+template <bool BF16>
+__device__ __attribute__((noinline)) double row_square_sum_windows(const uint4* __restrict__ row,
+                                                                   int64_t nvec, int lane) {
+  constexpr int V = BF16 ? 8 : 4;
   uint32_t tags = 0;
-  auto mark = [&](const uint4& v) {
+#pragma unroll 1
+  for (int64_t i = lane; i < nvec; i += 64) {
+    float f[V];
+    unpack_f32<BF16>(row[i], f);
 #pragma unroll
     for (int e = 0; e < V; ++e) {
       uint32_t tg;
       uint64_t tv;
-      exact_term(sq_bits(v, e), tg, tv);
+      exact_term(__float_as_uint(f[e] * f[e]), tg, tv);
       tags |= (tv != 0 ? 1u : 0u) << tg;
     }
-  };
-#pragma unroll
-  for (int u = 0; u < kActCache; ++u) mark(d[u]);
-  for (int64_t i = lane + 64 * kActCache; i < nvec; i += 64) mark(row[i]);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) tags |= (uint32_t)__shfl_xor((int)tags, off, 64);
   tags = __builtin_amdgcn_readfirstlane(tags);
@@ -182,18 +192,18 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant_act(const void* __restric
     const uint32_t tw = 31u - __clz(tags);
     tags &= ~(1u << tw);
     uint32_t a0 = 0, a1 = 0, a2 = 0;
-    auto add = [&](const uint4& v) {
+#pragma unroll 1
+    for (int64_t i = lane; i < nvec; i += 64) {
+      float f[V];
+      unpack_f32<BF16>(row[i], f);
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         uint32_t tg;
         uint64_t tv;
-        exact_term(sq_bits(v, e), tg, tv);
+        exact_term(__float_as_uint(f[e] * f[e]), tg, tv);
         add96(a0, a1, a2, tg == tw ? tv : 0ull);
       }
-    };
-#pragma unroll
-    for (int u = 0; u < kActCache; ++u) add(d[u]);
-    for (int64_t i = lane + 64 * kActCache; i < nvec; i += 64) add(row[i]);
+    }
     const unsigned long long lo = wave_sum_u64(a0);
     const unsigned long long hi = wave_sum_u64((unsigned long long)a1 | ((unsigned long long)a2 << 32));
 #pragma unroll
@@ -203,7 +213,93 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant_act(const void* __restric
         bins[2 * j + 1] = hi;
       }
   }
-  const double S = exact_bins_to_f64(bins);
+  return exact_bins_to_f64(bins);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_rmsnorm_quant_act(const void* __restrict__ xv,
+                                                           const float* __restrict__ gain,
+                                                           int64_t T, int64_t K, int64_t ldx,
+                                                           float eps_n, float eps,
+                                                           int8_t* __restrict__ xq,
+                                                           float* __restrict__ sx) {
+  constexpr int V = BF16 ? 8 : 4;
+  constexpr int SB = BF16 ? 16 : 24;                    // significant bits of a square
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * kActRowsPerBlock + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int64_t nvec = K / V;
+  const uint4* row = (const uint4*)((const char*)xv + t * ldx * (BF16 ? 2 : 4));
+  int8_t* qrow = xq + t * K;
+
+  uint4 d[kRmsCache];
+#pragma unroll
+  for (int u = 0; u < kRmsCache; ++u) {
+    const int64_t i = lane + 64 * u;
+    d[u] = i < nvec ? row[i] : make_uint4(0, 0, 0, 0);   // zero squares change nothing
+  }
+  // f(v, i) for the vectors past the register cache, kRmsBatch loads in flight
+  auto tail = [&](auto&& f) {
+    for (int64_t i0 = lane + 64 * kRmsCache; i0 < nvec; i0 += 64 * kRmsBatch) {
+      uint4 w[kRmsBatch];
+#pragma unroll
+      for (int b = 0; b < kRmsBatch; ++b) {
+        const int64_t i = i0 + 64 * b;
+        w[b] = i < nvec ? row[i] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int b = 0; b < kRmsBatch; ++b)
+        if (i0 + 64 * b < nvec) f(w[b], i0 + 64 * b);
+    }
+  };
+  // largest square and smallest nonzero square (bit patterns of non-negative
+  // floats order as their values)
+  uint32_t smax = 0, smin = 0xFFFFFFFFu;
+  auto range = [&](const uint4& v) {
+    float f[V];
+    unpack_f32<BF16>(v, f);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const uint32_t b = __float_as_uint(f[e] * f[e]);
+      smax = max(smax, b);
+      smin = min(smin, b != 0 ? b : 0xFFFFFFFFu);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kRmsCache; ++u) range(d[u]);
+  tail([&](const uint4& v, int64_t) { range(v); });
+  smax = __builtin_amdgcn_readfirstlane(wave_max_u32(smax));
+  smin = __builtin_amdgcn_readfirstlane(wave_min_u32(smin));
+  int lk = 0;                                            // ceil(log2 K)
+  while ((int64_t)1 << lk < K) ++lk;
+  const int W = 54 - SB - lk;                            // window width (binades)
+  const int emax = (int)(smax >> 23), emin = (int)(smin >> 23);
+  double S;
+  if (smax == 0) {
+    S = 0.0;
+  } else if (smax < 0x7F800000u && emin >= 1 && W >= 1 && emax - emin < 2 * W) {
+    // squares at or above 2^(emax - W + 1) (biased exponents) in one window,
+    // the rest in the window below
+    const uint32_t split = (uint32_t)(emax - W + 1) << 23;
+    double shi = 0.0, slo = 0.0;
+    auto acc = [&](const uint4& v) {
+      float f[V];
+      unpack_f32<BF16>(v, f);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float p = f[e] * f[e];
+        const double dp = (double)p;
+        if (__float_as_uint(p) >= split) shi += dp;
+        else slo += dp;
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < kRmsCache; ++u) acc(d[u]);
+    tail([&](const uint4& v, int64_t) { acc(v); });
+    S = wave_sum_f64(shi) + wave_sum_f64(slo);
+  } else {
+    S = row_square_sum_windows<BF16>(row, nvec, lane);
+  }
   const float r = (float)(1.0 / sqrt(S / (double)K + (double)eps_n));
 
   // z of vector i (V values)
@@ -225,7 +321,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant_act(const void* __restric
   uint32_t mx = 0;
   float z[V];
 #pragma unroll
-  for (int u = 0; u < kActCache; ++u) {
+  for (int u = 0; u < kRmsCache; ++u) {
     const int64_t i = lane + 64 * u;
     if (i < nvec) {
       norm(d[u], i, z);
@@ -233,11 +329,11 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant_act(const void* __restric
       for (int e = 0; e < V; ++e) mx = max(mx, __float_as_uint(z[e]) & 0x7FFFFFFFu);
     }
   }
-  for (int64_t i = lane + 64 * kActCache; i < nvec; i += 64) {
-    norm(row[i], i, z);
+  tail([&](const uint4& v, int64_t i) {
+    norm(v, i, z);
 #pragma unroll
     for (int e = 0; e < V; ++e) mx = max(mx, __float_as_uint(z[e]) & 0x7FFFFFFFu);
-  }
+  });
   mx = wave_max_u32(mx);
   const ActScale sc = act_scale(mx, eps);
   if (lane == 0) sx[t] = sc.s;
@@ -252,17 +348,17 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant_act(const void* __restric
       *(uint32_t*)(qrow + i * V) = pack_low_bytes(c[0], c[1], c[2], c[3]);
   };
 #pragma unroll
-  for (int u = 0; u < kActCache; ++u) {
+  for (int u = 0; u < kRmsCache; ++u) {
     const int64_t i = lane + 64 * u;
     if (i < nvec) {
       norm(d[u], i, z);
       put(i, z);
     }
   }
-  for (int64_t i = lane + 64 * kActCache; i < nvec; i += 64) {
-    norm(row[i], i, z);
+  tail([&](const uint4& v, int64_t i) {
+    norm(v, i, z);
     put(i, z);
-  }
+  });
 }
 
 hipError_t launch_rmsnorm_quant_act(const void* x, bool bf16, const float* gain, int64_t T,

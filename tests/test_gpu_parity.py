@@ -7,6 +7,8 @@ product taken in the reading's fixed fp32 order.
 Inputs are seeded synthetic tensors from the workload generators; no expected
 value comes from the HIP path.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -134,6 +136,48 @@ def test_rmsnorm_quant_act_extreme_ranges(S, dt):
     x[4, 1000] = -3.0
     x[5] = (rng.standard_normal(K) * 1e-3).astype(F32)
     x[5, :8] = 2.0 ** 50
+    if dt == "bf16":
+        x = bf16_round(x)
+    xt = bf16_tensor(x) if dt == "bf16" else to_dev(x)
+    for eps_n in (1e-6, 1e-30):
+        xq, sx = S.sbl_rmsnorm_quant_act(xt, None, eps_n=eps_n)
+        rq, rs = o.rmsnorm_quant_act(x, None, eps_n, 1e-5)
+        assert np.array_equal(host(xq), rq)
+        assert np.array_equal(f32_bits(host(sx)), f32_bits(rs))
+
+
+@pytest.mark.parametrize("dt,K", [("bf16", 1024), ("bf16", 11008), ("fp32", 1024), ("fp32", 11008)])
+def test_rmsnorm_quant_act_window_boundary(S, dt, K):
+    """Rows at the edge of the kernel's fast exact sum (two fp64 windows of
+    W = 54 - SB - ceil(log2 K) binades below the largest square, SB = 16 for
+    bf16 and 24 for fp32): squares spanning 2W - 1 binades (fast, both
+    windows used), 2W (general sum), squares exactly at the split and one
+    binade below it, and one large square with many small ones 47 binades
+    down whose low bits a single fp64 sum would lose. Codes and scales bit
+    for bit against the oracle's exactly rounded sum."""
+    sb = 16 if dt == "bf16" else 24
+    W = 54 - sb - math.ceil(math.log2(K))
+    log_case("rmsnorm_quant_act window boundary", dt, K, W)
+    rng = np.random.default_rng(K + sb)
+    rows = []
+    for span2 in (2 * W - 1, 2 * W):             # largest square 2.25 * 2^(2 e_hi), smallest set by r[1]
+        e_hi = 3
+        e = rng.integers(e_hi - W + 1, e_hi + 1, K)
+        r = (rng.uniform(1.0, 1.99, K) * np.exp2(e.astype(np.float64))).astype(F32)
+        r *= np.where(rng.random(K) < 0.5, -1, 1).astype(F32)
+        r[0] = F32(1.5 * 2.0 ** e_hi)                                   # square exponent 2 e_hi + 1
+        r[1] = F32(2.0 ** (e_hi - span2 // 2)) if span2 % 2 else F32(1.5 * 2.0 ** (e_hi - span2 // 2))
+        rows.append(r)
+    r = (rng.uniform(1.0, 1.99, K) * np.exp2(rng.integers(-2, 3, K).astype(np.float64))).astype(F32)
+    r[0] = F32(1.5 * 2.0 ** 4)                                          # largest square: exponent 9
+    split = 9 - W + 1                                                   # squares at 2^split go high
+    r[2:40] = F32(2.0 ** (split / 2)) if split % 2 == 0 else F32(2.0 ** ((split - 1) / 2) * 1.5)
+    r[40:80] = F32(2.0 ** ((split - 1) / 2)) if (split - 1) % 2 == 0 else F32(2.0 ** ((split - 2) / 2) * 1.5)
+    rows.append(r)
+    r = np.full(K, F32(1.5078125 * 2.0 ** -18), dtype=F32)
+    r[0] = F32(2.0 ** 6)
+    rows.append(r)
+    x = np.stack(rows).astype(F32)
     if dt == "bf16":
         x = bf16_round(x)
     xt = bf16_tensor(x) if dt == "bf16" else to_dev(x)
