@@ -222,12 +222,16 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant_act(const void* __restric
                                                            int64_t T, int64_t K, int64_t ldx,
                                                            float eps_n, float eps,
                                                            int8_t* __restrict__ xq,
-                                                           float* __restrict__ sx) {
+                                                           float* __restrict__ sx, int stage) {
+  extern __shared__ __attribute__((aligned(16))) float gsm[];   // the gain, when staged
   constexpr int V = BF16 ? 8 : 4;
   constexpr int SB = BF16 ? 16 : 24;                    // significant bits of a square
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * kActRowsPerBlock + (threadIdx.x >> 6);
-  if (t >= T) return;
+  const int64_t tw = (int64_t)blockIdx.x * kActRowsPerBlock + (threadIdx.x >> 6);
+  // a wave past the last row computes row T - 1 again and stores nothing (every
+  // wave takes part in the barrier that publishes the staged gain)
+  const bool own = tw < T;
+  const int64_t t = own ? tw : T - 1;
   const int64_t nvec = K / V;
   const uint4* row = (const uint4*)((const char*)xv + t * ldx * (BF16 ? 2 : 4));
   int8_t* qrow = xq + t * K;
@@ -237,6 +241,16 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant_act(const void* __restric
   for (int u = 0; u < kRmsCache; ++u) {
     const int64_t i = lane + 64 * u;
     d[u] = i < nvec ? row[i] : make_uint4(0, 0, 0, 0);   // zero squares change nothing
+  }
+  // the gain into LDS by DMA (one instruction: 64 float4), read by the last two passes
+  if (stage) {
+    const int wave = threadIdx.x >> 6;
+    const int64_t nq = K / 4;
+    for (int64_t c = wave; 64 * c < nq; c += kActRowsPerBlock)
+      if (64 * c + lane < nq)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(gain + 4 * (64 * c + lane)),
+            (__attribute__((address_space(3))) void*)(gsm + 256 * c), 16, 0, 0);
   }
   // f(v, i) for the vectors past the register cache, kRmsBatch loads in flight
   auto tail = [&](auto&& f) {
@@ -302,63 +316,75 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant_act(const void* __restric
   }
   const float r = (float)(1.0 / sqrt(S / (double)K + (double)eps_n));
 
-  // z of vector i (V values)
-  auto norm = [&](const uint4& v, int64_t i, float* z) {
-    unpack_f32<BF16>(v, z);
+  if (stage) {
+    __builtin_amdgcn_s_waitcnt(0);                       // this wave's gain copies landed ...
+    __syncthreads();                                     // ... and every wave's
+  }
+
+  // the absmax of z and the codes, with the gain read through gp (LDS when
+  // staged, else global memory)
+  auto finish = [&](const float* __restrict__ gp) {
+    // z of vector i (V values)
+    auto norm = [&](const uint4& v, int64_t i, float* z) {
+      unpack_f32<BF16>(v, z);
 #pragma unroll
-    for (int e = 0; e < V; ++e) z[e] = z[e] * r;
-    if (gain) {
+      for (int e = 0; e < V; ++e) z[e] = z[e] * r;
+      if (gp) {
 #pragma unroll
-      for (int e4 = 0; e4 < V; e4 += 4) {
-        const float4 g4 = *(const float4*)(gain + i * V + e4);
-        z[e4] = z[e4] * g4.x;
-        z[e4 + 1] = z[e4 + 1] * g4.y;
-        z[e4 + 2] = z[e4 + 2] * g4.z;
-        z[e4 + 3] = z[e4 + 3] * g4.w;
+        for (int e4 = 0; e4 < V; e4 += 4) {
+          const float4 g4 = *(const float4*)(gp + i * V + e4);
+          z[e4] = z[e4] * g4.x;
+          z[e4 + 1] = z[e4 + 1] * g4.y;
+          z[e4 + 2] = z[e4 + 2] * g4.z;
+          z[e4 + 3] = z[e4 + 3] * g4.w;
+        }
+      }
+    };
+    uint32_t mx = 0;
+    float z[V];
+#pragma unroll
+    for (int u = 0; u < kRmsCache; ++u) {
+      const int64_t i = lane + 64 * u;
+      if (i < nvec) {
+        norm(d[u], i, z);
+#pragma unroll
+        for (int e = 0; e < V; ++e) mx = max(mx, __float_as_uint(z[e]) & 0x7FFFFFFFu);
       }
     }
-  };
-  uint32_t mx = 0;
-  float z[V];
-#pragma unroll
-  for (int u = 0; u < kRmsCache; ++u) {
-    const int64_t i = lane + 64 * u;
-    if (i < nvec) {
-      norm(d[u], i, z);
+    tail([&](const uint4& v, int64_t i) {
+      norm(v, i, z);
 #pragma unroll
       for (int e = 0; e < V; ++e) mx = max(mx, __float_as_uint(z[e]) & 0x7FFFFFFFu);
+    });
+    mx = wave_max_u32(mx);
+    const ActScale sc = act_scale(mx, eps);
+    if (!own) return;                                    // (wave-uniform)
+    if (lane == 0) sx[t] = sc.s;
+    auto put = [&](int64_t i, const float* zz) {
+      uint32_t c[8];
+#pragma unroll
+      for (int e = 0; e < V; ++e) c[e] = act_code_bits(zz[e], sc.q);
+      if constexpr (BF16)
+        *(uint2*)(qrow + i * V) = make_uint2(pack_low_bytes(c[0], c[1], c[2], c[3]),
+                                             pack_low_bytes(c[4], c[5], c[6], c[7]));
+      else
+        *(uint32_t*)(qrow + i * V) = pack_low_bytes(c[0], c[1], c[2], c[3]);
+    };
+#pragma unroll
+    for (int u = 0; u < kRmsCache; ++u) {
+      const int64_t i = lane + 64 * u;
+      if (i < nvec) {
+        norm(d[u], i, z);
+        put(i, z);
+      }
     }
-  }
-  tail([&](const uint4& v, int64_t i) {
-    norm(v, i, z);
-#pragma unroll
-    for (int e = 0; e < V; ++e) mx = max(mx, __float_as_uint(z[e]) & 0x7FFFFFFFu);
-  });
-  mx = wave_max_u32(mx);
-  const ActScale sc = act_scale(mx, eps);
-  if (lane == 0) sx[t] = sc.s;
-  auto put = [&](int64_t i, const float* zz) {
-    uint32_t c[8];
-#pragma unroll
-    for (int e = 0; e < V; ++e) c[e] = act_code_bits(zz[e], sc.q);
-    if constexpr (BF16)
-      *(uint2*)(qrow + i * V) = make_uint2(pack_low_bytes(c[0], c[1], c[2], c[3]),
-                                           pack_low_bytes(c[4], c[5], c[6], c[7]));
-    else
-      *(uint32_t*)(qrow + i * V) = pack_low_bytes(c[0], c[1], c[2], c[3]);
-  };
-#pragma unroll
-  for (int u = 0; u < kRmsCache; ++u) {
-    const int64_t i = lane + 64 * u;
-    if (i < nvec) {
-      norm(d[u], i, z);
+    tail([&](const uint4& v, int64_t i) {
+      norm(v, i, z);
       put(i, z);
-    }
-  }
-  tail([&](const uint4& v, int64_t i) {
-    norm(v, i, z);
-    put(i, z);
-  });
+    });
+  };
+  if (stage) finish(gsm);
+  else finish(gain);
 }
 
 hipError_t launch_rmsnorm_quant_act(const void* x, bool bf16, const float* gain, int64_t T,
@@ -366,12 +392,18 @@ hipError_t launch_rmsnorm_quant_act(const void* x, bool bf16, const float* gain,
                                     float* sx, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const dim3 grid((unsigned)cdiv(T, kActRowsPerBlock)), block(256);
+  // the gain goes through LDS for rows of 4096 to 16384 values (one copy per
+  // block of four rows instead of two reads from L2 per row: Qwen2.5-3B down
+  // input, K = 11008, 151 -> 135 us; on 2048-value rows the copy and its
+  // barrier cost more than they save, 34 -> 38 us)
+  const int stage = gain != nullptr && K >= 4096 && K * 4 <= 65536 ? 1 : 0;
+  const size_t lds = stage ? (size_t)K * 4 : 0;
   if (bf16)
-    hipLaunchKernelGGL(k_rmsnorm_quant_act<true>, grid, block, 0, s, x, gain, T, K, ldx, eps_n,
-                       eps, xq, sx);
+    hipLaunchKernelGGL(k_rmsnorm_quant_act<true>, grid, block, lds, s, x, gain, T, K, ldx, eps_n,
+                       eps, xq, sx, stage);
   else
-    hipLaunchKernelGGL(k_rmsnorm_quant_act<false>, grid, block, 0, s, x, gain, T, K, ldx, eps_n,
-                       eps, xq, sx);
+    hipLaunchKernelGGL(k_rmsnorm_quant_act<false>, grid, block, lds, s, x, gain, T, K, ldx, eps_n,
+                       eps, xq, sx, stage);
   return hipGetLastError();
 }
 
