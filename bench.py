@@ -63,6 +63,9 @@ def parse():
     p.add_argument("--backward", action="store_true",
                    help="prefill: the step adds the Dual-STE backward of every projection (x~ in "
                         "bf16, dX and dW on the bf16 matrix cores) to the forward: a training step")
+    p.add_argument("--overlap-backward", action="store_true",
+                   help="with --backward: each group's dW on a second stream beside its dX "
+                        "(default: every call on one stream)")
     p.add_argument("--mask-gated-grad", action="store_true",
                    help="with --backward: the ablated estimator, dW gated by the mask (the weight "
                         "preparation also writes the keep bits)")
@@ -79,10 +82,12 @@ def parse():
 # ---------------------------------------------------------------- prefill --
 class PrefillStep:
     def __init__(self, wl_name, N, M, diagnostics=False, fused_norm=False, variant=0,
-                 backward=False, gated=False):
+                 backward=False, gated=False, overlap_backward=False):
         wl = WORKLOADS[wl_name]
         self.wl, self.N, self.M, self.diag, self.norm = wl, N, M, diagnostics, fused_norm
         self.bwd, self.gated = backward, gated and backward
+        # with overlap_backward: dW on a second stream (default priority), beside dX
+        self.side = torch.cuda.Stream() if backward and overlap_backward else None
         W, X = make_workload(wl_name)
         dev = torch.device("cuda:0")
         self.T = wl.T
@@ -201,8 +206,34 @@ class PrefillStep:
         for xn in self.groups:
             order += [c for c in calls if c[0] in (f"quant_act[{xn}]",) or
                       (c[0].startswith("gemm[") and c[0] == self._gemm_name(xn))]
-        order += [c for c in calls if c[0].split("[")[0] in ("act_dequant", "bwd_dx", "bwd_dw")]
+        if self.side is None:
+            order += [c for c in calls if c[0].split("[")[0] in ("act_dequant", "bwd_dx", "bwd_dw")]
+            run_all(order)
+            return
         run_all(order)
+        self._backward_two_streams(dict(calls))
+
+    def _backward_two_streams(self, f):
+        """The backward with each projection group's dW beside its dX: the
+        launch stream runs the groups' dX in reverse order (a group's upstream
+        gradient comes from the dX of the group after it, through the FFN's
+        activation), a second stream the x~ of every group and the dW of each
+        group once that group's upstream gradient exists (for all but the last
+        group: once the dX before it has run). The streams join at the end."""
+        main, side = torch.cuda.current_stream(), self.side
+        groups = list(reversed(list(self.groups.items())))
+        side.wait_stream(main)                       # after the forward
+        with torch.cuda.stream(side):
+            for xn, _ in groups:
+                f[f"act_dequant[{xn}]"]()
+        for gi, (xn, lins) in enumerate(groups):
+            tag = '+'.join(l.name for l in lins)
+            if gi > 0:
+                side.wait_stream(main)               # the previous group's dX has run
+            with torch.cuda.stream(side):
+                f[f"bwd_dw[{tag}]"]()
+            f[f"bwd_dx[{tag}]"]()
+        main.wait_stream(side)
 
     def _gemm_name(self, xn):
         return f"gemm[{'+'.join(l.name for l in self.groups[xn])}]"
@@ -595,7 +626,7 @@ def main():
     else:
         step = PrefillStep(a.workload, N, M, a.diagnostics, a.fused_norm,
                            1 if a.mask_from_ternary else 2 if a.mask_then_quant else 0,
-                           a.backward, a.mask_gated_grad)
+                           a.backward, a.mask_gated_grad, a.overlap_backward)
     ms = time_steps(step, a.steps, a.warmup, a.eager)
     per_call, calls_per_step = per_call_times(step, max(5, min(a.steps, 20)))
     share = {k: per_call[k] * calls_per_step[k] for k in per_call}
@@ -639,7 +670,9 @@ def main():
                   "mask": "recomputed every step", "dense_equiv_ops_per_step": step.ops,
                   "backward": bool(a.backward),
                   "gradient": ("mask-gated (ablation)" if a.mask_gated_grad and a.backward else
-                               "dense (Dual STE)") if a.backward else None}
+                               "dense (Dual STE)") if a.backward else None,
+                  "backward_schedule": (("dW on a second stream beside dX" if a.overlap_backward
+                                         else "one stream") if a.backward else None)}
     out = {
         "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
