@@ -984,7 +984,8 @@ enum TileCfg { kT256x256 = 0, kT256x128 = 1, kT128x256 = 2, kT128x128 = 3, kT256
                kR256x80 = 24,      // WO 4, KS 1, FI 4, FJ 5
                kR256x96 = 25,      // WO 4, KS 1, FI 4, FJ 6 (NA 2)
                kR512x128w8 = 26,   // WO 8, KS 1, FI 4, FJ 8 (NA 2)
-               kNumCfg = 27 };
+               kR384x64 = 27,      // WO 6, KS 1, FI 4, FJ 4
+               kNumCfg = 28 };
 
 struct Args {
   const int8_t* xq; const float* sx; const uint8_t* packed; int64_t pitch; const float* sw;
@@ -1069,6 +1070,7 @@ static hipError_t launch_sel(int cfg, const Args& a, hipStream_t s) {
     case kR256x80: return launch_ra<4, 1, 4, 5, 4, SP, KA16, YBF16>(a, s);
     case kR256x96: return launch_ra<4, 1, 4, 6, 2, SP, KA16, YBF16>(a, s);
     case kR512x128w8: return launch_ra<8, 1, 4, 8, 2, SP, KA16, YBF16>(a, s);
+    case kR384x64: return launch_ra<6, 1, 4, 4, 4, SP, KA16, YBF16>(a, s);
     case kT64x128: return launch_cfg<64, 128, 2, 2, SP, KA16, YBF16>(a, s);
     case kDma128x256: return launch_dma<128, 256, 2, 4, SP, YBF16, SP ? 3 : 4>(a, s);
     case kDma256x128: return launch_dma<256, 128, 4, 2, SP, YBF16, SP ? 4 : 5>(a, s);
@@ -1096,7 +1098,8 @@ static hipError_t launch_sel(int cfg, const Args& a, hipStream_t s) {
 //  - dense N:M otherwise: 256x96 (the 0.5B gate+up projection: 29.8 us
 //    against 33.7 with 256x64);
 //  - 2:4 and 2:8 (sparse MFMA): 256x96 (wave tile 64x96) below K = 4096; above,
-//    256x128 when there are at least two such tiles per CU, else 512x64 (8 waves).
+//    256x128 when there are at least two such tiles per CU, else 512x64 (8 waves)
+//    or 384x64 (6 waves), whichever leaves fewer CUs idle.
 static int choose_cfg(int64_t T, int64_t O, int64_t K, bool sp) {
   // tuning override (read on every call so tests can force each configuration)
   const char* ev = std::getenv("SBL_GEMM_TILE");
@@ -1113,7 +1116,15 @@ static int choose_cfg(int64_t T, int64_t O, int64_t K, bool sp) {
   if (K >= 4096 && cdiv(O, 512) * cdiv(T, 128) >= cus) return kR512x128w8;
   if (sp) {
     if (K < 4096) return kR256x96;
-    return t128 >= 2 * cus ? kR256x128 : kR512x64w8;
+    if (t128 >= 2 * cus) return kR256x128;
+    // one workgroup per CU: 512x64 tiles (8 waves) unless they leave CUs idle
+    // in the last round and 384x64 tiles (6 waves, measured 0.87x the rate
+    // per CU) fill more of them (Qwen2.5-1.5B down, O = 1536: 192 tiles of
+    // 512x64 against 256 of 384x64, 77 -> 66 us)
+    const int64_t n512 = cdiv(O, 512) * cdiv(T, 64), n384 = cdiv(O, 384) * cdiv(T, 64);
+    const double f512 = (double)n512 / (double)(cdiv(n512, cus) * cus);
+    const double f384 = 0.87 * (double)n384 / (double)(cdiv(n384, cus) * cus);
+    return f384 > f512 ? kR384x64 : kR512x64w8;
   }
   if (K >= 2048 && t128 >= 2 * cus) return kR256x128;
   return kR256x96;

@@ -856,7 +856,7 @@ def test_decode_large_k_falls_back(S):
     assert_f32_close(host(y), o.linear_fwd(bf16_round(x), W, N, M)["y"])
 
 
-@pytest.mark.parametrize("cfg", list(range(27)))
+@pytest.mark.parametrize("cfg", list(range(28)))
 def test_gemm_every_tile_config(S, cfg, monkeypatch):
     """Each workgroup-tile configuration of the GEMM, forced, on ragged shapes."""
     monkeypatch.setenv("SBL_GEMM_TILE", str(cfg))
