@@ -504,7 +504,8 @@ def _cpu_model():
 
 TRAFFIC_FILES = [os.path.join(ROOT, "profiles", f)
                  for f in ("traffic_qwen3b_sweep.txt", "traffic_qwen05b_ffn.txt",
-                           "traffic_bitnet_decode_t8.txt", "traffic_qwen15b_ffn_train.txt")]
+                           "traffic_qwen15b_ffn.txt", "traffic_bitnet_decode_t8.txt",
+                           "traffic_qwen15b_ffn_train.txt")]
 def measured_traffic(workload, kernel_call):
     """HBM bytes per launch of the dominant call from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summary (scaled by the same counters on a plain
