@@ -122,15 +122,17 @@ __device__ __forceinline__ void decode_dense16(uint32_t w, uint4& lo, uint4& hi)
 // Index-form chunk (code word cw, index word iw) -> 16 bf16 of groups
 // 4h..4h+3 (k = 32c + 16h + 0..15).
 __device__ __forceinline__ void decode_index16(uint32_t cw, uint32_t iw, int h, uint4& lo, uint4& hi) {
+  // group q = 4h + qq: its index nibble is bits 4qq.. of iwh, its codes are
+  // fields 2q and 2q + 1, i.e. bits field_shift(2qq) + 4h .. of cw
+  const uint32_t iwh = iw >> (16 * h), cwh = cw >> (4 * h);
   uint32_t out[8];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
-    const int q = 4 * h + qq;
-    const uint32_t s0 = (iw >> (4 * q)) & 3u, s1 = (iw >> (4 * q + 2)) & 3u;
-    const uint32_t c0 = (cw >> field_shift(2 * q)) & 3u, c1 = (cw >> field_shift(2 * q + 1)) & 3u;
-    const uint32_t d = (c0 << (2 * s0)) | (c1 << (2 * s1));   // 4 slot codes, 2 bits each
-    const uint32_t e = (d & 3u) | ((d & 0xCu) << 6) | ((d & 0x30u) << 12) | ((d & 0xC0u) << 18);
-    const uint2 v = codes4_bf16(e);
+    // the kept slots s0 < s1 times 8 (bit offsets of their bytes) and codes
+    const uint32_t b0 = (qq == 0 ? iwh << 3 : iwh >> (4 * qq - 3)) & 0x18u;
+    const uint32_t b1 = (qq == 0 ? iwh << 1 : iwh >> (4 * qq - 1)) & 0x18u;
+    const uint32_t c0 = (cwh >> field_shift(2 * qq)) & 3u, c1 = (cwh >> field_shift(2 * qq + 1)) & 3u;
+    const uint2 v = codes4_bf16((c0 << b0) | (c1 << b1));   // slot codes, one per byte
     out[2 * qq] = v.x;
     out[2 * qq + 1] = v.y;
   }
